@@ -1,0 +1,84 @@
+"""Planted mistakes in the oracle must fail at least one pin.
+
+Each mutant is a copy of oracle.c with one plausible error (a dropped clamp, a
+wrong row index, a flipped comparison ...).  It is compiled with gcc into a
+temporary library, swapped in for the real one, and the pins are re-run; the
+test passes only if some pin rejects the mutant.  Everything runs on the CPU.
+"""
+import ctypes
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "non_strict_accept": ("int acc = ui < thr;", "int acc = ui <= thr;"),
+    "scalar_residual": ("prob_at(draft, dtype, dr, v, md[n], Zd[n], T);",
+                        "prob_at(draft, dtype, dr, d[n], md[n], Zd[n], T);"),
+    "no_clamp": ("w[v] = diff > 0.0 ? diff : 0.0;", "w[v] = diff;"),
+    "residual_uses_previous_draft_row": ("const size_t dr = drow0 + (size_t)n * V;",
+                                         "const size_t dr = drow0 + (size_t)(n > 0 ? n - 1 : 1) * V;"),
+    "bonus_from_last_draft_position": ("w[v] = prob_at(target, dtype, tr, v, mt[K], Zt[K], T); S += w[v]; }\n    }",
+                                       "w[v] = prob_at(target, dtype, tr - (size_t)V, v, mt[K-1], Zt[K-1], T); S += w[v]; }\n    }"),
+    "cdf_ge": ("if (C > target_mass) { pick = v; break; }", "if (C >= target_mass) { pick = v; break; }"),
+    "temperature_multiplies": ("Z += exp((x - m) / T);", "Z += exp((x - m) * T);"),
+    "greedy_last_tie": ("if (x > best) { best = x; arg = v; }\n        }\n        if (!isfinite(best)) faulty = 1;",
+                        "if (x >= best) { best = x; arg = v; }\n        }\n        if (!isfinite(best)) faulty = 1;"),
+    "last_rejection": ("if (!acc && n == K) n = i;", "if (!acc) n = i;"),
+    "emit_draft_at_rejection": ("out[n] = pick;", "out[n] = n < K ? d[n] : pick;"),
+    "zero_ratio_accepts": ("double ratio = pd > 0.0 ? pt / pd : INFINITY;",
+                           "double ratio = pd > 0.0 ? pt / pd : 0.0;"),
+}
+
+PINS = [
+    pins.test_worked_example_acceptance_by_quadrature,
+    pins.test_worked_example_replacements_by_quadrature,
+    pins.test_worked_example_output_marginal_is_target,
+    lambda: pins.test_row_stats_against_logsumexp(0.8),
+    pins.test_identical_draft_accepts_everything_and_samples_bonus,
+    pins.test_disjoint_supports_reject_and_sample_target,
+    pins.test_zero_draft_probability_means_accept,
+    pins.test_greedy_is_argmax_prefix,
+    pins.test_accept_comparison_is_strict,
+    pins.test_inverse_cdf_skips_zero_weight_tokens,
+    pins.test_expected_tokens_closed_form,
+    lambda: pins.test_chi_square_output_follows_target(2.0),
+]
+
+
+def _build_mutant(name, old, new, tmp):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/found"
+    path = os.path.join(tmp, f"{name}.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    so = os.path.join(tmp, f"lib{name}.so")
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", so, path, "-lm"])
+    return so
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    old, new = MUTANTS[name]
+    real = oracle._load()
+    with tempfile.TemporaryDirectory() as tmp:
+        so = _build_mutant(name, old, new, tmp)
+        lib = ctypes.CDLL(so)
+        for fn in ("oracle_verify", "oracle_row_stats", "oracle_head"):
+            getattr(lib, fn).argtypes = getattr(real, fn).argtypes
+            getattr(lib, fn).restype = getattr(real, fn).restype
+        monkeypatch.setattr(oracle, "_lib", lib)
+        caught = []
+        for pin in PINS:
+            try:
+                pin()
+            except AssertionError:
+                caught.append(getattr(pin, "__name__", "pin"))
+                break
+        assert caught, f"mutant {name} passed every pin"

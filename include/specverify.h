@@ -1,0 +1,161 @@
+/*
+ * specverify.h -- C ABI of the MI355X (gfx950) speculative-sampling verify
+ * library (libspecverify.so).
+ *
+ * The library implements the verify step of speculative sampling over a large
+ * vocabulary, its greedy variant, and the shortlisted drafter head:
+ *
+ *   - For each sequence b and draft position i < K, the draft token d_i is
+ *     accepted with probability min(1, P_t,i(d_i) / P_d,i(d_i)), left to right,
+ *     where P = softmax(logits / T) for the target (t) and draft (d) models.
+ *     At the first rejection n a replacement is sampled from the normalised
+ *     residual (P_t,n - P_d,n)_+; if all K drafts are accepted a bonus token is
+ *     sampled from P_t,K.  Speculative Decoding lesson (nextadmin.net),
+ *     "Core algorithm" steps 4-6, "Step 1" and "Step 2"; LLMs-from-Scratch
+ *     lesson 25 (aiengineeringfromscratch.com), "The exact rule".
+ *   - Greedy (temperature 0): accept d_i iff it equals the argmax of target
+ *     row i; at the first mismatch emit that argmax and stop.  LLMs-from-Scratch
+ *     lesson 25, "Greedy case".
+ *   - Shortlisted drafter head: draft logits only on the union of the clusters
+ *     each context selects.  DynaSpec summary (lowest.today, arXiv 2510.13847),
+ *     "Model architecture", items 1, 3 and 4.
+ *
+ * Conventions shared by every entry point:
+ *   - All array arguments are device pointers (hipMalloc / torch CUDA tensors),
+ *     contiguous, row-major, owned by the caller.  The library allocates no
+ *     memory and keeps no global state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *     are asynchronous on that stream; nothing is read back to the host.
+ *   - Argument errors are returned synchronously before anything is enqueued;
+ *     outputs are then left untouched.  SPEC_ERR_HIP reports a failed launch.
+ *   - Calls with distinct workspaces may run concurrently.  Two calls that
+ *     share a workspace must be ordered (same stream or synchronised).
+ */
+#ifndef SPECVERIFY_H_
+#define SPECVERIFY_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_ABI_VERSION 1
+#define SPEC_MAX_K 64
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
+typedef enum { SPEC_MODE_SAMPLE = 0, SPEC_MODE_GREEDY = 1 } spec_mode_t;
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_ERR_INVALID_ARG = 1, /* NULL pointer, negative size, bad temperature, bad enum, overflow */
+  SPEC_ERR_UNSUPPORTED = 2, /* K > SPEC_MAX_K, V > 2^30, a grid too large for one launch, V % cluster_size != 0 */
+  SPEC_ERR_WORKSPACE = 3,   /* workspace NULL, too small, or not 256-byte aligned */
+  SPEC_ERR_HIP = 4          /* a HIP launch failed; the workspace must be re-zeroed */
+} spec_status_t;
+
+/* Library ABI version (SPEC_ABI_VERSION of the build). */
+int spec_abi_version(void);
+
+/* Static string naming a status code. */
+const char* spec_status_string(spec_status_t status);
+
+/*
+ * Workspace bytes spec_verify needs for this shape (0 when B == 0).
+ * The workspace holds per-sequence arrival counters and partial row
+ * statistics.  It must be zero-filled once before its first use; every call
+ * that returns SPEC_OK leaves the counters at zero again, so the same buffer
+ * can be reused by later calls of any shape that fits.
+ */
+size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V, spec_dtype_t dtype,
+                                   spec_mode_t mode);
+
+/*
+ * Speculative-sampling verify step.
+ *
+ *   target_logits  [B, K+1, V] of dtype: target logits at the K draft
+ *                  positions and the bonus position.
+ *   draft_logits   [B, K, V] of dtype: draft-model logits at the K positions.
+ *                  Unused (may be NULL) in GREEDY mode or when K == 0.
+ *   draft_tokens   [B, K] int32 token ids.  Unused (may be NULL) when K == 0.
+ *   uniforms       [B, K+1, 2] float in [0, 1): uniforms[b,i,0] is the accept
+ *                  uniform of position i, uniforms[b,i,1] the sampling uniform
+ *                  used if the output token at position i is sampled.
+ *                  Unused (may be NULL) in GREEDY mode.
+ *   temperature    SAMPLE: finite and > 0; both softmaxes use logits / T.
+ *                  GREEDY: ignored.
+ *   accepted_len   [B] int32 out: n in [0, K] accepted drafts, or -1 when the
+ *                  sequence is faulty (a draft token outside [0, V), or a row
+ *                  the rule reads whose maximum logit is not finite).
+ *   out_tokens     [B, K+1] int32 out: d_0..d_{n-1}, then the sampled (or
+ *                  argmax) token at position n, then -1.  All -1 when faulty.
+ *   p_target_at_draft, p_draft_at_draft
+ *                  optional [B, K] float outs (NULL = skip): P_t,i(d_i) and
+ *                  P_d,i(d_i) in SAMPLE mode, NaN in GREEDY mode or where a
+ *                  sequence is faulty.
+ *   workspace      device buffer of at least spec_verify_workspace_bytes(),
+ *                  256-byte aligned, zero-filled before its first use.
+ *
+ * Logits must be finite or -inf (-inf marks tokens outside a shortlist).
+ * The inverse-CDF sample picks the smallest token id v whose cumulative mass,
+ * in token-id order, exceeds u * (total mass).
+ */
+spec_status_t spec_verify(const void* target_logits, const void* draft_logits,
+                          const int32_t* draft_tokens, const float* uniforms,
+                          int32_t B, int32_t K, int32_t V, spec_dtype_t dtype,
+                          float temperature, spec_mode_t mode,
+                          int32_t* accepted_len, int32_t* out_tokens,
+                          float* p_target_at_draft, float* p_draft_at_draft,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify with kernel timing.  Identical work and launches; in addition
+ * events[0], events[1] and events[2] (hipEvent_t passed as void*, any may be
+ * NULL) are recorded on `stream` before the first kernel, between the row
+ * statistics kernel and the sampling kernel, and after the last kernel.
+ * In GREEDY mode there is one kernel: events[1] and events[2] are recorded
+ * after it.
+ */
+spec_status_t spec_verify_timed(const void* target_logits, const void* draft_logits,
+                                const int32_t* draft_tokens, const float* uniforms,
+                                int32_t B, int32_t K, int32_t V, spec_dtype_t dtype,
+                                float temperature, spec_mode_t mode,
+                                int32_t* accepted_len, int32_t* out_tokens,
+                                float* p_target_at_draft, float* p_draft_at_draft,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                void* const* events);
+
+/*
+ * Shortlisted drafter head (DynaSpec summary, "Model architecture", items 1,
+ * 3 and 4).  The vocabulary is split into V / cluster_size contiguous
+ * clusters; cluster c holds ids [c*cluster_size, (c+1)*cluster_size).  Context
+ * b (shared by its K positions) selects n_sel clusters.
+ *
+ *   h             bf16 [B, K, d]   drafter hidden states.
+ *   W             bf16 [V, d]      LM-head weight, row-major (one row per token).
+ *   cluster_ids   int32 [B, n_sel] strictly ascending ids in [0, V/cluster_size).
+ *   logits_compact float [B, K, n_sel*cluster_size] out: the shortlist logits,
+ *                 sum_j h[b,k,j] * W[tok,j] accumulated in fp32, ordered by
+ *                 ascending token id (cluster_ids order, then id within the
+ *                 cluster).  May be NULL if dense_out is given.
+ *   dense_out     NULL or [B, K, V] of dense_dtype out: the same logits at
+ *                 their token ids and -inf off the shortlist, ready to be the
+ *                 draft_logits of spec_verify.
+ *   workspace     unused today; pass NULL and 0.
+ * Errors: SPEC_ERR_UNSUPPORTED if V % cluster_size != 0; SPEC_ERR_INVALID_ARG
+ * for NULL inputs or non-positive sizes.  Cluster ids are not validated on the
+ * host (they live on the device): an id out of range or out of order makes the
+ * kernel skip that entry and leaves its outputs unwritten.
+ */
+spec_status_t spec_draft_head_shortlist(const void* h, const void* W, const int32_t* cluster_ids,
+                                        int32_t B, int32_t K, int32_t d, int32_t V,
+                                        int32_t cluster_size, int32_t n_sel,
+                                        float* logits_compact, void* dense_out,
+                                        spec_dtype_t dense_dtype,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H_ */

@@ -1,0 +1,168 @@
+"""MI355X (gfx950) speculative-sampling verify over large vocabularies.
+
+Python face of libspecverify.so.  Functions take torch tensors on a ROCm GPU
+and call the C ABI on torch's current stream; results are new tensors on the
+same device.  See include/specverify.h for the full contract.
+
+    accepted_len, out_tokens = spec_verify(target, draft, draft_tokens, uniforms,
+                                           temperature=1.0, mode="sample")
+    compact, dense = spec_draft_head_shortlist(h, W, cluster_ids, cluster_size)
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import torch
+
+from . import _native
+from ._native import SpecVerifyError  # noqa: F401
+
+__all__ = ["spec_verify", "spec_verify_workspace_bytes", "spec_draft_head_shortlist",
+           "Workspace", "SpecVerifyError", "abi_version"]
+
+_DTYPES = {torch.bfloat16: _native.SPEC_BF16, torch.float32: _native.SPEC_F32}
+_MODES = {"sample": _native.SPEC_MODE_SAMPLE, "greedy": _native.SPEC_MODE_GREEDY}
+
+
+def abi_version() -> int:
+    return _native.load().spec_abi_version()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_gpu(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(device: torch.device, stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def spec_verify_workspace_bytes(B: int, K: int, V: int, dtype: torch.dtype, mode: str = "sample") -> int:
+    return int(_native.load().spec_verify_workspace_bytes(B, K, V, _DTYPES[dtype], _MODES[mode]))
+
+
+class Workspace:
+    """A zero-filled device buffer reused across calls (the library leaves it zeroed)."""
+
+    def __init__(self, device):
+        self.device = torch.device(device)
+        self.buf = torch.zeros(0, dtype=torch.uint8, device=self.device)
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 2 * self.buf.numel()), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+    def reset(self):
+        """Re-zero after a failed call (the library cannot clean up after a failed launch)."""
+        self.buf.zero_()
+
+
+_default_ws = {}
+
+
+def _workspace_for(device) -> Workspace:
+    key = torch.device(device)
+    if key not in _default_ws:
+        _default_ws[key] = Workspace(key)
+    return _default_ws[key]
+
+
+def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: Optional[torch.Tensor],
+                uniforms: Optional[torch.Tensor], temperature: float = 1.0, mode: str = "sample", *,
+                return_probs: bool = False, workspace: Optional[Workspace] = None, stream=None,
+                events: Optional[Sequence] = None):
+    """Speculative-sampling verify step on the GPU.
+
+    target [B, K+1, V] and draft [B, K, V] (bf16 or float32), draft_tokens int32
+    [B, K], uniforms float32 [B, K+1, 2].  Returns (accepted_len int32 [B],
+    out_tokens int32 [B, K+1]) and, with return_probs, also (P_t(d), P_d(d))
+    float32 [B, K].  `events`: up to three torch.cuda.Event recorded around the
+    kernels (see spec_verify_timed in the C header).
+    """
+    if mode not in _MODES:
+        raise ValueError(f"mode must be one of {list(_MODES)}")
+    _need_gpu(target, "target")
+    if target.dim() != 3:
+        raise ValueError("target must be [B, K+1, V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dt = _DTYPES.get(target.dtype)
+    if dt is None:
+        raise ValueError("logits must be bfloat16 or float32")
+    dev = target.device
+    if mode == "sample" and K > 0:
+        if draft is None:
+            raise ValueError("draft logits are required in sample mode")
+        _need_gpu(draft, "draft")
+        if draft.dtype != target.dtype or tuple(draft.shape) != (B, K, V):
+            raise ValueError("draft must match target dtype and be [B, K, V]")
+    if K > 0:
+        if draft_tokens is None:
+            raise ValueError("draft_tokens are required when K > 0")
+        _need_gpu(draft_tokens, "draft_tokens")
+        if draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != (B, K):
+            raise ValueError("draft_tokens must be int32 [B, K]")
+    if mode == "sample":
+        if uniforms is None:
+            raise ValueError("uniforms are required in sample mode")
+        _need_gpu(uniforms, "uniforms")
+        if uniforms.dtype != torch.float32 or tuple(uniforms.shape) != (B, K + 1, 2):
+            raise ValueError("uniforms must be float32 [B, K+1, 2]")
+    lib = _native.load()
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    pt = torch.empty((B, K), dtype=torch.float32, device=dev) if return_probs else None
+    pd = torch.empty((B, K), dtype=torch.float32, device=dev) if return_probs else None
+    need = lib.spec_verify_workspace_bytes(B, K, V, dt, _MODES[mode])
+    ws = (workspace or _workspace_for(dev)).get(need)
+    args = [_ptr(target), _ptr(draft) if mode == "sample" else None,
+            _ptr(draft_tokens) if K > 0 else None, _ptr(uniforms) if mode == "sample" else None,
+            B, K, V, dt, ctypes.c_float(temperature if mode == "sample" else 0.0), _MODES[mode],
+            _ptr(acc), _ptr(out), _ptr(pt), _ptr(pd), _ptr(ws), ws.numel(), _stream_handle(dev, stream)]
+    if events is not None:
+        evs = [ctypes.c_void_p(e.cuda_event if e is not None else 0) for e in list(events) + [None] * (3 - len(events))]
+        arr = (ctypes.c_void_p * 3)(*[e.value for e in evs])
+        st = lib.spec_verify_timed(*args, arr)
+    else:
+        st = lib.spec_verify(*args)
+    _native.check(st, "spec_verify")
+    if return_probs:
+        return acc, out, pt, pd
+    return acc, out
+
+
+def spec_draft_head_shortlist(h: torch.Tensor, W: torch.Tensor, cluster_ids: torch.Tensor, cluster_size: int, *,
+                              compact: bool = True, dense: bool = True, dense_dtype: torch.dtype = torch.float32,
+                              stream=None):
+    """Shortlisted drafter head.  h bf16 [B, K, d], W bf16 [V, d], cluster_ids int32 [B, n_sel]
+    (ascending).  Returns (compact float32 [B, K, n_sel*cluster_size] or None,
+    dense [B, K, V] of dense_dtype with -inf off the shortlist, or None)."""
+    for t, name in ((h, "h"), (W, "W"), (cluster_ids, "cluster_ids")):
+        _need_gpu(t, name)
+    if h.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+        raise ValueError("h and W must be bfloat16")
+    if cluster_ids.dtype != torch.int32:
+        raise ValueError("cluster_ids must be int32")
+    B, K, d = h.shape
+    V = W.shape[0]
+    if W.shape[1] != d:
+        raise ValueError("W must be [V, d]")
+    n_sel = cluster_ids.shape[1]
+    dev = h.device
+    comp = torch.empty((B, K, n_sel * cluster_size), dtype=torch.float32, device=dev) if compact else None
+    dn = torch.empty((B, K, V), dtype=dense_dtype, device=dev) if dense else None
+    lib = _native.load()
+    st = lib.spec_draft_head_shortlist(_ptr(h), _ptr(W), _ptr(cluster_ids), B, K, d, V, cluster_size, n_sel,
+                                       _ptr(comp), _ptr(dn), _DTYPES[dense_dtype] if dense else 0, None, 0,
+                                       _stream_handle(dev, stream))
+    _native.check(st, "spec_draft_head_shortlist")
+    return comp, dn

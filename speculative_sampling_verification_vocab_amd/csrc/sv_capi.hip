@@ -1,0 +1,158 @@
+// C ABI of libspecverify.so: argument validation, workspace sizing, launches.
+// Declarations and the contract of every entry point are in include/specverify.h.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/specverify.h"
+#include "sv_internal.h"
+
+namespace {
+
+constexpr size_t kMaxGrid = 0x7fffffffu;
+
+bool valid_dtype(spec_dtype_t d) { return d == SPEC_F32 || d == SPEC_BF16; }
+bool valid_mode(spec_mode_t m) { return m == SPEC_MODE_SAMPLE || m == SPEC_MODE_GREEDY; }
+size_t elem_size(spec_dtype_t d) { return d == SPEC_BF16 ? 2 : 4; }
+
+// Shape checks shared by the sizing function and the entry points.
+spec_status_t check_shape(int32_t B, int32_t K, int32_t V, spec_dtype_t dtype, spec_mode_t mode) {
+  if (!valid_dtype(dtype) || !valid_mode(mode)) return SPEC_ERR_INVALID_ARG;
+  if (B < 0 || K < 0 || V < 1) return SPEC_ERR_INVALID_ARG;
+  if (K > SPEC_MAX_K) return SPEC_ERR_UNSUPPORTED;
+  if (V > (1 << 30)) return SPEC_ERR_UNSUPPORTED;  // token ids and tile offsets stay in int32
+  // element counts must fit size_t with room for byte offsets
+  const size_t rows = (size_t)B * (size_t)(K + 1);
+  if ((size_t)B != 0 && rows / (size_t)B != (size_t)(K + 1)) return SPEC_ERR_INVALID_ARG;
+  if (rows != 0 && (size_t)V > SIZE_MAX / 8 / rows) return SPEC_ERR_INVALID_ARG;
+  const sv::VerifyShape s = sv::make_shape(B, K, V, dtype == SPEC_BF16 ? 1 : 0, false);
+  const size_t per_seq_rows = mode == SPEC_MODE_GREEDY ? (size_t)(K + 1) : (size_t)(2 * K);
+  if ((size_t)B * per_seq_rows * (size_t)s.NG > kMaxGrid) return SPEC_ERR_UNSUPPORTED;
+  if ((size_t)B * (size_t)s.NG > kMaxGrid) return SPEC_ERR_UNSUPPORTED;
+  return SPEC_OK;
+}
+
+spec_status_t verify_impl(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                          const float* uniforms, int32_t B, int32_t K, int32_t V, spec_dtype_t dtype,
+                          float temperature, spec_mode_t mode, int32_t* accepted_len, int32_t* out_tokens,
+                          float* p_target_at_draft, float* p_draft_at_draft, void* workspace,
+                          size_t workspace_bytes, void* stream, void* const* events) {
+  const spec_status_t sc = check_shape(B, K, V, dtype, mode);
+  if (sc != SPEC_OK) return sc;
+  const bool sample = mode == SPEC_MODE_SAMPLE;
+  if (sample && !(temperature > 0.0f && isfinite(temperature))) return SPEC_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  auto record = [&](int i) {
+    if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
+  };
+  if (B == 0) {
+    record(0);
+    record(1);
+    record(2);
+    return SPEC_OK;
+  }
+  if (!target_logits || !accepted_len || !out_tokens) return SPEC_ERR_INVALID_ARG;
+  if (K > 0 && !draft_tokens) return SPEC_ERR_INVALID_ARG;
+  if (sample && K > 0 && !draft_logits) return SPEC_ERR_INVALID_ARG;
+  if (sample && !uniforms) return SPEC_ERR_INVALID_ARG;
+
+  const size_t esz = elem_size(dtype);
+  const size_t vec = 16 / esz;
+  bool aligned = ((size_t)V % vec == 0) && ((uintptr_t)target_logits % 16 == 0);
+  if (sample && K > 0) aligned = aligned && ((uintptr_t)draft_logits % 16 == 0);
+  const sv::VerifyShape s = sv::make_shape(B, K, V, dtype == SPEC_BF16 ? 1 : 0, aligned);
+
+  const size_t need = sv::verify_workspace_layout(s, !sample, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 256) != 0) return SPEC_ERR_WORKSPACE;
+  sv::VerifyWorkspace ws{};
+  sv::verify_workspace_layout(s, !sample, workspace, &ws);
+
+  sv::VerifyIO io{};
+  io.target = target_logits;
+  io.draft = draft_logits;
+  io.tokens = draft_tokens;
+  io.uniforms = uniforms;
+  io.temperature = temperature;
+  io.accepted_len = accepted_len;
+  io.out_tokens = out_tokens;
+  io.p_target = p_target_at_draft;
+  io.p_draft = p_draft_at_draft;
+
+  (void)hipGetLastError();  // clear a stale error so the checks below see only ours
+  record(0);
+  hipError_t e = hipSuccess;
+  if (sample) {
+    e = sv::launch_stats(s, io, ws, st);
+    record(1);
+    if (e == hipSuccess) e = sv::launch_sample(s, io, ws, st);
+    record(2);
+  } else {
+    e = sv::launch_greedy(s, io, ws, st);
+    record(1);
+    record(2);
+  }
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_abi_version(void) { return SPEC_ABI_VERSION; }
+
+const char* spec_status_string(spec_status_t status) {
+  switch (status) {
+    case SPEC_OK: return "SPEC_OK";
+    case SPEC_ERR_INVALID_ARG: return "SPEC_ERR_INVALID_ARG: invalid argument";
+    case SPEC_ERR_UNSUPPORTED: return "SPEC_ERR_UNSUPPORTED: shape outside what the library supports";
+    case SPEC_ERR_WORKSPACE: return "SPEC_ERR_WORKSPACE: workspace missing, too small or misaligned";
+    case SPEC_ERR_HIP: return "SPEC_ERR_HIP: a HIP launch failed";
+  }
+  return "unknown spec_status_t";
+}
+
+size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V, spec_dtype_t dtype, spec_mode_t mode) {
+  if (check_shape(B, K, V, dtype, mode) != SPEC_OK || B == 0) return 0;
+  const sv::VerifyShape s = sv::make_shape(B, K, V, dtype == SPEC_BF16 ? 1 : 0, false);
+  return sv::verify_workspace_layout(s, mode == SPEC_MODE_GREEDY, nullptr, nullptr);
+}
+
+spec_status_t spec_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                          const float* uniforms, int32_t B, int32_t K, int32_t V, spec_dtype_t dtype,
+                          float temperature, spec_mode_t mode, int32_t* accepted_len, int32_t* out_tokens,
+                          float* p_target_at_draft, float* p_draft_at_draft, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, B, K, V, dtype, temperature, mode,
+                     accepted_len, out_tokens, p_target_at_draft, p_draft_at_draft, workspace, workspace_bytes,
+                     stream, nullptr);
+}
+
+spec_status_t spec_verify_timed(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                                const float* uniforms, int32_t B, int32_t K, int32_t V, spec_dtype_t dtype,
+                                float temperature, spec_mode_t mode, int32_t* accepted_len, int32_t* out_tokens,
+                                float* p_target_at_draft, float* p_draft_at_draft, void* workspace,
+                                size_t workspace_bytes, void* stream, void* const* events) {
+  return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, B, K, V, dtype, temperature, mode,
+                     accepted_len, out_tokens, p_target_at_draft, p_draft_at_draft, workspace, workspace_bytes,
+                     stream, events);
+}
+
+spec_status_t spec_draft_head_shortlist(const void* h, const void* W, const int32_t* cluster_ids, int32_t B,
+                                        int32_t K, int32_t d, int32_t V, int32_t cluster_size, int32_t n_sel,
+                                        float* logits_compact, void* dense_out, spec_dtype_t dense_dtype,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (B < 0 || K < 0 || d < 1 || V < 1 || cluster_size < 1 || n_sel < 0) return SPEC_ERR_INVALID_ARG;
+  if (!valid_dtype(dense_dtype)) return SPEC_ERR_INVALID_ARG;
+  if (V % cluster_size != 0) return SPEC_ERR_UNSUPPORTED;
+  if (n_sel > V / cluster_size) return SPEC_ERR_INVALID_ARG;
+  if (B == 0 || K == 0) return SPEC_OK;
+  if (!h || !W || (!cluster_ids && n_sel > 0) || (!logits_compact && !dense_out)) return SPEC_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  const hipError_t e = sv::launch_head(h, W, cluster_ids, B, K, d, V, cluster_size, n_sel, logits_compact,
+                                       dense_out, dense_dtype == SPEC_BF16 ? 1 : 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,208 @@
+// Device-side building blocks shared by the verify kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = kWave * kWavesPerBlock;
+constexpr int kLoads = 8;  // 16-byte loads per lane per row tile
+constexpr int kMaxK = 64;
+
+// Storage element types: bf16 logits are handled as their uint16 bit patterns.
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> { static constexpr int kVec = 8; };
+template <> struct Elem<float> { static constexpr int kVec = 4; };
+
+template <typename T> constexpr int kPerLane = Elem<T>::kVec * kLoads;  // 64 bf16, 32 f32
+template <typename T> constexpr int kTile = kWave * kPerLane<T>;         // 4096 bf16, 2048 f32
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ float to_f32(float f) { return f; }
+
+// Position of lane element e inside a tile: 16-byte load j = e / kVec covers
+// kWave*kVec consecutive ids, lane l owns ids [l*kVec, l*kVec + kVec) of it.
+// A lane's elements are therefore in increasing token-id order.
+template <typename T>
+__device__ __forceinline__ int tile_offset(int e, int lane) {
+  constexpr int V8 = Elem<T>::kVec;
+  return (e / V8) * (kWave * V8) + lane * V8 + (e % V8);
+}
+
+// Load the lane's kPerLane elements of tile t of a row of V logits as float;
+// ids >= V read as -inf.  kAligned requires a 16-byte aligned row and
+// V % kVec == 0, so a 16-byte vector is either fully inside the row or fully out.
+template <typename T, bool kAligned>
+__device__ __forceinline__ void load_tile(const T* __restrict__ row, int V, int t, int lane,
+                                          float (&x)[kPerLane<T>]) {
+  constexpr int V8 = Elem<T>::kVec;
+  const int base = t * kTile<T> + lane * V8;
+  if constexpr (kAligned) {
+    u32x4 raw[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int off = base + j * (kWave * V8);
+      if (off < V) {
+        raw[j] = *reinterpret_cast<const u32x4*>(row + off);
+      } else {
+        const uint32_t ninf = sizeof(T) == 2 ? 0xff80ff80u : 0xff800000u;
+        raw[j] = u32x4{ninf, ninf, ninf, ninf};
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          x[j * 8 + 2 * q] = bf16_lo(raw[j][q]);
+          x[j * 8 + 2 * q + 1] = bf16_hi(raw[j][q]);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[j * 4 + q] = __uint_as_float(raw[j][q]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+#pragma unroll
+      for (int k = 0; k < V8; ++k) {
+        const int off = base + j * (kWave * V8) + k;
+        x[j * V8 + k] = off < V ? to_f32(row[off]) : -__builtin_inff();
+      }
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ float lane_max(const float (&x)[N]) {
+  float m = x[0];
+#pragma unroll
+  for (int e = 1; e < N; ++e) m = fmaxf(m, x[e]);
+  return m;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes in lane order.
+__device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    double u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Block-wide reductions for a 256-thread block; `sh` is kWavesPerBlock doubles of LDS.
+__device__ __forceinline__ double block_sum(double v, double* sh) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  v = wave_sum(v);
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  double r = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWavesPerBlock; ++i) r += sh[i];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float block_max(float v, float* sh) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  v = wave_max(v);
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  float r = sh[0];
+#pragma unroll
+  for (int i = 1; i < kWavesPerBlock; ++i) r = fmaxf(r, sh[i]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ int block_min(int v, int* sh) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  v = wave_min(v);
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  int r = sh[0];
+#pragma unroll
+  for (int i = 1; i < kWavesPerBlock; ++i) r = min(r, sh[i]);
+  __syncthreads();
+  return r;
+}
+
+// Fast 2^((x - m) * s) for the row statistics pass: hardware v_exp_f32 on a
+// float32 argument.  Used where relative errors of ~1e-7 are harmless.
+__device__ __forceinline__ float exp2_fast(float a) { return __builtin_amdgcn_exp2f(a); }
+
+// Accurate 2^((x - m) * s) with s = s_hi + s_lo given as a float pair.  The
+// rounding error of the product d*s_hi is recovered exactly with an FMA and,
+// with d*s_lo, applied as the first-order factor (1 + lo*ln2).  What remains
+// is v_exp_f32's own error (< 0.8 ulp on gfx950) plus one rounding.  x - m is
+// exact for bf16 operands whose exponents are within 16 of each other.
+// Returns 0 for x = -inf and for results below 2^-200.
+__device__ __forceinline__ float exp2_accurate(float x, float m, float s_hi, float s_lo) {
+  constexpr float kLn2 = 0.693147180559945309f;
+  const float d = x - m;
+  const float hi = d * s_hi;
+  float lo = __builtin_fmaf(d, s_hi, -hi);
+  lo = __builtin_fmaf(d, s_lo, lo);
+  const float e = __builtin_amdgcn_exp2f(hi);
+  const float r = __builtin_fmaf(e, lo * kLn2, e);
+  return hi < -200.0f ? 0.0f : r;
+}
+
+// Arrival at a per-sequence counter.  Every wave publishes its partial results
+// (release at agent scope, so other XCDs see them), the block synchronises,
+// and thread 0 counts the block in.  Returns true in every thread of the block
+// that arrives last; that block then owns the sequence's counter and resets it.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total, int* sh_flag) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *sh_flag = (old == total - 1u);
+  }
+  __syncthreads();
+  const bool last = *sh_flag != 0;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
+}
+
+}  // namespace sv

@@ -1,0 +1,72 @@
+// Internal launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sv {
+
+// Per-tile partial of the row-statistics pass: tile max and sum of 2^((x-max)*s).
+struct TileStat {
+  float m;
+  float s;
+};
+
+// Per-tile partial of the sampling pass (see sample_kernel).
+struct SampleTile {
+  double mt, md;   // tile maxima of the target / draft row (as double)
+  double zt, zd;   // sums of the accurate 2^((x - tile max) * s) over the tile
+  double g, h;     // the same sums restricted to the residual's positive set
+};
+
+struct ArgTile {
+  float v;
+  int i;
+};
+
+struct VerifyShape {
+  int B, K, V;
+  int dtype;     // 0 f32, 1 bf16
+  bool aligned;  // 16-byte aligned rows and V % (16 / sizeof(elem)) == 0
+  int tile;      // elements per tile (one wave)
+  int NT;        // tiles per row
+  int NG;        // blocks (4 tiles each) per row
+};
+
+struct VerifyWorkspace {
+  uint32_t* counter_a;  // [B] arrivals of the statistics pass
+  uint32_t* counter_b;  // [B] arrivals of the sampling pass (greedy uses this one)
+  TileStat* part_a;     // [B][2K][NT]
+  float* row_m;         // [B][2K]
+  double* row_z;        // [B][2K]
+  int32_t* job;         // [B] position to sample, or -1 for a faulty sequence
+  SampleTile* part_b;   // [B][NT]
+  ArgTile* part_g;      // [B][K+1][NT]
+};
+
+struct VerifyIO {
+  const void* target;
+  const void* draft;
+  const int32_t* tokens;
+  const float* uniforms;
+  float temperature;
+  int32_t* accepted_len;
+  int32_t* out_tokens;
+  float* p_target;
+  float* p_draft;
+};
+
+int tile_elems(int dtype);
+VerifyShape make_shape(int B, int K, int V, int dtype, bool aligned);
+size_t verify_workspace_layout(const VerifyShape& s, bool greedy, void* base, VerifyWorkspace* out);
+
+hipError_t launch_stats(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);
+hipError_t launch_sample(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);
+hipError_t launch_greedy(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);
+
+hipError_t launch_head(const void* h, const void* W, const int32_t* cluster_ids, int B, int K, int d, int V,
+                       int cluster_size, int n_sel, float* compact, void* dense, int dense_dtype,
+                       hipStream_t st);
+
+}  // namespace sv

@@ -1,0 +1,694 @@
+// Speculative-sampling verify kernels for gfx950.
+//
+// SAMPLE mode runs two kernels on the caller's stream.
+//
+//  1. stats_kernel streams target rows 0..K-1 and draft rows 0..K-1 once.
+//     One wave owns one tile (8 KiB) of one row: 16-byte loads, a per-lane
+//     maximum, 2^((x - max) * log2(e)/T) with v_exp_f32, and a wave reduction
+//     to a (tile max, tile sum) partial.  The last block of a sequence to
+//     arrive combines the partials into (max, Z) per row, evaluates
+//     P_t,i(d_i) and P_d,i(d_i) in double, takes every accept decision
+//     u < min(1, P_t/P_d) and finds the first rejection n (Speculative
+//     Decoding lesson, nextadmin.net, "Core algorithm" steps 4-5, "Step 1").
+//
+//  2. sample_kernel re-reads only what the output token at n needs: target
+//     and draft row n at a rejection (residual (P_t - P_d)_+, "Step 2"), or
+//     target row K when every draft was accepted (bonus token, step 6).  It
+//     recomputes every element with a compensated exponential, sums in double,
+//     and the sequence's last block turns the tile masses into an inverse-CDF
+//     choice of tile, then scans that one tile in token-id order.
+//
+// The statistics pass is deliberately cheap (its normalisers only decide
+// accept tests, ~1e-7 relative is ample); the sampling pass recomputes the
+// normalisers of the row pair it samples from with the accurate exponential,
+// so the inverse-CDF boundaries carry only per-element rounding.
+//
+// GREEDY mode runs greedy_kernel: an argmax (first index on ties) per target
+// row and the longest prefix of drafts equal to those argmaxes
+// (LLMs-from-Scratch lesson 25, "Greedy case").
+
+#include <math.h>
+
+#include "sv_common.h"
+#include "sv_internal.h"
+
+namespace sv {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+
+struct StatsArgs {
+  const void* target;
+  const void* draft;
+  const int32_t* tokens;
+  const float* uniforms;
+  int B, K, V, NT, NG;
+  float s_hi;  // log2(e)/T rounded to float
+  double T;
+  TileStat* part;
+  uint32_t* counter;
+  float* row_m;
+  double* row_z;
+  int32_t* job;
+  int32_t* accepted_len;
+  int32_t* out_tokens;
+  float* p_t_out;
+  float* p_d_out;
+};
+
+template <typename T>
+__device__ __forceinline__ const T* row_ptr(const void* base, size_t rows_before, int V) {
+  return static_cast<const T*>(base) + rows_before * (size_t)V;
+}
+
+// ---------------------------------------------------------------------------
+// Row statistics and accept decisions.
+// ---------------------------------------------------------------------------
+
+template <typename T>
+__device__ void finalize_stats(const StatsArgs& a, int b) {
+  __shared__ float sh_m[2 * kMaxK];
+  __shared__ double sh_z[2 * kMaxK];
+  __shared__ int sh_acc[kMaxK];
+  __shared__ int sh_bad;
+  __shared__ int sh_n;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int K = a.K, R = 2 * K;
+  if (threadIdx.x == 0) sh_bad = 0;
+
+  for (int r = wave; r < R; r += kWavesPerBlock) {
+    const TileStat* p = a.part + ((size_t)b * R + r) * a.NT;
+    float m = kNegInf;
+    for (int t = lane; t < a.NT; t += kWave) m = fmaxf(m, p[t].m);
+    m = wave_max(m);
+    double z = 0.0;
+    if (m != kNegInf) {
+      for (int t = lane; t < a.NT; t += kWave) {
+        const TileStat q = p[t];
+        if (q.m != kNegInf) z += (double)q.s * (double)exp2_fast((q.m - m) * a.s_hi);
+      }
+    }
+    z = wave_sum(z);
+    if (lane == 0) {
+      sh_m[r] = m;
+      sh_z[r] = z;
+      a.row_m[(size_t)b * R + r] = m;
+      a.row_z[(size_t)b * R + r] = z;
+    }
+  }
+  __syncthreads();
+
+  double pt = __builtin_nan(""), pd = __builtin_nan("");
+  if ((int)threadIdx.x < K) {
+    const int i = threadIdx.x;
+    const int d = a.tokens[(size_t)b * K + i];
+    const float mt = sh_m[i], md = sh_m[K + i];
+    const double zt = sh_z[i], zd = sh_z[K + i];
+    const bool bad = d < 0 || d >= a.V || !isfinite(mt) || !isfinite(md) || !(zt > 0.0) || !isfinite(zt) ||
+                     !(zd > 0.0) || !isfinite(zd);
+    int acc = 0;
+    if (!bad) {
+      const T* trow = row_ptr<T>(a.target, (size_t)b * (K + 1) + i, a.V);
+      const T* drow = row_ptr<T>(a.draft, (size_t)b * K + i, a.V);
+      const double xt = (double)to_f32(trow[d]);
+      const double xd = (double)to_f32(drow[d]);
+      pt = exp((xt - (double)mt) / a.T) / zt;
+      pd = exp((xd - (double)md) / a.T) / zd;
+      const double ratio = pd > 0.0 ? pt / pd : __builtin_inf();
+      const double thr = ratio < 1.0 ? ratio : 1.0;
+      acc = (double)a.uniforms[((size_t)b * (K + 1) + i) * 2] < thr;
+    } else {
+      atomicOr(&sh_bad, 1);
+    }
+    sh_acc[i] = acc;
+  }
+  __syncthreads();
+  const bool bad = sh_bad != 0;
+  if ((int)threadIdx.x < K) {
+    const int i = threadIdx.x;
+    if (a.p_t_out) a.p_t_out[(size_t)b * K + i] = bad ? __builtin_nanf("") : (float)pt;
+    if (a.p_d_out) a.p_d_out[(size_t)b * K + i] = bad ? __builtin_nanf("") : (float)pd;
+  }
+  if (threadIdx.x == 0) {
+    int n = K;
+    for (int i = 0; i < K; ++i)
+      if (!sh_acc[i]) {
+        n = i;
+        break;
+      }
+    if (bad) n = -1;
+    sh_n = n;
+    a.job[b] = n;
+    a.accepted_len[b] = n;
+    a.counter[b] = 0u;  // every block of this sequence has arrived
+  }
+  __syncthreads();
+  const int n = sh_n;
+  for (int i = threadIdx.x; i <= K; i += kBlock)
+    a.out_tokens[(size_t)b * (K + 1) + i] = (n >= 0 && i < n) ? a.tokens[(size_t)b * K + i] : -1;
+}
+
+template <typename T, bool kAligned>
+__global__ void __launch_bounds__(kBlock) stats_kernel(StatsArgs a) {
+  __shared__ int sh_flag;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int K = a.K, R = 2 * K;
+  const int g = blockIdx.x % a.NG;
+  const int rb = blockIdx.x / a.NG;
+  const int r = rb % R;
+  const int b = rb / R;
+  const T* row = r < K ? row_ptr<T>(a.target, (size_t)b * (K + 1) + r, a.V)
+                       : row_ptr<T>(a.draft, (size_t)b * K + (r - K), a.V);
+  const int t = g * kWavesPerBlock + wave;
+  if (t < a.NT) {
+    float x[kPerLane<T>];
+    load_tile<T, kAligned>(row, a.V, t, lane, x);
+    const float ml = lane_max(x);
+    float sl = 0.0f;
+    if (ml != kNegInf) {
+#pragma unroll
+      for (int e = 0; e < kPerLane<T>; ++e) sl += exp2_fast((x[e] - ml) * a.s_hi);
+    }
+    const float M = wave_max(ml);
+    const float scaled = ml == kNegInf ? 0.0f : sl * exp2_fast((ml - M) * a.s_hi);
+    const float S = wave_sum(scaled);
+    if (lane == 0) a.part[((size_t)b * R + r) * a.NT + t] = TileStat{M, S};
+  }
+  if (!arrive_last(a.counter + b, (uint32_t)(R * a.NG), &sh_flag)) return;
+  finalize_stats<T>(a, b);
+}
+
+// ---------------------------------------------------------------------------
+// Sampling: residual at the first rejection, or the bonus token.
+// ---------------------------------------------------------------------------
+
+struct SampleArgs {
+  const void* target;
+  const void* draft;
+  const float* uniforms;
+  int B, K, V, NT, NG;
+  float s_hi, s_lo;  // log2(e)/T as a float pair
+  double s64;        // log2(e)/T in double
+  const float* row_m;
+  const double* row_z;
+  const int32_t* job;
+  SampleTile* part;
+  uint32_t* counter;
+  int32_t* accepted_len;
+  int32_t* out_tokens;
+};
+
+// Everything the sampling of one sequence needs to agree on between the tile
+// pass and the final scan.
+struct SampleRow {
+  int n;
+  bool resid;
+  float m_t, m_d;    // statistics-pass row maxima (residual)
+  double za_t, za_d; // statistics-pass normalisers: decide the positive set only
+};
+
+template <typename T, bool kAligned>
+__device__ void finalize_sample(const SampleArgs& a, int b, const SampleRow& sr, const T* trow, const T* drow) {
+  __shared__ double sh_d[kWavesPerBlock];
+  __shared__ float sh_f[kWavesPerBlock];
+  __shared__ int sh_i[kWavesPerBlock];
+  __shared__ double sh_scan[kWavesPerBlock];
+  __shared__ double sh_cbefore;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int K = a.K, NT = a.NT, n = sr.n;
+  const SampleTile* P = a.part + (size_t)b * NT;
+  constexpr double kNegInfD = -__builtin_inf();
+
+  // Reference maximum: the statistics-pass maximum for a residual row pair, the
+  // maximum over tiles for the bonus row (the statistics pass skips row K).
+  float mref_t = sr.m_t;
+  if (!sr.resid) {
+    float mm = kNegInf;
+    for (int tt = threadIdx.x; tt < NT; tt += kBlock) mm = fmaxf(mm, (float)P[tt].mt);
+    mref_t = block_max(mm, sh_f);
+  }
+  // Accurate normalisers of the sampled row(s).
+  double zbt = 0.0, zbd = 0.0;
+  if (isfinite(mref_t)) {
+    for (int tt = threadIdx.x; tt < NT; tt += kBlock) {
+      const SampleTile q = P[tt];
+      if (q.mt != kNegInfD) zbt += q.zt * exp2((q.mt - (double)mref_t) * a.s64);
+      if (sr.resid && q.md != kNegInfD) zbd += q.zd * exp2((q.md - (double)sr.m_d) * a.s64);
+    }
+  }
+  zbt = block_sum(zbt, sh_d);
+  if (sr.resid) zbd = block_sum(zbd, sh_d);
+
+  if (!isfinite(mref_t) || !(zbt > 0.0) || !isfinite(zbt) || (sr.resid && (!(zbd > 0.0) || !isfinite(zbd)))) {
+    // A row without a finite maximum: the sequence is faulty.
+    for (int i = threadIdx.x; i <= K; i += kBlock) a.out_tokens[(size_t)b * (K + 1) + i] = -1;
+    if (threadIdx.x == 0) {
+      a.accepted_len[b] = -1;
+      a.counter[b] = 0u;
+    }
+    return;
+  }
+
+  auto tile_mass = [&](int tt, bool fallback) -> double {
+    const SampleTile q = P[tt];
+    const double gt = q.mt == kNegInfD ? 0.0 : exp2((q.mt - (double)mref_t) * a.s64) / zbt;
+    if (!sr.resid || fallback) return q.zt * gt;
+    const double gd = q.md == kNegInfD ? 0.0 : exp2((q.md - (double)sr.m_d) * a.s64) / zbd;
+    return q.g * gt - q.h * gd;
+  };
+
+  double S = 0.0;
+  for (int tt = threadIdx.x; tt < NT; tt += kBlock) S += tile_mass(tt, false);
+  S = block_sum(S, sh_d);
+  bool fallback = false;
+  if (sr.resid && !(S > 0.0)) {
+    // Rejection with no residual mass left by rounding: sample P_t instead.
+    fallback = true;
+    S = 0.0;
+    for (int tt = threadIdx.x; tt < NT; tt += kBlock) S += tile_mass(tt, true);
+    S = block_sum(S, sh_d);
+  }
+  const double target = (double)a.uniforms[((size_t)b * (K + 1) + n) * 2 + 1] * S;
+
+  // Tile holding the inverse-CDF point: block scan over tiles in id order.
+  int jstar = -1;
+  double cbefore = 0.0;
+  double offset = 0.0;
+  for (int c0 = 0; c0 < NT; c0 += kBlock) {
+    const int tt = c0 + threadIdx.x;
+    const double ms = tt < NT ? tile_mass(tt, fallback) : 0.0;
+    double incl = wave_inclusive_scan(ms, lane);
+    if (lane == kWave - 1) sh_scan[wave] = incl;
+    __syncthreads();
+    double before_wave = 0.0, total = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      if (w < wave) before_wave += sh_scan[w];
+      total += sh_scan[w];
+    }
+    __syncthreads();
+    incl += before_wave;
+    const bool cross = tt < NT && offset + incl > target;
+    const int first = block_min(cross ? tt : 0x7fffffff, sh_i);
+    if (first != 0x7fffffff) {
+      if (tt == first) sh_cbefore = offset + incl - ms;
+      __syncthreads();
+      cbefore = sh_cbefore;
+      jstar = first;
+      break;
+    }
+    offset += total;
+  }
+  bool no_cross = false;
+  if (jstar < 0) {
+    // Rounding left the point beyond the last boundary: take the last tile
+    // with mass, and in it the last element with positive weight.
+    int last = -1;
+    for (int tt = threadIdx.x; tt < NT; tt += kBlock)
+      if (tile_mass(tt, fallback) > 0.0) last = tt;
+    last = -block_min(-last, sh_i);
+    jstar = last;
+    no_cross = true;
+  }
+
+  if (wave == 0) {
+    int token = -1;
+    if (jstar >= 0) {
+      float x[kPerLane<T>];
+      load_tile<T, kAligned>(trow, a.V, jstar, lane, x);
+      const float mt = wave_max(lane_max(x));
+      const bool use_d = sr.resid && !fallback;
+      float y[kPerLane<T>];
+      float md = kNegInf;
+      if (use_d) {
+        load_tile<T, kAligned>(drow, a.V, jstar, lane, y);
+        md = wave_max(lane_max(y));
+      }
+      const double gt = mt == kNegInf ? 0.0 : exp2(((double)mt - (double)mref_t) * a.s64) / zbt;
+      const double gd = (!use_d || md == kNegInf) ? 0.0 : exp2(((double)md - (double)sr.m_d) * a.s64) / zbd;
+      const double ft = (!use_d || mt == kNegInf) ? 0.0 : exp2(((double)mt - (double)sr.m_t) * a.s64) / sr.za_t;
+      const double fd = (!use_d || md == kNegInf) ? 0.0 : exp2(((double)md - (double)sr.m_d) * a.s64) / sr.za_d;
+      constexpr int V8 = Elem<T>::kVec;
+      double running = cbefore;
+      int found = 0x7fffffff;
+      int last_pos = -1;
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) {
+        double cum[V8];
+        double acc = 0.0;
+#pragma unroll
+        for (int k = 0; k < V8; ++k) {
+          const int e = j * V8 + k;
+          const float et = mt == kNegInf ? 0.0f : exp2_accurate(x[e], mt, a.s_hi, a.s_lo);
+          double w;
+          if (use_d) {
+            const float ed = md == kNegInf ? 0.0f : exp2_accurate(y[e], md, a.s_hi, a.s_lo);
+            const bool pos = (double)et * ft > (double)ed * fd;
+            w = pos ? (double)et * gt - (double)ed * gd : 0.0;
+          } else {
+            w = (double)et * gt;
+          }
+          if (w > 0.0) last_pos = j * (kWave * V8) + lane * V8 + k;
+          acc += w;
+          cum[k] = acc;
+        }
+        const double incl = wave_inclusive_scan(acc, lane);
+        const double base = running + (incl - acc);
+        int mine = 0x7fffffff;
+        if (!no_cross) {
+#pragma unroll
+          for (int k = V8 - 1; k >= 0; --k)
+            if (base + cum[k] > target) mine = j * (kWave * V8) + lane * V8 + k;
+        }
+        const int f = wave_min(mine);
+        running += __shfl(incl, kWave - 1);
+        if (f != 0x7fffffff) {
+          found = f;
+          break;
+        }
+      }
+      if (found == 0x7fffffff) found = wave_max(last_pos);
+      token = found >= 0 ? jstar * kTile<T> + found : -1;
+    }
+    if (lane == 0) {
+      a.out_tokens[(size_t)b * (K + 1) + n] = token;
+      a.accepted_len[b] = token >= 0 ? n : -1;
+      if (token < 0)
+        for (int i = 0; i <= K; ++i) a.out_tokens[(size_t)b * (K + 1) + i] = -1;
+      a.counter[b] = 0u;
+    }
+  }
+}
+
+template <typename T, bool kAligned>
+__global__ void __launch_bounds__(kBlock) sample_kernel(SampleArgs a) {
+  __shared__ int sh_flag;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int K = a.K;
+  const int g = blockIdx.x % a.NG;
+  const int b = blockIdx.x / a.NG;
+  SampleRow sr;
+  sr.n = K == 0 ? 0 : a.job[b];
+  if (sr.n < 0) return;  // faulty sequence: the statistics pass wrote its outputs
+  sr.resid = sr.n < K;
+  sr.m_t = sr.m_d = 0.0f;
+  sr.za_t = sr.za_d = 1.0;
+  if (sr.resid) {
+    const size_t R = 2 * (size_t)K;
+    sr.m_t = a.row_m[b * R + sr.n];
+    sr.m_d = a.row_m[b * R + K + sr.n];
+    sr.za_t = a.row_z[b * R + sr.n];
+    sr.za_d = a.row_z[b * R + K + sr.n];
+  }
+  const T* trow = row_ptr<T>(a.target, (size_t)b * (K + 1) + sr.n, a.V);
+  const T* drow = sr.resid ? row_ptr<T>(a.draft, (size_t)b * K + sr.n, a.V) : nullptr;
+
+  const int t = g * kWavesPerBlock + wave;
+  if (t < a.NT) {
+    float x[kPerLane<T>];
+    load_tile<T, kAligned>(trow, a.V, t, lane, x);
+    const float mt = wave_max(lane_max(x));
+    double zt = 0.0, zd = 0.0, gs = 0.0, hs = 0.0;
+    float md = kNegInf;
+    if (!sr.resid) {
+      if (mt != kNegInf) {
+#pragma unroll
+        for (int e = 0; e < kPerLane<T>; ++e) zt += (double)exp2_accurate(x[e], mt, a.s_hi, a.s_lo);
+      }
+    } else {
+      float y[kPerLane<T>];
+      load_tile<T, kAligned>(drow, a.V, t, lane, y);
+      md = wave_max(lane_max(y));
+      // Per-tile factors to P_t and P_d with the statistics-pass normalisers:
+      // they decide only which elements are in the residual's positive set.
+      const double ft = mt == kNegInf ? 0.0 : exp2(((double)mt - (double)sr.m_t) * a.s64) / sr.za_t;
+      const double fd = md == kNegInf ? 0.0 : exp2(((double)md - (double)sr.m_d) * a.s64) / sr.za_d;
+#pragma unroll
+      for (int e = 0; e < kPerLane<T>; ++e) {
+        const float et = mt == kNegInf ? 0.0f : exp2_accurate(x[e], mt, a.s_hi, a.s_lo);
+        const float ed = md == kNegInf ? 0.0f : exp2_accurate(y[e], md, a.s_hi, a.s_lo);
+        const double etd = (double)et, edd = (double)ed;
+        zt += etd;
+        zd += edd;
+        if (etd * ft > edd * fd) {
+          gs += etd;
+          hs += edd;
+        }
+      }
+    }
+    zt = wave_sum(zt);
+    zd = wave_sum(zd);
+    gs = wave_sum(gs);
+    hs = wave_sum(hs);
+    if (lane == 0) a.part[(size_t)b * a.NT + t] = SampleTile{(double)mt, (double)md, zt, zd, gs, hs};
+  }
+  if (!arrive_last(a.counter + b, (uint32_t)a.NG, &sh_flag)) return;
+  finalize_sample<T, kAligned>(a, b, sr, trow, drow);
+}
+
+// ---------------------------------------------------------------------------
+// Greedy verify.
+// ---------------------------------------------------------------------------
+
+struct GreedyArgs {
+  const void* target;
+  const int32_t* tokens;
+  int B, K, V, NT, NG;
+  ArgTile* part;
+  uint32_t* counter;
+  int32_t* accepted_len;
+  int32_t* out_tokens;
+  float* p_t_out;
+  float* p_d_out;
+};
+
+__device__ __forceinline__ void argmax_merge(float& best, int& idx, float ob, int oi) {
+  if (ob > best || (ob == best && oi < idx)) {
+    best = ob;
+    idx = oi;
+  }
+}
+
+__device__ void finalize_greedy(const GreedyArgs& a, int b) {
+  __shared__ int sh_arg[kMaxK + 1];
+  __shared__ int sh_bad;
+  const int K = a.K, R = K + 1;
+  if (threadIdx.x == 0) sh_bad = 0;
+  __syncthreads();
+  if ((int)threadIdx.x < R) {
+    const int r = threadIdx.x;
+    const ArgTile* p = a.part + ((size_t)b * R + r) * a.NT;
+    float best = kNegInf;
+    int idx = 0x7fffffff;
+    for (int t = 0; t < a.NT; ++t) argmax_merge(best, idx, p[t].v, p[t].i);
+    if (!isfinite(best)) atomicOr(&sh_bad, 1);
+    sh_arg[r] = idx;
+  }
+  if ((int)threadIdx.x < K) {
+    const int d = a.tokens[(size_t)b * K + threadIdx.x];
+    if (d < 0 || d >= a.V) atomicOr(&sh_bad, 1);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const bool bad = sh_bad != 0;
+    int n = K;
+    for (int i = 0; i < K; ++i)
+      if (a.tokens[(size_t)b * K + i] != sh_arg[i]) {
+        n = i;
+        break;
+      }
+    int32_t* out = a.out_tokens + (size_t)b * R;
+    for (int i = 0; i <= K; ++i) out[i] = bad ? -1 : (i < n ? a.tokens[(size_t)b * K + i] : (i == n ? sh_arg[n] : -1));
+    a.accepted_len[b] = bad ? -1 : n;
+    a.counter[b] = 0u;
+  }
+  for (int i = threadIdx.x; i < K; i += kBlock) {
+    if (a.p_t_out) a.p_t_out[(size_t)b * K + i] = __builtin_nanf("");
+    if (a.p_d_out) a.p_d_out[(size_t)b * K + i] = __builtin_nanf("");
+  }
+}
+
+template <typename T, bool kAligned>
+__global__ void __launch_bounds__(kBlock) greedy_kernel(GreedyArgs a) {
+  __shared__ int sh_flag;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int K = a.K, R = K + 1;
+  const int g = blockIdx.x % a.NG;
+  const int rb = blockIdx.x / a.NG;
+  const int r = rb % R;
+  const int b = rb / R;
+  const T* row = row_ptr<T>(a.target, (size_t)b * R + r, a.V);
+  const int t = g * kWavesPerBlock + wave;
+  if (t < a.NT) {
+    float x[kPerLane<T>];
+    load_tile<T, kAligned>(row, a.V, t, lane, x);
+    float best = kNegInf;
+    int idx = 0x7fffffff;
+#pragma unroll
+    for (int e = 0; e < kPerLane<T>; ++e)
+      if (x[e] > best) {
+        best = x[e];
+        idx = t * kTile<T> + tile_offset<T>(e, lane);
+      }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ob = __shfl_xor(best, o);
+      const int oi = __shfl_xor(idx, o);
+      argmax_merge(best, idx, ob, oi);
+    }
+    if (lane == 0) a.part[((size_t)b * R + r) * a.NT + t] = ArgTile{best, idx};
+  }
+  if (!arrive_last(a.counter + b, (uint32_t)(R * a.NG), &sh_flag)) return;
+  finalize_greedy(a, b);
+}
+
+template <typename K1, typename K2, typename K3, typename K4, typename... Args>
+hipError_t dispatch4(int dtype, bool aligned, dim3 grid, hipStream_t st, K1 k_b_a, K2 k_b_u, K3 k_f_a, K4 k_f_u,
+                     Args... args) {
+  if (dtype == 1) {
+    if (aligned) hipLaunchKernelGGL(k_b_a, grid, dim3(kBlock), 0, st, args...);
+    else hipLaunchKernelGGL(k_b_u, grid, dim3(kBlock), 0, st, args...);
+  } else {
+    if (aligned) hipLaunchKernelGGL(k_f_a, grid, dim3(kBlock), 0, st, args...);
+    else hipLaunchKernelGGL(k_f_u, grid, dim3(kBlock), 0, st, args...);
+  }
+  return hipGetLastError();
+}
+
+double log2e_over(float temperature) { return 1.4426950408889634073599 / (double)temperature; }
+
+}  // namespace
+
+int tile_elems(int dtype) { return dtype == 1 ? kTile<uint16_t> : kTile<float>; }
+
+VerifyShape make_shape(int B, int K, int V, int dtype, bool aligned) {
+  VerifyShape s;
+  s.B = B;
+  s.K = K;
+  s.V = V;
+  s.dtype = dtype;
+  s.aligned = aligned;
+  s.tile = tile_elems(dtype);
+  s.NT = (V + s.tile - 1) / s.tile;
+  s.NG = (s.NT + kWavesPerBlock - 1) / kWavesPerBlock;
+  return s;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t verify_workspace_layout(const VerifyShape& s, bool greedy, void* base, VerifyWorkspace* out) {
+  const size_t B = (size_t)s.B, K = (size_t)s.K, NT = (size_t)s.NT;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  VerifyWorkspace w{};
+  const size_t o_ca = take(B * sizeof(uint32_t));
+  const size_t o_cb = take(B * sizeof(uint32_t));
+  size_t o_pa = 0, o_rm = 0, o_rz = 0, o_job = 0, o_pb = 0, o_pg = 0;
+  if (greedy) {
+    o_pg = take(B * (K + 1) * NT * sizeof(ArgTile));
+  } else {
+    o_pa = take(B * 2 * K * NT * sizeof(TileStat));
+    o_rm = take(B * 2 * K * sizeof(float));
+    o_rz = take(B * 2 * K * sizeof(double));
+    o_job = take(B * sizeof(int32_t));
+    o_pb = take(B * NT * sizeof(SampleTile));
+  }
+  if (out && base) {
+    char* p = static_cast<char*>(base);
+    w.counter_a = reinterpret_cast<uint32_t*>(p + o_ca);
+    w.counter_b = reinterpret_cast<uint32_t*>(p + o_cb);
+    if (greedy) {
+      w.part_g = reinterpret_cast<ArgTile*>(p + o_pg);
+    } else {
+      w.part_a = reinterpret_cast<TileStat*>(p + o_pa);
+      w.row_m = reinterpret_cast<float*>(p + o_rm);
+      w.row_z = reinterpret_cast<double*>(p + o_rz);
+      w.job = reinterpret_cast<int32_t*>(p + o_job);
+      w.part_b = reinterpret_cast<SampleTile*>(p + o_pb);
+    }
+    *out = w;
+  }
+  return off;
+}
+
+hipError_t launch_stats(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {
+  if (s.B == 0 || s.K == 0) return hipSuccess;
+  StatsArgs a{};
+  a.target = io.target;
+  a.draft = io.draft;
+  a.tokens = io.tokens;
+  a.uniforms = io.uniforms;
+  a.B = s.B;
+  a.K = s.K;
+  a.V = s.V;
+  a.NT = s.NT;
+  a.NG = s.NG;
+  a.s_hi = (float)log2e_over(io.temperature);
+  a.T = (double)io.temperature;
+  a.part = ws.part_a;
+  a.counter = ws.counter_a;
+  a.row_m = ws.row_m;
+  a.row_z = ws.row_z;
+  a.job = ws.job;
+  a.accepted_len = io.accepted_len;
+  a.out_tokens = io.out_tokens;
+  a.p_t_out = io.p_target;
+  a.p_d_out = io.p_draft;
+  const dim3 grid((unsigned)((size_t)s.B * 2 * s.K * s.NG));
+  return dispatch4(s.dtype, s.aligned, grid, st, stats_kernel<uint16_t, true>, stats_kernel<uint16_t, false>,
+                   stats_kernel<float, true>, stats_kernel<float, false>, a);
+}
+
+hipError_t launch_sample(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {
+  if (s.B == 0) return hipSuccess;
+  SampleArgs a{};
+  a.target = io.target;
+  a.draft = io.draft;
+  a.uniforms = io.uniforms;
+  a.B = s.B;
+  a.K = s.K;
+  a.V = s.V;
+  a.NT = s.NT;
+  a.NG = s.NG;
+  a.s64 = log2e_over(io.temperature);
+  a.s_hi = (float)a.s64;
+  a.s_lo = (float)(a.s64 - (double)a.s_hi);
+  a.row_m = ws.row_m;
+  a.row_z = ws.row_z;
+  a.job = ws.job;
+  a.part = ws.part_b;
+  a.counter = ws.counter_b;
+  a.accepted_len = io.accepted_len;
+  a.out_tokens = io.out_tokens;
+  const dim3 grid((unsigned)((size_t)s.B * s.NG));
+  return dispatch4(s.dtype, s.aligned, grid, st, sample_kernel<uint16_t, true>, sample_kernel<uint16_t, false>,
+                   sample_kernel<float, true>, sample_kernel<float, false>, a);
+}
+
+hipError_t launch_greedy(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {
+  if (s.B == 0) return hipSuccess;
+  GreedyArgs a{};
+  a.target = io.target;
+  a.tokens = io.tokens;
+  a.B = s.B;
+  a.K = s.K;
+  a.V = s.V;
+  a.NT = s.NT;
+  a.NG = s.NG;
+  a.part = ws.part_g;
+  a.counter = ws.counter_b;
+  a.accepted_len = io.accepted_len;
+  a.out_tokens = io.out_tokens;
+  a.p_t_out = io.p_target;
+  a.p_d_out = io.p_draft;
+  const dim3 grid((unsigned)((size_t)s.B * (s.K + 1) * s.NG));
+  return dispatch4(s.dtype, s.aligned, grid, st, greedy_kernel<uint16_t, true>, greedy_kernel<uint16_t, false>,
+                   greedy_kernel<float, true>, greedy_kernel<float, false>, a);
+}
+
+}  // namespace sv

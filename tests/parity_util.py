@@ -1,0 +1,118 @@
+"""Comparison of GPU verify outputs with the fp64 oracle (decision-level tie accounting).
+
+A verify call makes B*(K+1) decisions: K accept tests and one sampled (or
+argmax) token per sequence.  Outputs must match the oracle exactly, except
+that a disagreement is *excused* when the oracle's own margin for the first
+differing decision is below 1e-6 (|u - min(1, ratio)| for an accept test, the
+normalised distance of u*S to the nearest CDF boundary for a sample).  Once a
+sequence disagrees, its later decisions are not compared.  Any other
+disagreement fails.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+import oracle
+
+TIE_BAND = 1e-6
+PROB_RTOL = 1e-5
+
+
+@dataclasses.dataclass
+class Report:
+    decisions: int = 0
+    excused: int = 0
+    failures: list = dataclasses.field(default_factory=list)
+    prob_max_rel: float = 0.0
+
+    def merge(self, o: "Report"):
+        self.decisions += o.decisions
+        self.excused += o.excused
+        self.failures += o.failures
+        self.prob_max_rel = max(self.prob_max_rel, o.prob_max_rel)
+
+    @property
+    def excused_rate(self):
+        return self.excused / max(1, self.decisions)
+
+
+def compare(gpu_len, gpu_out, orc, K, greedy=False, gpu_pt=None, gpu_pd=None, seq_ids=None) -> Report:
+    gl = np.asarray(gpu_len)
+    go = np.asarray(gpu_out)
+    B = gl.shape[0]
+    rep = Report(decisions=B * (K + 1))
+    ids = np.arange(B) if seq_ids is None else np.asarray(seq_ids)
+    for b in range(B):
+        nl, no = int(gl[b]), int(orc["accepted_len"][b])
+        same = nl == no and np.array_equal(go[b], orc["out_tokens"][b])
+        if same:
+            continue
+        if nl < 0 or no < 0:
+            rep.failures.append((int(ids[b]), "faulty flag differs", nl, no))
+            continue
+        if greedy:
+            rep.failures.append((int(ids[b]), "greedy mismatch", go[b].tolist(), orc["out_tokens"][b].tolist()))
+            continue
+        if nl != no:
+            i = min(nl, no)
+            margin = float(orc["accept_margin"][b, i])
+            what = f"accept decision at {i}"
+        else:
+            margin = float(orc["sample_margin"][b])
+            what = f"sample at {no}"
+        if margin < TIE_BAND:
+            rep.excused += 1
+        else:
+            rep.failures.append((int(ids[b]), what, margin, go[b].tolist(), orc["out_tokens"][b].tolist()))
+    if gpu_pt is not None:
+        for gp, key in ((gpu_pt, "p_target"), (gpu_pd, "p_draft")):
+            g = np.asarray(gp, np.float64)
+            o = orc[key]
+            ok = np.isfinite(o)
+            if not np.array_equal(np.isfinite(g), ok):
+                rep.failures.append(("probability NaN pattern differs", key))
+                continue
+            if ok.any():
+                denom = np.maximum(np.abs(o[ok]), 1e-300)
+                rel = float(np.max(np.abs(g[ok] - o[ok]) / denom))
+                rep.prob_max_rel = max(rep.prob_max_rel, rel)
+    return rep
+
+
+def run_gpu(case, mode="sample", return_probs=True, **kw):
+    import speculative_sampling_verification_vocab_amd as sv
+    dev = torch.device("cuda", 0)
+    tgt = case.target.to(dev)
+    dr = case.draft.to(dev) if case.draft is not None else None
+    tok = case.draft_tokens.to(dev)
+    uni = case.uniforms.to(dev)
+    res = sv.spec_verify(tgt, dr, tok, uni, case.temperature if mode == "sample" else 0.0, mode,
+                         return_probs=return_probs, **kw)
+    torch.cuda.synchronize()
+    return [r.cpu().numpy() for r in res]
+
+
+def run_oracle(case, mode="sample", threads=None):
+    threads = threads or oracle.default_threads()
+    return oracle.verify(case.target, case.draft, case.draft_tokens, case.uniforms,
+                         case.temperature, mode=oracle.GREEDY if mode == "greedy" else oracle.SAMPLE,
+                         threads=threads)
+
+
+def check_case(case, mode="sample", max_excused_rate=None):
+    """Run both sides on one case and return the report (asserting no failure)."""
+    out = run_gpu(case, mode)
+    orc = run_oracle(case, mode)
+    if mode == "greedy":
+        rep = compare(out[0], out[1], orc, case.K, greedy=True)
+    else:
+        rep = compare(out[0], out[1], orc, case.K, gpu_pt=out[2], gpu_pd=out[3])
+    assert not rep.failures, rep.failures[:5]
+    if mode == "sample":
+        assert rep.prob_max_rel <= PROB_RTOL, rep.prob_max_rel
+    if max_excused_rate is not None:
+        assert rep.excused_rate <= max_excused_rate, (rep.excused, rep.decisions)
+    return rep, out, orc

@@ -1,0 +1,101 @@
+"""The C ABI library loads, exports what the header declares, sizes workspaces
+and rejects bad arguments on the host before touching the GPU.  CPU only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from speculative_sampling_verification_vocab_amd import _native
+    return _native.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("spec_verify", "spec_verify_timed", "spec_verify_workspace_bytes",
+              "spec_draft_head_shortlist", "spec_status_string", "spec_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    assert lib.spec_abi_version() == 1
+    for code in range(5):
+        s = lib.spec_status_string(code).decode()
+        assert s.startswith("SPEC_")
+    assert "unknown" in lib.spec_status_string(99).decode()
+
+
+def test_workspace_sizes(lib):
+    big = lib.spec_verify_workspace_bytes(256, 7, 262144, 1, 0)
+    assert 1 << 20 < big < 64 << 20
+    assert lib.spec_verify_workspace_bytes(0, 7, 262144, 1, 0) == 0
+    assert lib.spec_verify_workspace_bytes(4, 65, 1000, 1, 0) == 0      # K too large
+    assert lib.spec_verify_workspace_bytes(4, 3, 0, 1, 0) == 0          # V < 1
+    assert lib.spec_verify_workspace_bytes(4, 3, 1000, 7, 0) == 0       # bad dtype
+    g = lib.spec_verify_workspace_bytes(256, 7, 262144, 1, 1)
+    assert 0 < g < big
+
+
+def _call(lib, **over):
+    fake = ctypes.c_void_p(0x10000)   # never dereferenced: every case below fails validation first
+    args = dict(target=fake, draft=fake, tokens=fake, uni=fake, B=2, K=3, V=1000, dt=1, T=1.0, mode=0,
+                acc=fake, out=fake, pt=None, pd=None, ws=None, wsb=0, stream=None)
+    args.update(over)
+    return lib.spec_verify(args["target"], args["draft"], args["tokens"], args["uni"], args["B"], args["K"],
+                           args["V"], args["dt"], ctypes.c_float(args["T"]), args["mode"], args["acc"],
+                           args["out"], args["pt"], args["pd"], args["ws"], args["wsb"], args["stream"])
+
+
+def test_host_validation(lib):
+    INVALID, UNSUP, WS = 1, 2, 3
+    assert _call(lib, target=None) == INVALID
+    assert _call(lib, draft=None) == INVALID
+    assert _call(lib, tokens=None) == INVALID
+    assert _call(lib, uni=None) == INVALID
+    assert _call(lib, acc=None) == INVALID
+    assert _call(lib, out=None) == INVALID
+    assert _call(lib, T=0.0) == INVALID
+    assert _call(lib, T=-1.0) == INVALID
+    assert _call(lib, T=float("nan")) == INVALID
+    assert _call(lib, T=float("inf")) == INVALID
+    assert _call(lib, B=-1) == INVALID
+    assert _call(lib, V=0) == INVALID
+    assert _call(lib, dt=5) == INVALID
+    assert _call(lib, mode=3) == INVALID
+    assert _call(lib, K=65) == UNSUP
+    # the workspace is checked after the arguments: missing, too small, misaligned
+    assert _call(lib) == WS
+    assert _call(lib, ws=ctypes.c_void_p(0x10000), wsb=16) == WS
+    need = lib.spec_verify_workspace_bytes(2, 3, 1000, 1, 0)
+    assert _call(lib, ws=ctypes.c_void_p(0x10010), wsb=need) == WS
+    # greedy ignores temperature, draft logits and uniforms
+    assert _call(lib, mode=1, T=0.0, draft=None, uni=None) == WS
+    # B == 0 is a valid empty call
+    assert _call(lib, B=0) == 0
+
+
+def test_head_validation(lib):
+    fake = ctypes.c_void_p(0x10000)
+    f = lib.spec_draft_head_shortlist
+    assert f(fake, fake, fake, 2, 4, 64, 1000, 7, 2, fake, None, 0, None, 0, None) == 2   # V % cs
+    assert f(None, fake, fake, 2, 4, 64, 1000, 10, 2, fake, None, 0, None, 0, None) == 1
+    assert f(fake, fake, fake, 2, 4, 64, 1000, 10, 2, None, None, 0, None, 0, None) == 1
+    assert f(fake, fake, fake, 2, 4, 64, 1000, 10, 101, fake, None, 0, None, 0, None) == 1
+    assert f(fake, fake, fake, 0, 4, 64, 1000, 10, 2, fake, None, 0, None, 0, None) == 0

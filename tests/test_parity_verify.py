@@ -1,0 +1,165 @@
+"""GPU verify (SAMPLE and GREEDY) against the fp64 oracle, element by element.
+
+Sizes here are small enough for the oracle to finish in seconds while still
+spanning several tiles and a ragged tail; the full workloads are in
+test_parity_workloads.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+from tests.parity_util import check_case, compare, run_gpu, run_oracle
+from workloads import VerifyCase, verify_case, verify_uniforms
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(B, K, V, dtype, T=1.0, std=3.0, zipf=1.1, sigma=0.7, key=(7,)):
+    return verify_case(B, K, V, dtype, target_std=std, zipf_s=zipf, sigma=sigma, temperature=T, key=key)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [4096, 10000, 20000, 5003, 33, 1])
+def test_sample_shapes(dtype, V):
+    """Several tiles, a ragged last tile (10000, 20000), rows that are not
+    16-byte multiples (5003, 33) and a one-token vocabulary."""
+    print(f"case dtype={dtype} V={V}", flush=True)
+    c = _case(6, 3, V, dtype, key=(11, V))
+    rep, out, orc = check_case(c)
+    assert rep.excused <= 1
+
+
+@pytest.mark.parametrize("T", [0.37, 0.8, 2.5])
+def test_sample_temperatures(T):
+    print(f"case T={T}", flush=True)
+    c = _case(8, 4, 12345 * 8, "bf16", T=T, key=(12, int(T * 100)))
+    check_case(c)
+
+
+def test_sample_k0_only_bonus():
+    c = _case(5, 0, 9000, "bf16", key=(13,))
+    rep, out, orc = check_case(c)
+    assert np.all(out[0] == 0)
+
+
+def test_sample_identical_draft_accepts_all():
+    c = _case(8, 5, 30000, "bf16", sigma=0.0, key=(14,))
+    assert torch.equal(c.draft, c.target[:, :5])
+    rep, out, orc = check_case(c)
+    assert np.all(out[0] == 5)
+
+
+def test_sample_low_acceptance():
+    c = _case(16, 6, 20000, "bf16", sigma=4.0, key=(15,))
+    rep, out, orc = check_case(c)
+    assert np.mean(out[0]) < 2
+
+
+def test_faulty_sequences():
+    c = _case(6, 3, 8192, "bf16", key=(16,))
+    c.draft_tokens[1, 2] = 8192          # out of range
+    c.draft_tokens[2, 0] = -5
+    c.target[3, 1, :] = float("-inf")    # a row without a finite maximum
+    c.draft[4, 2, :] = float("-inf")
+    rep, out, orc = check_case(c)
+    for b in (1, 2, 3, 4):
+        assert out[0][b] == -1 and np.all(out[1][b] == -1)
+    assert out[0][0] >= 0 and out[0][5] >= 0
+
+
+def test_faulty_bonus_row_only_matters_when_sampled():
+    c = _case(4, 2, 4096, "bf16", sigma=0.0, key=(17,))
+    c.target[0, 2, :] = float("-inf")    # bonus row of sequence 0; all drafts accepted
+    rep, out, orc = check_case(c)
+    assert out[0][0] == -1 and orc["accepted_len"][0] == -1
+
+
+def test_shortlist_draft_rows_with_neg_inf():
+    """Draft rows that are -inf off a shortlist (P_d = 0 there)."""
+    c = _case(8, 4, 16384, "bf16", key=(18,))
+    mask = torch.ones(16384, dtype=torch.bool)
+    mask[::3] = False
+    c.draft[..., mask] = float("-inf")
+    # redraw draft tokens inside the shortlist
+    keep = torch.nonzero(~mask).flatten()
+    g = torch.Generator().manual_seed(5)
+    c.draft_tokens = keep[torch.randint(0, len(keep), (8, 4), generator=g)].to(torch.int32)
+    check_case(c)
+
+
+def test_zero_uniforms_and_near_one():
+    c = _case(8, 3, 8192, "bf16", key=(19,))
+    c.uniforms[:4] = 0.0
+    c.uniforms[4:] = 1.0 - 2.0 ** -24
+    check_case(c)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [50257, 4096, 7])
+def test_greedy(dtype, V):
+    g = torch.Generator().manual_seed(V)
+    B, K = 16, 5
+    # coarse values: ties are common and the lowest id must win
+    x = torch.randint(-20, 20, (B, K + 1, V), generator=g).to(torch.float32) * 0.25
+    x = x.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    a = torch.argmax(x.float(), dim=-1)
+    tok = a[:, :K].clone()
+    flip = torch.rand(B, K, generator=g) < 0.2
+    tok[flip] = torch.randint(0, V, (int(flip.sum()),), generator=g)
+    c = VerifyCase(x, None, tok.to(torch.int32), verify_uniforms(B, K, (1,)), 0.0, dtype)
+    check_case(c, mode="greedy")
+
+
+def test_greedy_faulty():
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(4, 3, 3000, generator=g).to(torch.bfloat16)
+    tok = torch.argmax(x[:, :2].float(), -1).to(torch.int32)
+    tok[1, 1] = 3000
+    x[2, 2] = float("-inf")
+    c = VerifyCase(x, None, tok, verify_uniforms(4, 2, (1,)), 0.0, "bf16")
+    rep, out, orc = check_case(c, mode="greedy")
+    assert out[0][1] == -1 and out[0][2] == -1
+
+
+def test_repeat_calls_are_identical():
+    """Bit-identical reruns (no float atomics; counters reset by the library)."""
+    c = _case(32, 5, 50000, "bf16", key=(20,))
+    a = run_gpu(c)
+    b = run_gpu(c)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_shape_change_reuses_workspace():
+    """A smaller call after a larger one on the same default workspace."""
+    c1 = _case(16, 6, 40000, "bf16", key=(21,))
+    c2 = _case(3, 2, 1000, "bf16", key=(22,))
+    check_case(c1)
+    check_case(c2)
+    check_case(c1)
+
+
+def test_chi_square_on_gpu():
+    """Emitted tokens follow P_t on V = 8 over 10^6 sequences (GPU output)."""
+    import scipy.special
+    import scipy.stats
+    import speculative_sampling_verification_vocab_amd as sv
+    rng = np.random.default_rng(42)
+    V, K, B = 8, 4, 1_000_000
+    xt = (rng.standard_normal((K + 1, V)) * 2).astype(np.float32)
+    xd = (xt[:K] + rng.standard_normal((K, V)) * 1.0).astype(np.float32)
+    pt = scipy.special.softmax(xt.astype(np.float64), axis=-1)
+    pd = scipy.special.softmax(xd.astype(np.float64), axis=-1)
+    tok = np.stack([rng.choice(V, size=B, p=pd[i]) for i in range(K)], axis=1).astype(np.int32)
+    uni = rng.random((B, K + 1, 2), dtype=np.float32)
+    dev = torch.device("cuda", 0)
+    tgt = torch.from_numpy(xt).to(dev).expand(B, K + 1, V).contiguous()
+    dr = torch.from_numpy(xd).to(dev).expand(B, K, V).contiguous()
+    n, out = sv.spec_verify(tgt, dr, torch.from_numpy(tok).to(dev), torch.from_numpy(uni).to(dev), 1.0)
+    n, out = n.cpu().numpy(), out.cpu().numpy()
+    for i in range(K + 1):
+        sel = n >= i
+        cnt = np.bincount(out[sel, i], minlength=V)
+        p = scipy.stats.chisquare(cnt, pt[i] * cnt.sum()).pvalue
+        assert p > 1e-3 / (K + 1), (i, p)
+        assert 0.5 * np.abs(cnt / cnt.sum() - pt[i]).sum() < 0.01

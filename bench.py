@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-sampling verify step on one MI355X.
+
+Default workload: B=256 sequences, K=7 draft positions, V=262144 vocabulary,
+bf16 logits (target N(0,3^2) plus a Zipf(1.1) log-prior, draft = target +
+N(0,0.7^2) noise, draft tokens sampled from the draft softmax), temperature 1,
+SAMPLE mode.  One step = one spec_verify call over the whole batch with its
+inputs already resident in HBM.
+
+Prints ONE JSON line on stdout:
+  value      verified draft positions per second, B*(K+1) / step time
+  roofline   the row-statistics kernel (the dominant one): algorithmic bytes
+             per launch (every logit of target and draft rows 0..K-1 read
+             once) / its average duration from HIP events on the launch
+             stream, against MI355X's 8 TB/s HBM peak; `traffic` is HBM
+             bytes per launch from the rocprofv3 PMC summary in profiles/
+             when that summary matches the current kernel source, else null.
+  cpu_baseline  the fp64 oracle timed on this host's cores on a sample of the
+             same batch (it is a baseline, not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILE_PMC = os.path.join(ROOT, "profiles", "stats_kernel_b256_k7_v262144_bf16_pmc.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "speculative_sampling_verification_vocab_amd", "csrc", f)
+                  for f in ("sv_verify.hip", "sv_common.h")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per stats-kernel launch from the committed PMC summary, if it
+    was taken on the current kernel source."""
+    if not os.path.exists(PROFILE_PMC):
+        return None
+    txt = open(PROFILE_PMC).read()
+    m_hash = re.search(r"source_sha256:\s*([0-9a-f]+)", txt)
+    m_tr = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_tr or m_hash.group(1) != source_hash():
+        return None
+    return float(m_tr.group(1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="b256_k7_v262144_bf16")
+    ap.add_argument("--mode", default="sample", choices=["sample", "greedy"])
+    ap.add_argument("--cpu-sample", type=int, default=32, help="sequences timed on the CPU oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
+                    help="also run one plain device copy of this many GiB (PMC scaling reference)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(verify shards over sequences with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import speculative_sampling_verification_vocab_amd as sv
+    from workloads import workload_case
+
+    dev = torch.device("cuda", 0)
+    t0 = time.time()
+    case = workload_case(args.workload, device=dev, greedy=args.mode == "greedy")
+    torch.cuda.synchronize()
+    B, K, V = case.B, case.K, case.V
+    esz = 2 if case.dtype == "bf16" else 4
+    log(f"inputs generated in {time.time() - t0:.1f}s: B={B} K={K} V={V} {case.dtype} T={case.temperature}")
+
+    if args.calibrate_copy_gib > 0:
+        n = int(args.calibrate_copy_gib * (1 << 30)) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n * 4} bytes read, {n * 4} bytes written")
+        del a, b
+
+    ws = sv.Workspace(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    NE = sv.TIMED_EVENTS
+
+    def mk_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(NE * n)]
+        for e in evs:
+            e.record(stream)  # creates the underlying hipEvent
+        return evs
+
+    draft = case.draft if args.mode == "sample" else None
+    uni = case.uniforms if args.mode == "sample" else None
+
+    def step(evs=None):
+        return sv.spec_verify(case.target, draft, case.draft_tokens, uni, case.temperature, args.mode,
+                              workspace=ws, events=evs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = mk_events(args.steps)
+    torch.cuda.synchronize()
+    start = time.perf_counter()
+    for s in range(args.steps):
+        res = step(evs[NE * s:NE * s + NE])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - start
+    ms_step = wall * 1e3 / args.steps
+
+    def span(i, j):
+        return float(np.mean([evs[NE * s + i].elapsed_time(evs[NE * s + j]) for s in range(args.steps)]))
+
+    k_ms = {"stats_or_greedy": span(0, 1), "accept_or_finalize": span(1, 2), "sample": span(2, 3),
+            "pick": span(3, 4), "events_step": span(0, 4)}
+    acc = res[0].float()
+    mean_tokens = float((acc[acc >= 0] + 1).mean()) if (acc >= 0).any() else float("nan")
+
+    positions = B * (K + 1)
+    value = positions / (ms_step * 1e-3)
+    if args.mode == "sample":
+        step_bytes = B * (2 * K + 1) * V * esz          # every logit read once
+        dom_bytes = B * 2 * K * V * esz                 # rows 0..K-1 of target and draft
+        dom_name, dom_ms = "stats_kernel (row statistics)", k_ms["stats_or_greedy"]
+    else:
+        step_bytes = B * (K + 1) * V * esz
+        dom_bytes = step_bytes
+        dom_name, dom_ms = "greedy_kernel (per-tile argmax)", k_ms["stats_or_greedy"]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile() if (args.workload == "b256_k7_v262144_bf16" and args.mode == "sample") else None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nb = min(args.cpu_sample, B)
+        sl = slice(0, nb)
+        tgt_h = case.target[sl].cpu()
+        dr_h = case.draft[sl].cpu() if args.mode == "sample" else None
+        tok_h = case.draft_tokens[sl].cpu()
+        uni_h = case.uniforms[sl].cpu()
+        threads = oracle.default_threads()
+        t1 = time.perf_counter()
+        orc = oracle.verify(tgt_h, dr_h, tok_h, uni_h, case.temperature,
+                            mode=oracle.GREEDY if args.mode == "greedy" else oracle.SAMPLE, threads=threads)
+        cpu_s = time.perf_counter() - t1
+        agree = int(np.sum(orc["accepted_len"] == res[0][sl].cpu().numpy()))
+        cpu = {"value": nb * (K + 1) / cpu_s, "unit": "positions/s", "cores": threads, "kind": "oracle",
+               "sample": f"first {nb} of {B} sequences of the same batch, fp64 C oracle, {threads} threads, "
+                         f"{cpu_s:.2f} s wall; accepted_len agrees on {agree}/{nb}"}
+
+    out = {
+        "metric": "verified draft positions/sec (B*(K+1)) and achieved HBM GB/s vs peak",
+        "value": value,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic (seeded generators; no dataset or model weights)",
+        "config": {"workload": args.workload, "B": B, "K": K, "V": V, "logits": case.dtype,
+                   "temperature": case.temperature, "mode": args.mode},
+        "achieved_gbs_step": step_bytes / (ms_step * 1e-3) / 1e9,
+        "hbm_frac_step": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "kernels_ms": k_ms,
+        "mean_tokens_per_verify": mean_tokens,
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": dom_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

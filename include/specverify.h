@@ -43,6 +43,7 @@ extern "C" {
 
 #define SPEC_ABI_VERSION 1
 #define SPEC_MAX_K 64
+#define SPEC_TIMED_EVENTS 5
 
 typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
 typedef enum { SPEC_MODE_SAMPLE = 0, SPEC_MODE_GREEDY = 1 } spec_mode_t;
@@ -51,7 +52,7 @@ typedef enum {
   SPEC_ERR_INVALID_ARG = 1, /* NULL pointer, negative size, bad temperature, bad enum, overflow */
   SPEC_ERR_UNSUPPORTED = 2, /* K > SPEC_MAX_K, V > 2^30, a grid too large for one launch, V % cluster_size != 0 */
   SPEC_ERR_WORKSPACE = 3,   /* workspace NULL, too small, or not 256-byte aligned */
-  SPEC_ERR_HIP = 4          /* a HIP launch failed; the workspace must be re-zeroed */
+  SPEC_ERR_HIP = 4          /* a HIP launch failed */
 } spec_status_t;
 
 /* Library ABI version (SPEC_ABI_VERSION of the build). */
@@ -62,10 +63,9 @@ const char* spec_status_string(spec_status_t status);
 
 /*
  * Workspace bytes spec_verify needs for this shape (0 when B == 0).
- * The workspace holds per-sequence arrival counters and partial row
- * statistics.  It must be zero-filled once before its first use; every call
- * that returns SPEC_OK leaves the counters at zero again, so the same buffer
- * can be reused by later calls of any shape that fits.
+ * The workspace holds per-tile partial results between the kernels of one
+ * call.  Its contents need no initialisation and carry nothing from one call
+ * to the next, so one buffer serves any later call whose size fits.
  */
 size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V, spec_dtype_t dtype,
                                    spec_mode_t mode);
@@ -94,7 +94,7 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V, spec_dtype_t
  *                  P_d,i(d_i) in SAMPLE mode, NaN in GREEDY mode or where a
  *                  sequence is faulty.
  *   workspace      device buffer of at least spec_verify_workspace_bytes(),
- *                  256-byte aligned, zero-filled before its first use.
+ *                  256-byte aligned.
  *
  * Logits must be finite or -inf (-inf marks tokens outside a shortlist).
  * The inverse-CDF sample picks the smallest token id v whose cumulative mass,
@@ -110,11 +110,11 @@ spec_status_t spec_verify(const void* target_logits, const void* draft_logits,
 
 /*
  * spec_verify with kernel timing.  Identical work and launches; in addition
- * events[0], events[1] and events[2] (hipEvent_t passed as void*, any may be
- * NULL) are recorded on `stream` before the first kernel, between the row
- * statistics kernel and the sampling kernel, and after the last kernel.
- * In GREEDY mode there is one kernel: events[1] and events[2] are recorded
- * after it.
+ * events[0..SPEC_TIMED_EVENTS-1] (hipEvent_t passed as void*, any may be NULL)
+ * are recorded on `stream`.  SAMPLE mode: [0] before the row-statistics
+ * kernel, [1] after it, [2] after the accept-decision kernel, [3] after the
+ * sampling kernel, [4] after the token-pick kernel.  GREEDY mode: [0] before
+ * the argmax kernel, [1] after it, [2], [3] and [4] after its finalize kernel.
  */
 spec_status_t spec_verify_timed(const void* target_logits, const void* draft_logits,
                                 const int32_t* draft_tokens, const float* uniforms,

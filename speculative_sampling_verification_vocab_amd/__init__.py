@@ -23,6 +23,7 @@ __all__ = ["spec_verify", "spec_verify_workspace_bytes", "spec_draft_head_shortl
 
 _DTYPES = {torch.bfloat16: _native.SPEC_BF16, torch.float32: _native.SPEC_F32}
 _MODES = {"sample": _native.SPEC_MODE_SAMPLE, "greedy": _native.SPEC_MODE_GREEDY}
+TIMED_EVENTS = 5
 
 
 def abi_version() -> int:
@@ -50,20 +51,18 @@ def spec_verify_workspace_bytes(B: int, K: int, V: int, dtype: torch.dtype, mode
 
 
 class Workspace:
-    """A zero-filled device buffer reused across calls (the library leaves it zeroed)."""
+    """A device scratch buffer reused across calls; it grows to the largest size asked for.
+
+    Calls that share one Workspace must be ordered on the GPU (same stream)."""
 
     def __init__(self, device):
         self.device = torch.device(device)
-        self.buf = torch.zeros(0, dtype=torch.uint8, device=self.device)
+        self.buf = torch.empty(0, dtype=torch.uint8, device=self.device)
 
     def get(self, nbytes: int) -> torch.Tensor:
         if self.buf.numel() < nbytes:
-            self.buf = torch.zeros(max(nbytes, 2 * self.buf.numel()), dtype=torch.uint8, device=self.device)
+            self.buf = torch.empty(max(nbytes, 2 * self.buf.numel()), dtype=torch.uint8, device=self.device)
         return self.buf
-
-    def reset(self):
-        """Re-zero after a failed call (the library cannot clean up after a failed launch)."""
-        self.buf.zero_()
 
 
 _default_ws = {}
@@ -85,8 +84,8 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_token
     target [B, K+1, V] and draft [B, K, V] (bf16 or float32), draft_tokens int32
     [B, K], uniforms float32 [B, K+1, 2].  Returns (accepted_len int32 [B],
     out_tokens int32 [B, K+1]) and, with return_probs, also (P_t(d), P_d(d))
-    float32 [B, K].  `events`: up to three torch.cuda.Event recorded around the
-    kernels (see spec_verify_timed in the C header).
+    float32 [B, K].  `events`: up to five recorded torch.cuda.Event objects,
+    re-recorded around the kernels (see spec_verify_timed in the C header).
     """
     if mode not in _MODES:
         raise ValueError(f"mode must be one of {list(_MODES)}")
@@ -129,8 +128,8 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_token
             B, K, V, dt, ctypes.c_float(temperature if mode == "sample" else 0.0), _MODES[mode],
             _ptr(acc), _ptr(out), _ptr(pt), _ptr(pd), _ptr(ws), ws.numel(), _stream_handle(dev, stream)]
     if events is not None:
-        evs = [ctypes.c_void_p(e.cuda_event if e is not None else 0) for e in list(events) + [None] * (3 - len(events))]
-        arr = (ctypes.c_void_p * 3)(*[e.value for e in evs])
+        evs = list(events) + [None] * (TIMED_EVENTS - len(events))
+        arr = (ctypes.c_void_p * TIMED_EVENTS)(*[e.cuda_event if e is not None else None for e in evs])
         st = lib.spec_verify_timed(*args, arr)
     else:
         st = lib.spec_verify(*args)

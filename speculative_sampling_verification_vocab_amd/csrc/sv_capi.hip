@@ -28,7 +28,7 @@ spec_status_t check_shape(int32_t B, int32_t K, int32_t V, spec_dtype_t dtype, s
   const sv::VerifyShape s = sv::make_shape(B, K, V, dtype == SPEC_BF16 ? 1 : 0, false);
   const size_t per_seq_rows = mode == SPEC_MODE_GREEDY ? (size_t)(K + 1) : (size_t)(2 * K);
   if ((size_t)B * per_seq_rows * (size_t)s.NG > kMaxGrid) return SPEC_ERR_UNSUPPORTED;
-  if ((size_t)B * (size_t)s.NG > kMaxGrid) return SPEC_ERR_UNSUPPORTED;
+  if ((size_t)B * (size_t)s.NG_s > kMaxGrid) return SPEC_ERR_UNSUPPORTED;
   return SPEC_OK;
 }
 
@@ -46,9 +46,7 @@ spec_status_t verify_impl(const void* target_logits, const void* draft_logits, c
     if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
   };
   if (B == 0) {
-    record(0);
-    record(1);
-    record(2);
+    for (int i = 0; i < SPEC_TIMED_EVENTS; ++i) record(i);
     return SPEC_OK;
   }
   if (!target_logits || !accepted_len || !out_tokens) return SPEC_ERR_INVALID_ARG;
@@ -84,12 +82,19 @@ spec_status_t verify_impl(const void* target_logits, const void* draft_logits, c
   if (sample) {
     e = sv::launch_stats(s, io, ws, st);
     record(1);
-    if (e == hipSuccess) e = sv::launch_sample(s, io, ws, st);
+    if (e == hipSuccess) e = sv::launch_accept(s, io, ws, st);
     record(2);
+    if (e == hipSuccess) e = sv::launch_sample(s, io, ws, st);
+    record(3);
+    if (e == hipSuccess) e = sv::launch_pick(s, io, ws, st);
+    record(4);
   } else {
     e = sv::launch_greedy(s, io, ws, st);
     record(1);
+    if (e == hipSuccess) e = sv::launch_greedy_finalize(s, io, ws, st);
     record(2);
+    record(3);
+    record(4);
   }
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }

@@ -9,7 +9,8 @@ namespace sv {
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = kWave * kWavesPerBlock;
-constexpr int kLoads = 8;  // 16-byte loads per lane per row tile
+constexpr int kLoads = 8;   // 16-byte loads per lane per tile of the streaming passes
+constexpr int kLoadsS = 4;  // 16-byte loads per lane per tile of the sampling pass
 constexpr int kMaxK = 64;
 
 // Storage element types: bf16 logits are handled as their uint16 bit patterns.
@@ -17,8 +18,10 @@ template <typename T> struct Elem;
 template <> struct Elem<uint16_t> { static constexpr int kVec = 8; };
 template <> struct Elem<float> { static constexpr int kVec = 4; };
 
-template <typename T> constexpr int kPerLane = Elem<T>::kVec * kLoads;  // 64 bf16, 32 f32
-template <typename T> constexpr int kTile = kWave * kPerLane<T>;         // 4096 bf16, 2048 f32
+template <typename T> constexpr int kPerLane = Elem<T>::kVec * kLoads;    // 64 bf16, 32 f32
+template <typename T> constexpr int kTile = kWave * kPerLane<T>;           // 4096 bf16, 2048 f32
+template <typename T> constexpr int kPerLaneS = Elem<T>::kVec * kLoadsS;  // 32 bf16, 16 f32
+template <typename T> constexpr int kTileS = kWave * kPerLaneS<T>;        // 2048 bf16, 1024 f32
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -37,18 +40,22 @@ __device__ __forceinline__ int tile_offset(int e, int lane) {
   return (e / V8) * (kWave * V8) + lane * V8 + (e % V8);
 }
 
-// Load the lane's kPerLane elements of tile t of a row of V logits as float;
-// ids >= V read as -inf.  kAligned requires a 16-byte aligned row and
-// V % kVec == 0, so a 16-byte vector is either fully inside the row or fully out.
-template <typename T, bool kAligned>
-__device__ __forceinline__ void load_tile(const T* __restrict__ row, int V, int t, int lane,
-                                          float (&x)[kPerLane<T>]) {
+// Load the lane's L*kVec elements of tile t (tiles of kWave*L*kVec ids) of a
+// row of V logits as float; ids >= V read as -inf.  kAligned requires a
+// 16-byte aligned row and V % kVec == 0, so a 16-byte vector is either fully
+// inside the row or fully out.  `first` skips the tile's first loads (a wave
+// that owns only part of a tile).
+template <typename T, bool kAligned, int L, int N>
+__device__ __forceinline__ void load_tile(const T* __restrict__ row, int V, int t, int lane, float (&x)[N],
+                                          int first = 0) {
   constexpr int V8 = Elem<T>::kVec;
-  const int base = t * kTile<T> + lane * V8;
+  static_assert(N % V8 == 0 && N / V8 <= L, "tile slice");
+  constexpr int kL = N / V8;
+  const int base = t * (kWave * L * V8) + first * (kWave * V8) + lane * V8;
   if constexpr (kAligned) {
-    u32x4 raw[kLoads];
+    u32x4 raw[kL];
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
+    for (int j = 0; j < kL; ++j) {
       const int off = base + j * (kWave * V8);
       if (off < V) {
         raw[j] = *reinterpret_cast<const u32x4*>(row + off);
@@ -58,7 +65,7 @@ __device__ __forceinline__ void load_tile(const T* __restrict__ row, int V, int 
       }
     }
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
+    for (int j = 0; j < kL; ++j) {
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -72,7 +79,7 @@ __device__ __forceinline__ void load_tile(const T* __restrict__ row, int V, int 
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
+    for (int j = 0; j < kL; ++j) {
 #pragma unroll
       for (int k = 0; k < V8; ++k) {
         const int off = base + j * (kWave * V8) + k;
@@ -178,6 +185,7 @@ __device__ __forceinline__ float exp2_fast(float a) { return __builtin_amdgcn_ex
 // exact for bf16 operands whose exponents are within 16 of each other.
 // Returns 0 for x = -inf and for results below 2^-200.
 __device__ __forceinline__ float exp2_accurate(float x, float m, float s_hi, float s_lo) {
+#pragma clang fp contract(off)
   constexpr float kLn2 = 0.693147180559945309f;
   const float d = x - m;
   const float hi = d * s_hi;
@@ -186,23 +194,6 @@ __device__ __forceinline__ float exp2_accurate(float x, float m, float s_hi, flo
   const float e = __builtin_amdgcn_exp2f(hi);
   const float r = __builtin_fmaf(e, lo * kLn2, e);
   return hi < -200.0f ? 0.0f : r;
-}
-
-// Arrival at a per-sequence counter.  Every wave publishes its partial results
-// (release at agent scope, so other XCDs see them), the block synchronises,
-// and thread 0 counts the block in.  Returns true in every thread of the block
-// that arrives last; that block then owns the sequence's counter and resets it.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total, int* sh_flag) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *sh_flag = (old == total - 1u);
-  }
-  __syncthreads();
-  const bool last = *sh_flag != 0;
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return last;
 }
 
 }  // namespace sv

@@ -32,16 +32,16 @@ struct VerifyShape {
   int tile;      // elements per tile (one wave)
   int NT;        // tiles per row
   int NG;        // blocks (4 tiles each) per row
+  int NT_s;      // sampling-pass tiles per row
+  int NG_s;      // sampling-pass blocks per row
 };
 
 struct VerifyWorkspace {
-  uint32_t* counter_a;  // [B] arrivals of the statistics pass
-  uint32_t* counter_b;  // [B] arrivals of the sampling pass (greedy uses this one)
   TileStat* part_a;     // [B][2K][NT]
   float* row_m;         // [B][2K]
   double* row_z;        // [B][2K]
   int32_t* job;         // [B] position to sample, or -1 for a faulty sequence
-  SampleTile* part_b;   // [B][NT]
+  SampleTile* part_b;   // [B][NT_s]
   ArgTile* part_g;      // [B][K+1][NT]
 };
 
@@ -61,9 +61,14 @@ int tile_elems(int dtype);
 VerifyShape make_shape(int B, int K, int V, int dtype, bool aligned);
 size_t verify_workspace_layout(const VerifyShape& s, bool greedy, void* base, VerifyWorkspace* out);
 
+// SAMPLE: stats -> accept -> sample -> pick.  GREEDY: greedy -> greedy_finalize.
 hipError_t launch_stats(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);
+hipError_t launch_accept(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);
 hipError_t launch_sample(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);
+hipError_t launch_pick(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);
 hipError_t launch_greedy(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);
+hipError_t launch_greedy_finalize(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws,
+                                  hipStream_t st);
 
 hipError_t launch_head(const void* h, const void* W, const int32_t* cluster_ids, int B, int K, int d, int V,
                        int cluster_size, int n_sel, float* compact, void* dense, int dense_dtype,

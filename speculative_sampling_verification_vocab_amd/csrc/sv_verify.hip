@@ -1,31 +1,35 @@
 // Speculative-sampling verify kernels for gfx950.
 //
-// SAMPLE mode runs two kernels on the caller's stream.
+// SAMPLE mode runs four kernels on the caller's stream.
 //
 //  1. stats_kernel streams target rows 0..K-1 and draft rows 0..K-1 once.
 //     One wave owns one tile (8 KiB) of one row: 16-byte loads, a per-lane
 //     maximum, 2^((x - max) * log2(e)/T) with v_exp_f32, and a wave reduction
-//     to a (tile max, tile sum) partial.  The last block of a sequence to
-//     arrive combines the partials into (max, Z) per row, evaluates
-//     P_t,i(d_i) and P_d,i(d_i) in double, takes every accept decision
-//     u < min(1, P_t/P_d) and finds the first rejection n (Speculative
-//     Decoding lesson, nextadmin.net, "Core algorithm" steps 4-5, "Step 1").
-//
-//  2. sample_kernel re-reads only what the output token at n needs: target
+//     to a (tile max, tile sum) partial.
+//  2. accept_kernel (one block per sequence) combines the partials into
+//     (max, Z) per row, evaluates P_t,i(d_i) and P_d,i(d_i) in double, takes
+//     every accept decision u < min(1, P_t/P_d) and finds the first rejection
+//     n (Speculative Decoding lesson, nextadmin.net, "Core algorithm" steps
+//     4-5, "Step 1").
+//  3. sample_kernel re-reads only what the output token at n needs: target
 //     and draft row n at a rejection (residual (P_t - P_d)_+, "Step 2"), or
 //     target row K when every draft was accepted (bonus token, step 6).  It
-//     recomputes every element with a compensated exponential, sums in double,
-//     and the sequence's last block turns the tile masses into an inverse-CDF
-//     choice of tile, then scans that one tile in token-id order.
+//     recomputes every element with a compensated exponential and sums per
+//     tile in double.
+//  4. pick_kernel (one block per sequence) turns the tile masses into an
+//     inverse-CDF choice of tile, then scans that one tile in token-id order.
+//
+// Kernel boundaries order the passes: partial results cross XCDs through
+// the end-of-kernel cache write-back instead of per-block fences.
 //
 // The statistics pass is deliberately cheap (its normalisers only decide
 // accept tests, ~1e-7 relative is ample); the sampling pass recomputes the
 // normalisers of the row pair it samples from with the accurate exponential,
 // so the inverse-CDF boundaries carry only per-element rounding.
 //
-// GREEDY mode runs greedy_kernel: an argmax (first index on ties) per target
-// row and the longest prefix of drafts equal to those argmaxes
-// (LLMs-from-Scratch lesson 25, "Greedy case").
+// GREEDY mode runs greedy_kernel (argmax per tile, first index on ties) and
+// greedy_finalize_kernel (argmax per row and the longest prefix of drafts equal
+// to those argmaxes; LLMs-from-Scratch lesson 25, "Greedy case").
 
 #include <math.h>
 
@@ -47,7 +51,6 @@ struct StatsArgs {
   float s_hi;  // log2(e)/T rounded to float
   double T;
   TileStat* part;
-  uint32_t* counter;
   float* row_m;
   double* row_z;
   int32_t* job;
@@ -141,7 +144,6 @@ __device__ void finalize_stats(const StatsArgs& a, int b) {
     sh_n = n;
     a.job[b] = n;
     a.accepted_len[b] = n;
-    a.counter[b] = 0u;  // every block of this sequence has arrived
   }
   __syncthreads();
   const int n = sh_n;
@@ -151,7 +153,6 @@ __device__ void finalize_stats(const StatsArgs& a, int b) {
 
 template <typename T, bool kAligned>
 __global__ void __launch_bounds__(kBlock) stats_kernel(StatsArgs a) {
-  __shared__ int sh_flag;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int K = a.K, R = 2 * K;
   const int g = blockIdx.x % a.NG;
@@ -163,7 +164,7 @@ __global__ void __launch_bounds__(kBlock) stats_kernel(StatsArgs a) {
   const int t = g * kWavesPerBlock + wave;
   if (t < a.NT) {
     float x[kPerLane<T>];
-    load_tile<T, kAligned>(row, a.V, t, lane, x);
+    load_tile<T, kAligned, kLoads>(row, a.V, t, lane, x);
     const float ml = lane_max(x);
     float sl = 0.0f;
     if (ml != kNegInf) {
@@ -175,8 +176,13 @@ __global__ void __launch_bounds__(kBlock) stats_kernel(StatsArgs a) {
     const float S = wave_sum(scaled);
     if (lane == 0) a.part[((size_t)b * R + r) * a.NT + t] = TileStat{M, S};
   }
-  if (!arrive_last(a.counter + b, (uint32_t)(R * a.NG), &sh_flag)) return;
-  finalize_stats<T>(a, b);
+}
+
+// One block per sequence, after stats_kernel: combine the tile partials and
+// take the accept decisions.
+template <typename T>
+__global__ void __launch_bounds__(kBlock) accept_kernel(StatsArgs a) {
+  finalize_stats<T>(a, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -187,48 +193,144 @@ struct SampleArgs {
   const void* target;
   const void* draft;
   const float* uniforms;
-  int B, K, V, NT, NG;
-  float s_hi, s_lo;  // log2(e)/T as a float pair
-  double s64;        // log2(e)/T in double
+  int B, K, V, NT, NG;  // NT, NG count sampling-pass tiles (kTileS ids) and blocks
+  float s_hi, s_lo;     // log2(e)/T as a float pair
+  double s64;           // log2(e)/T in double
   const float* row_m;
   const double* row_z;
   const int32_t* job;
   SampleTile* part;
-  uint32_t* counter;
   int32_t* accepted_len;
   int32_t* out_tokens;
 };
 
-// Everything the sampling of one sequence needs to agree on between the tile
-// pass and the final scan.
+// What the sampling of one sequence needs, shared by the tile pass and the pick.
 struct SampleRow {
   int n;
   bool resid;
-  float m_t, m_d;    // statistics-pass row maxima (residual)
-  double za_t, za_d; // statistics-pass normalisers: decide the positive set only
+  float m_t, m_d;     // statistics-pass row maxima (residual)
+  double za_t, za_d;  // statistics-pass normalisers: decide the positive set only
 };
 
+// Position to sample and the statistics-pass row data it needs; false for a
+// faulty sequence (the statistics pass already wrote its outputs).
+__device__ __forceinline__ bool load_sample_row(const SampleArgs& a, int b, SampleRow& sr) {
+  const int K = a.K;
+  sr.n = K == 0 ? 0 : a.job[b];
+  if (sr.n < 0) return false;
+  sr.resid = sr.n < K;
+  sr.m_t = sr.m_d = 0.0f;
+  sr.za_t = sr.za_d = 1.0;
+  if (sr.resid) {
+    const size_t R = 2 * (size_t)K;
+    sr.m_t = a.row_m[b * R + sr.n];
+    sr.m_d = a.row_m[b * R + K + sr.n];
+    sr.za_t = a.row_z[b * R + sr.n];
+    sr.za_d = a.row_z[b * R + K + sr.n];
+  }
+  return true;
+}
+
+// Per-tile ratio that decides the residual's positive set: element v of a tile
+// with maxima (mt, md) is in the set iff e_t * rho > e_d, i.e. P_t(v) > P_d(v)
+// with the statistics-pass normalisers.  Both sampling kernels evaluate this
+// same function, so they agree on the set.
+__device__ __forceinline__ float tile_rho(float mt, float md, const SampleRow& sr, double s64) {
+#pragma clang fp contract(off)
+  if (mt == kNegInf) return 0.0f;
+  if (md == kNegInf) return 1e30f;
+  const double lr = ((double)mt - (double)sr.m_t - ((double)md - (double)sr.m_d)) * s64 +
+                    log2(sr.za_d) - log2(sr.za_t);
+  const double r = exp2(fmin(fmax(lr, -99.0), 99.0));
+  return (float)r;
+}
+
+// Accurate 2^((x - tile max) * s) for a whole tile slice; 0 when the tile is all -inf.
+template <int N>
+__device__ __forceinline__ void tile_exp(const float (&x)[N], float m, float s_hi, float s_lo, float (&e)[N]) {
+  if (m == kNegInf) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) e[i] = 0.0f;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) e[i] = exp2_accurate(x[i], m, s_hi, s_lo);
+  }
+}
+
 template <typename T, bool kAligned>
-__device__ void finalize_sample(const SampleArgs& a, int b, const SampleRow& sr, const T* trow, const T* drow) {
+__global__ void __launch_bounds__(kBlock) sample_kernel(SampleArgs a) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int K = a.K;
+  const int g = blockIdx.x % a.NG;
+  const int b = blockIdx.x / a.NG;
+  SampleRow sr;
+  if (!load_sample_row(a, b, sr)) return;
+  const T* trow = row_ptr<T>(a.target, (size_t)b * (K + 1) + sr.n, a.V);
+  const int t = g * kWavesPerBlock + wave;
+  if (t >= a.NT) return;
+  constexpr int P = kPerLaneS<T>;
+  float x[P], e[P];
+  load_tile<T, kAligned, kLoadsS>(trow, a.V, t, lane, x);
+  const float mt = wave_max(lane_max(x));
+  double zt = 0.0, zd = 0.0, gs = 0.0, hs = 0.0;
+  float md = kNegInf;
+  if (!sr.resid) {
+    tile_exp(x, mt, a.s_hi, a.s_lo, e);
+#pragma unroll
+    for (int i = 0; i < P; ++i) zt += (double)e[i];
+  } else {
+    const T* drow = row_ptr<T>(a.draft, (size_t)b * K + sr.n, a.V);
+    float y[P], f[P];
+    load_tile<T, kAligned, kLoadsS>(drow, a.V, t, lane, y);
+    md = wave_max(lane_max(y));
+    tile_exp(x, mt, a.s_hi, a.s_lo, e);
+    tile_exp(y, md, a.s_hi, a.s_lo, f);
+    const float rho = tile_rho(mt, md, sr, a.s64);
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const double et = (double)e[i], ed = (double)f[i];
+      const bool pos = e[i] * rho > f[i];
+      zt += et;
+      zd += ed;
+      gs += pos ? et : 0.0;
+      hs += pos ? ed : 0.0;
+    }
+  }
+  zt = wave_sum(zt);
+  zd = wave_sum(zd);
+  gs = wave_sum(gs);
+  hs = wave_sum(hs);
+  if (lane == 0) a.part[(size_t)b * a.NT + t] = SampleTile{(double)mt, (double)md, zt, zd, gs, hs};
+}
+
+// One block per sequence, after sample_kernel: the inverse-CDF choice of tile
+// from the tile masses, then a four-wave scan of that tile in token-id order.
+template <typename T, bool kAligned>
+__global__ void __launch_bounds__(kBlock) pick_kernel(SampleArgs a) {
   __shared__ double sh_d[kWavesPerBlock];
   __shared__ float sh_f[kWavesPerBlock];
   __shared__ int sh_i[kWavesPerBlock];
   __shared__ double sh_scan[kWavesPerBlock];
   __shared__ double sh_cbefore;
+  const int b = blockIdx.x;
+  SampleRow sr;
+  if (!load_sample_row(a, b, sr)) return;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int K = a.K, NT = a.NT, n = sr.n;
+  const T* trow = row_ptr<T>(a.target, (size_t)b * (K + 1) + n, a.V);
+  const T* drow = sr.resid ? row_ptr<T>(a.draft, (size_t)b * K + n, a.V) : nullptr;
   const SampleTile* P = a.part + (size_t)b * NT;
   constexpr double kNegInfD = -__builtin_inf();
 
-  // Reference maximum: the statistics-pass maximum for a residual row pair, the
-  // maximum over tiles for the bonus row (the statistics pass skips row K).
+  // Reference maxima: statistics-pass maxima for a residual pair, the maximum
+  // over tiles for the bonus row (the statistics pass does not read row K).
   float mref_t = sr.m_t;
   if (!sr.resid) {
     float mm = kNegInf;
     for (int tt = threadIdx.x; tt < NT; tt += kBlock) mm = fmaxf(mm, (float)P[tt].mt);
     mref_t = block_max(mm, sh_f);
   }
-  // Accurate normalisers of the sampled row(s).
+  // Normalisers of the sampled rows from the accurate per-element values.
   double zbt = 0.0, zbd = 0.0;
   if (isfinite(mref_t)) {
     for (int tt = threadIdx.x; tt < NT; tt += kBlock) {
@@ -239,23 +341,20 @@ __device__ void finalize_sample(const SampleArgs& a, int b, const SampleRow& sr,
   }
   zbt = block_sum(zbt, sh_d);
   if (sr.resid) zbd = block_sum(zbd, sh_d);
-
   if (!isfinite(mref_t) || !(zbt > 0.0) || !isfinite(zbt) || (sr.resid && (!(zbd > 0.0) || !isfinite(zbd)))) {
-    // A row without a finite maximum: the sequence is faulty.
+    // A sampled row without a finite maximum: the sequence is faulty.
     for (int i = threadIdx.x; i <= K; i += kBlock) a.out_tokens[(size_t)b * (K + 1) + i] = -1;
-    if (threadIdx.x == 0) {
-      a.accepted_len[b] = -1;
-      a.counter[b] = 0u;
-    }
+    if (threadIdx.x == 0) a.accepted_len[b] = -1;
     return;
   }
 
+  // Tile scale factors: P_t(v) = e_t(v) * gt, P_d(v) = e_d(v) * gd.
+  auto scale_t = [&](double mt) { return mt == kNegInfD ? 0.0 : exp2((mt - (double)mref_t) * a.s64) / zbt; };
+  auto scale_d = [&](double md) { return md == kNegInfD ? 0.0 : exp2((md - (double)sr.m_d) * a.s64) / zbd; };
   auto tile_mass = [&](int tt, bool fallback) -> double {
     const SampleTile q = P[tt];
-    const double gt = q.mt == kNegInfD ? 0.0 : exp2((q.mt - (double)mref_t) * a.s64) / zbt;
-    if (!sr.resid || fallback) return q.zt * gt;
-    const double gd = q.md == kNegInfD ? 0.0 : exp2((q.md - (double)sr.m_d) * a.s64) / zbd;
-    return q.g * gt - q.h * gd;
+    if (!sr.resid || fallback) return q.zt * scale_t(q.mt);
+    return q.g * scale_t(q.mt) - q.h * scale_d(q.md);
   };
 
   double S = 0.0;
@@ -273,8 +372,7 @@ __device__ void finalize_sample(const SampleArgs& a, int b, const SampleRow& sr,
 
   // Tile holding the inverse-CDF point: block scan over tiles in id order.
   int jstar = -1;
-  double cbefore = 0.0;
-  double offset = 0.0;
+  double cbefore = 0.0, offset = 0.0;
   for (int c0 = 0; c0 < NT; c0 += kBlock) {
     const int tt = c0 + threadIdx.x;
     const double ms = tt < NT ? tile_mass(tt, fallback) : 0.0;
@@ -307,144 +405,74 @@ __device__ void finalize_sample(const SampleArgs& a, int b, const SampleRow& sr,
     int last = -1;
     for (int tt = threadIdx.x; tt < NT; tt += kBlock)
       if (tile_mass(tt, fallback) > 0.0) last = tt;
-    last = -block_min(-last, sh_i);
-    jstar = last;
+    jstar = -block_min(-last, sh_i);
     no_cross = true;
   }
-
-  if (wave == 0) {
-    int token = -1;
-    if (jstar >= 0) {
-      float x[kPerLane<T>];
-      load_tile<T, kAligned>(trow, a.V, jstar, lane, x);
-      const float mt = wave_max(lane_max(x));
-      const bool use_d = sr.resid && !fallback;
-      float y[kPerLane<T>];
-      float md = kNegInf;
-      if (use_d) {
-        load_tile<T, kAligned>(drow, a.V, jstar, lane, y);
-        md = wave_max(lane_max(y));
-      }
-      const double gt = mt == kNegInf ? 0.0 : exp2(((double)mt - (double)mref_t) * a.s64) / zbt;
-      const double gd = (!use_d || md == kNegInf) ? 0.0 : exp2(((double)md - (double)sr.m_d) * a.s64) / zbd;
-      const double ft = (!use_d || mt == kNegInf) ? 0.0 : exp2(((double)mt - (double)sr.m_t) * a.s64) / sr.za_t;
-      const double fd = (!use_d || md == kNegInf) ? 0.0 : exp2(((double)md - (double)sr.m_d) * a.s64) / sr.za_d;
-      constexpr int V8 = Elem<T>::kVec;
-      double running = cbefore;
-      int found = 0x7fffffff;
-      int last_pos = -1;
-#pragma unroll
-      for (int j = 0; j < kLoads; ++j) {
-        double cum[V8];
-        double acc = 0.0;
-#pragma unroll
-        for (int k = 0; k < V8; ++k) {
-          const int e = j * V8 + k;
-          const float et = mt == kNegInf ? 0.0f : exp2_accurate(x[e], mt, a.s_hi, a.s_lo);
-          double w;
-          if (use_d) {
-            const float ed = md == kNegInf ? 0.0f : exp2_accurate(y[e], md, a.s_hi, a.s_lo);
-            const bool pos = (double)et * ft > (double)ed * fd;
-            w = pos ? (double)et * gt - (double)ed * gd : 0.0;
-          } else {
-            w = (double)et * gt;
-          }
-          if (w > 0.0) last_pos = j * (kWave * V8) + lane * V8 + k;
-          acc += w;
-          cum[k] = acc;
-        }
-        const double incl = wave_inclusive_scan(acc, lane);
-        const double base = running + (incl - acc);
-        int mine = 0x7fffffff;
-        if (!no_cross) {
-#pragma unroll
-          for (int k = V8 - 1; k >= 0; --k)
-            if (base + cum[k] > target) mine = j * (kWave * V8) + lane * V8 + k;
-        }
-        const int f = wave_min(mine);
-        running += __shfl(incl, kWave - 1);
-        if (f != 0x7fffffff) {
-          found = f;
-          break;
-        }
-      }
-      if (found == 0x7fffffff) found = wave_max(last_pos);
-      token = found >= 0 ? jstar * kTile<T> + found : -1;
-    }
-    if (lane == 0) {
-      a.out_tokens[(size_t)b * (K + 1) + n] = token;
-      a.accepted_len[b] = token >= 0 ? n : -1;
-      if (token < 0)
-        for (int i = 0; i <= K; ++i) a.out_tokens[(size_t)b * (K + 1) + i] = -1;
-      a.counter[b] = 0u;
-    }
+  if (jstar < 0) {
+    for (int i = threadIdx.x; i <= K; i += kBlock) a.out_tokens[(size_t)b * (K + 1) + i] = -1;
+    if (threadIdx.x == 0) a.accepted_len[b] = -1;
+    return;
   }
-}
 
-template <typename T, bool kAligned>
-__global__ void __launch_bounds__(kBlock) sample_kernel(SampleArgs a) {
-  __shared__ int sh_flag;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int K = a.K;
-  const int g = blockIdx.x % a.NG;
-  const int b = blockIdx.x / a.NG;
-  SampleRow sr;
-  sr.n = K == 0 ? 0 : a.job[b];
-  if (sr.n < 0) return;  // faulty sequence: the statistics pass wrote its outputs
-  sr.resid = sr.n < K;
-  sr.m_t = sr.m_d = 0.0f;
-  sr.za_t = sr.za_d = 1.0;
-  if (sr.resid) {
-    const size_t R = 2 * (size_t)K;
-    sr.m_t = a.row_m[b * R + sr.n];
-    sr.m_d = a.row_m[b * R + K + sr.n];
-    sr.za_t = a.row_z[b * R + sr.n];
-    sr.za_d = a.row_z[b * R + K + sr.n];
+  // Scan of tile jstar: wave w owns the tile's load w (kWave*kVec consecutive
+  // ids).  The tile maxima and every element value are recomputed exactly as
+  // the tile pass computed them.
+  constexpr int V8 = Elem<T>::kVec;
+  static_assert(kLoadsS == kWavesPerBlock, "one load of the tile per wave");
+  const bool use_d = sr.resid && !fallback;
+  float x[V8], y[V8], e[V8], f[V8];
+  load_tile<T, kAligned, kLoadsS>(trow, a.V, jstar, lane, x, wave);
+  const float mt = block_max(lane_max(x), sh_f);
+  float md = kNegInf;
+  if (use_d) {
+    load_tile<T, kAligned, kLoadsS>(drow, a.V, jstar, lane, y, wave);
+    md = block_max(lane_max(y), sh_f);
   }
-  const T* trow = row_ptr<T>(a.target, (size_t)b * (K + 1) + sr.n, a.V);
-  const T* drow = sr.resid ? row_ptr<T>(a.draft, (size_t)b * K + sr.n, a.V) : nullptr;
-
-  const int t = g * kWavesPerBlock + wave;
-  if (t < a.NT) {
-    float x[kPerLane<T>];
-    load_tile<T, kAligned>(trow, a.V, t, lane, x);
-    const float mt = wave_max(lane_max(x));
-    double zt = 0.0, zd = 0.0, gs = 0.0, hs = 0.0;
-    float md = kNegInf;
-    if (!sr.resid) {
-      if (mt != kNegInf) {
+  const double gt = scale_t((double)mt);
+  const double gd = use_d ? scale_d((double)md) : 0.0;
+  tile_exp(x, mt, a.s_hi, a.s_lo, e);
+  double w[V8];
+  if (use_d) {
+    tile_exp(y, md, a.s_hi, a.s_lo, f);
+    const float rho = tile_rho(mt, md, sr, a.s64);
 #pragma unroll
-        for (int e = 0; e < kPerLane<T>; ++e) zt += (double)exp2_accurate(x[e], mt, a.s_hi, a.s_lo);
-      }
-    } else {
-      float y[kPerLane<T>];
-      load_tile<T, kAligned>(drow, a.V, t, lane, y);
-      md = wave_max(lane_max(y));
-      // Per-tile factors to P_t and P_d with the statistics-pass normalisers:
-      // they decide only which elements are in the residual's positive set.
-      const double ft = mt == kNegInf ? 0.0 : exp2(((double)mt - (double)sr.m_t) * a.s64) / sr.za_t;
-      const double fd = md == kNegInf ? 0.0 : exp2(((double)md - (double)sr.m_d) * a.s64) / sr.za_d;
+    for (int k = 0; k < V8; ++k) w[k] = e[k] * rho > f[k] ? (double)e[k] * gt - (double)f[k] * gd : 0.0;
+  } else {
 #pragma unroll
-      for (int e = 0; e < kPerLane<T>; ++e) {
-        const float et = mt == kNegInf ? 0.0f : exp2_accurate(x[e], mt, a.s_hi, a.s_lo);
-        const float ed = md == kNegInf ? 0.0f : exp2_accurate(y[e], md, a.s_hi, a.s_lo);
-        const double etd = (double)et, edd = (double)ed;
-        zt += etd;
-        zd += edd;
-        if (etd * ft > edd * fd) {
-          gs += etd;
-          hs += edd;
-        }
-      }
-    }
-    zt = wave_sum(zt);
-    zd = wave_sum(zd);
-    gs = wave_sum(gs);
-    hs = wave_sum(hs);
-    if (lane == 0) a.part[(size_t)b * a.NT + t] = SampleTile{(double)mt, (double)md, zt, zd, gs, hs};
+    for (int k = 0; k < V8; ++k) w[k] = (double)e[k] * gt;
   }
-  if (!arrive_last(a.counter + b, (uint32_t)a.NG, &sh_flag)) return;
-  finalize_sample<T, kAligned>(a, b, sr, trow, drow);
+  const int id0 = jstar * kTileS<T> + wave * (kWave * V8) + lane * V8;
+  double cum[V8];
+  double acc = 0.0;
+  int last_pos = -1;
+#pragma unroll
+  for (int k = 0; k < V8; ++k) {
+    acc += w[k];
+    cum[k] = acc;
+    if (w[k] > 0.0) last_pos = id0 + k;
+  }
+  const double incl = wave_inclusive_scan(acc, lane);
+  if (lane == kWave - 1) sh_scan[wave] = incl;
+  __syncthreads();
+  double before = cbefore;
+#pragma unroll
+  for (int v = 0; v < kWavesPerBlock; ++v)
+    if (v < wave) before += sh_scan[v];
+  const double base = before + (incl - acc);
+  int mine = 0x7fffffff;
+  if (!no_cross) {
+#pragma unroll
+    for (int k = V8 - 1; k >= 0; --k)
+      if (base + cum[k] > target) mine = id0 + k;
+  }
+  int token = block_min(mine, sh_i);
+  if (token == 0x7fffffff) token = -block_min(-last_pos, sh_i);
+  if (threadIdx.x == 0) {
+    a.out_tokens[(size_t)b * (K + 1) + n] = token;
+    a.accepted_len[b] = token >= 0 ? n : -1;
+    if (token < 0)
+      for (int i = 0; i <= K; ++i) a.out_tokens[(size_t)b * (K + 1) + i] = -1;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -456,7 +484,6 @@ struct GreedyArgs {
   const int32_t* tokens;
   int B, K, V, NT, NG;
   ArgTile* part;
-  uint32_t* counter;
   int32_t* accepted_len;
   int32_t* out_tokens;
   float* p_t_out;
@@ -501,7 +528,6 @@ __device__ void finalize_greedy(const GreedyArgs& a, int b) {
     int32_t* out = a.out_tokens + (size_t)b * R;
     for (int i = 0; i <= K; ++i) out[i] = bad ? -1 : (i < n ? a.tokens[(size_t)b * K + i] : (i == n ? sh_arg[n] : -1));
     a.accepted_len[b] = bad ? -1 : n;
-    a.counter[b] = 0u;
   }
   for (int i = threadIdx.x; i < K; i += kBlock) {
     if (a.p_t_out) a.p_t_out[(size_t)b * K + i] = __builtin_nanf("");
@@ -511,7 +537,6 @@ __device__ void finalize_greedy(const GreedyArgs& a, int b) {
 
 template <typename T, bool kAligned>
 __global__ void __launch_bounds__(kBlock) greedy_kernel(GreedyArgs a) {
-  __shared__ int sh_flag;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int K = a.K, R = K + 1;
   const int g = blockIdx.x % a.NG;
@@ -522,7 +547,7 @@ __global__ void __launch_bounds__(kBlock) greedy_kernel(GreedyArgs a) {
   const int t = g * kWavesPerBlock + wave;
   if (t < a.NT) {
     float x[kPerLane<T>];
-    load_tile<T, kAligned>(row, a.V, t, lane, x);
+    load_tile<T, kAligned, kLoads>(row, a.V, t, lane, x);
     float best = kNegInf;
     int idx = 0x7fffffff;
 #pragma unroll
@@ -539,9 +564,9 @@ __global__ void __launch_bounds__(kBlock) greedy_kernel(GreedyArgs a) {
     }
     if (lane == 0) a.part[((size_t)b * R + r) * a.NT + t] = ArgTile{best, idx};
   }
-  if (!arrive_last(a.counter + b, (uint32_t)(R * a.NG), &sh_flag)) return;
-  finalize_greedy(a, b);
 }
+
+__global__ void __launch_bounds__(kBlock) greedy_finalize_kernel(GreedyArgs a) { finalize_greedy(a, blockIdx.x); }
 
 template <typename K1, typename K2, typename K3, typename K4, typename... Args>
 hipError_t dispatch4(int dtype, bool aligned, dim3 grid, hipStream_t st, K1 k_b_a, K2 k_b_u, K3 k_f_a, K4 k_f_u,
@@ -572,6 +597,9 @@ VerifyShape make_shape(int B, int K, int V, int dtype, bool aligned) {
   s.tile = tile_elems(dtype);
   s.NT = (V + s.tile - 1) / s.tile;
   s.NG = (s.NT + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int tile_s = dtype == 1 ? kTileS<uint16_t> : kTileS<float>;
+  s.NT_s = (V + tile_s - 1) / tile_s;
+  s.NG_s = (s.NT_s + kWavesPerBlock - 1) / kWavesPerBlock;
   return s;
 }
 
@@ -585,9 +613,6 @@ size_t verify_workspace_layout(const VerifyShape& s, bool greedy, void* base, Ve
     off = align256(off + bytes);
     return at;
   };
-  VerifyWorkspace w{};
-  const size_t o_ca = take(B * sizeof(uint32_t));
-  const size_t o_cb = take(B * sizeof(uint32_t));
   size_t o_pa = 0, o_rm = 0, o_rz = 0, o_job = 0, o_pb = 0, o_pg = 0;
   if (greedy) {
     o_pg = take(B * (K + 1) * NT * sizeof(ArgTile));
@@ -596,12 +621,11 @@ size_t verify_workspace_layout(const VerifyShape& s, bool greedy, void* base, Ve
     o_rm = take(B * 2 * K * sizeof(float));
     o_rz = take(B * 2 * K * sizeof(double));
     o_job = take(B * sizeof(int32_t));
-    o_pb = take(B * NT * sizeof(SampleTile));
+    o_pb = take(B * (size_t)s.NT_s * sizeof(SampleTile));
   }
   if (out && base) {
+    VerifyWorkspace w{};
     char* p = static_cast<char*>(base);
-    w.counter_a = reinterpret_cast<uint32_t*>(p + o_ca);
-    w.counter_b = reinterpret_cast<uint32_t*>(p + o_cb);
     if (greedy) {
       w.part_g = reinterpret_cast<ArgTile*>(p + o_pg);
     } else {
@@ -616,8 +640,7 @@ size_t verify_workspace_layout(const VerifyShape& s, bool greedy, void* base, Ve
   return off;
 }
 
-hipError_t launch_stats(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {
-  if (s.B == 0 || s.K == 0) return hipSuccess;
+static StatsArgs stats_args(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws) {
   StatsArgs a{};
   a.target = io.target;
   a.draft = io.draft;
@@ -631,7 +654,6 @@ hipError_t launch_stats(const VerifyShape& s, const VerifyIO& io, const VerifyWo
   a.s_hi = (float)log2e_over(io.temperature);
   a.T = (double)io.temperature;
   a.part = ws.part_a;
-  a.counter = ws.counter_a;
   a.row_m = ws.row_m;
   a.row_z = ws.row_z;
   a.job = ws.job;
@@ -639,13 +661,10 @@ hipError_t launch_stats(const VerifyShape& s, const VerifyIO& io, const VerifyWo
   a.out_tokens = io.out_tokens;
   a.p_t_out = io.p_target;
   a.p_d_out = io.p_draft;
-  const dim3 grid((unsigned)((size_t)s.B * 2 * s.K * s.NG));
-  return dispatch4(s.dtype, s.aligned, grid, st, stats_kernel<uint16_t, true>, stats_kernel<uint16_t, false>,
-                   stats_kernel<float, true>, stats_kernel<float, false>, a);
+  return a;
 }
 
-hipError_t launch_sample(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {
-  if (s.B == 0) return hipSuccess;
+static SampleArgs sample_args(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws) {
   SampleArgs a{};
   a.target = io.target;
   a.draft = io.draft;
@@ -653,8 +672,8 @@ hipError_t launch_sample(const VerifyShape& s, const VerifyIO& io, const VerifyW
   a.B = s.B;
   a.K = s.K;
   a.V = s.V;
-  a.NT = s.NT;
-  a.NG = s.NG;
+  a.NT = s.NT_s;
+  a.NG = s.NG_s;
   a.s64 = log2e_over(io.temperature);
   a.s_hi = (float)a.s64;
   a.s_lo = (float)(a.s64 - (double)a.s_hi);
@@ -662,12 +681,40 @@ hipError_t launch_sample(const VerifyShape& s, const VerifyIO& io, const VerifyW
   a.row_z = ws.row_z;
   a.job = ws.job;
   a.part = ws.part_b;
-  a.counter = ws.counter_b;
   a.accepted_len = io.accepted_len;
   a.out_tokens = io.out_tokens;
-  const dim3 grid((unsigned)((size_t)s.B * s.NG));
+  return a;
+}
+
+hipError_t launch_stats(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {
+  if (s.B == 0 || s.K == 0) return hipSuccess;
+  const StatsArgs a = stats_args(s, io, ws);
+  const dim3 grid((unsigned)((size_t)s.B * 2 * s.K * s.NG));
+  return dispatch4(s.dtype, s.aligned, grid, st, stats_kernel<uint16_t, true>, stats_kernel<uint16_t, false>,
+                   stats_kernel<float, true>, stats_kernel<float, false>, a);
+}
+
+hipError_t launch_accept(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {
+  if (s.B == 0 || s.K == 0) return hipSuccess;
+  const StatsArgs a = stats_args(s, io, ws);
+  if (s.dtype == 1) hipLaunchKernelGGL(accept_kernel<uint16_t>, dim3(s.B), dim3(kBlock), 0, st, a);
+  else hipLaunchKernelGGL(accept_kernel<float>, dim3(s.B), dim3(kBlock), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {
+  if (s.B == 0) return hipSuccess;
+  const SampleArgs a = sample_args(s, io, ws);
+  const dim3 grid((unsigned)((size_t)s.B * s.NG_s));
   return dispatch4(s.dtype, s.aligned, grid, st, sample_kernel<uint16_t, true>, sample_kernel<uint16_t, false>,
                    sample_kernel<float, true>, sample_kernel<float, false>, a);
+}
+
+hipError_t launch_pick(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {
+  if (s.B == 0) return hipSuccess;
+  const SampleArgs a = sample_args(s, io, ws);
+  return dispatch4(s.dtype, s.aligned, dim3(s.B), st, pick_kernel<uint16_t, true>, pick_kernel<uint16_t, false>,
+                   pick_kernel<float, true>, pick_kernel<float, false>, a);
 }
 
 hipError_t launch_greedy(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {
@@ -681,7 +728,6 @@ hipError_t launch_greedy(const VerifyShape& s, const VerifyIO& io, const VerifyW
   a.NT = s.NT;
   a.NG = s.NG;
   a.part = ws.part_g;
-  a.counter = ws.counter_b;
   a.accepted_len = io.accepted_len;
   a.out_tokens = io.out_tokens;
   a.p_t_out = io.p_target;
@@ -689,6 +735,25 @@ hipError_t launch_greedy(const VerifyShape& s, const VerifyIO& io, const VerifyW
   const dim3 grid((unsigned)((size_t)s.B * (s.K + 1) * s.NG));
   return dispatch4(s.dtype, s.aligned, grid, st, greedy_kernel<uint16_t, true>, greedy_kernel<uint16_t, false>,
                    greedy_kernel<float, true>, greedy_kernel<float, false>, a);
+}
+
+hipError_t launch_greedy_finalize(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws,
+                                  hipStream_t st) {
+  if (s.B == 0) return hipSuccess;
+  GreedyArgs a{};
+  a.tokens = io.tokens;
+  a.B = s.B;
+  a.K = s.K;
+  a.V = s.V;
+  a.NT = s.NT;
+  a.NG = s.NG;
+  a.part = ws.part_g;
+  a.accepted_len = io.accepted_len;
+  a.out_tokens = io.out_tokens;
+  a.p_t_out = io.p_target;
+  a.p_d_out = io.p_draft;
+  hipLaunchKernelGGL(greedy_finalize_kernel, dim3(s.B), dim3(kBlock), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace sv

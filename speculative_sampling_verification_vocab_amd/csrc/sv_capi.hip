@@ -153,6 +153,8 @@ spec_status_t spec_draft_head_shortlist(const void* h, const void* W, const int3
   if (V % cluster_size != 0) return SPEC_ERR_UNSUPPORTED;
   if (n_sel > V / cluster_size) return SPEC_ERR_INVALID_ARG;
   if (B == 0 || K == 0) return SPEC_OK;
+  if (B > sv::head_max_contexts() || n_sel > 0xffff) return SPEC_ERR_UNSUPPORTED;
+  if ((size_t)B * (size_t)n_sel > 0x7fffffffu || (size_t)B * K * (size_t)V > SIZE_MAX / 8) return SPEC_ERR_INVALID_ARG;
   if (!h || !W || (!cluster_ids && n_sel > 0) || (!logits_compact && !dense_out)) return SPEC_ERR_INVALID_ARG;
   (void)hipGetLastError();
   const hipError_t e = sv::launch_head(h, W, cluster_ids, B, K, d, V, cluster_size, n_sel, logits_compact,

@@ -73,5 +73,6 @@ hipError_t launch_greedy_finalize(const VerifyShape& s, const VerifyIO& io, cons
 hipError_t launch_head(const void* h, const void* W, const int32_t* cluster_ids, int B, int K, int d, int V,
                        int cluster_size, int n_sel, float* compact, void* dense, int dense_dtype,
                        hipStream_t st);
+int head_max_contexts();
 
 }  // namespace sv

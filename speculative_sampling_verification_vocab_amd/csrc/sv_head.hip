@@ -6,9 +6,10 @@
 // Cluster-major gather-GEMM on bf16 MFMA (gfx950 v_mfma_f32_16x16x32_bf16,
 // fp32 accumulation).  One block owns a slab of 64 consecutive tokens of one
 // cluster (W rows are contiguous, so the slab is one 512 KiB block of W for
-// d = 4096).  It finds the contexts that selected the cluster, stages their
-// hidden rows in LDS chunk by chunk, and streams its W slab through MFMA once
-// per pass of up to 32 (context, position) rows.  The same block writes -inf
+// d = 4096).  It finds the contexts that selected the cluster and streams its
+// W slab through MFMA once per pass of up to 32 (context, position) rows,
+// staging W and the hidden rows through LDS so that global loads stay fully
+// coalesced while MFMA reads its lane-major fragments.  The same block writes -inf
 // into the dense output for every context that did not select the cluster, so
 // each dense element is written exactly once.
 
@@ -24,9 +25,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSlabTok = 64;       // tokens per block: 4 waves x 16 MFMA columns
 constexpr int kPassRows = 32;      // A rows per pass over W: two 16-row MFMA chunks
-constexpr int kDChunk = 512;       // hidden dims staged in LDS per step
-constexpr int kAStride = kDChunk + 8;  // LDS row stride: 16-byte skew per row avoids bank conflicts
-constexpr int kMaxCtx = 2048;      // contexts listed per cluster (host-checked: B <= kMaxCtx)
+constexpr int kStageK = 256;       // hidden dims per LDS stage
+constexpr int kLdsStride = kStageK + 8;  // bf16 per LDS row: 16-byte skew per row, no bank conflicts
+constexpr int kWLoads = kSlabTok * kStageK / 8 / kBlock;   // 16-byte W loads per thread per stage (8)
+constexpr int kALoads = kPassRows * kStageK / 8 / kBlock;  // 16-byte A loads per thread per stage (4)
+constexpr int kDepth = 1;          // stages of loads in flight ahead of the MFMAs (deeper measured slower)
+constexpr int kMaxCtx = 1024;      // contexts listed per cluster (host-checked: B <= kMaxCtx)
 
 struct HeadArgs {
   const uint16_t* h;    // bf16 [B, K, d]
@@ -51,11 +55,21 @@ __device__ __forceinline__ void store_dense(const HeadArgs& a, size_t idx, float
   else static_cast<float*>(a.dense)[idx] = v;
 }
 
+// 8 consecutive bf16 of a row starting at k (zero beyond d).
+__device__ __forceinline__ u32x4 load8(const uint16_t* row, int k, int d, int vec_ok) {
+  if (vec_ok && k + 8 <= d) return *reinterpret_cast<const u32x4*>(row + k);
+  uint32_t t4[4] = {0u, 0u, 0u, 0u};
+  for (int e = 0; e < 8; ++e)
+    if (k + e < d) t4[e >> 1] |= (uint32_t)row[k + e] << (16 * (e & 1));
+  return u32x4{t4[0], t4[1], t4[2], t4[3]};
+}
+
 __global__ void __launch_bounds__(kBlock) head_mfma_kernel(HeadArgs a) {
   __shared__ int sh_ctx[kMaxCtx];     // (b << 16) | s of every context that selected this cluster
   __shared__ uint32_t sh_sel[kMaxCtx / 32];
   __shared__ int sh_count;
-  __shared__ __attribute__((aligned(16))) uint16_t sh_a[kPassRows * kAStride];  // 32.5 KiB
+  __shared__ __attribute__((aligned(16))) uint16_t sh_w[kSlabTok * kLdsStride];   // 33 KiB
+  __shared__ __attribute__((aligned(16))) uint16_t sh_a[kPassRows * kLdsStride];  // 16.5 KiB
 
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int c = blockIdx.x;
@@ -106,76 +120,82 @@ __global__ void __launch_bounds__(kBlock) head_mfma_kernel(HeadArgs a) {
   if (nctx == 0) return;
 
   // 3. Passes of up to kPassRows A rows (row r = context p*, position k).
+  //    Per stage of kStageK hidden dims the block loads its 64 W rows with
+  //    fully coalesced 16-byte loads (each wave instruction covers two rows x
+  //    512 bytes) and the pass's A rows likewise, stores them to LDS, and every
+  //    wave reads the lane-major MFMA fragments of its 16 tokens from LDS.
+  //    Loads run kDepth stages ahead in registers, so several hundred KiB are
+  //    in flight per CU while the MFMAs of the current stage execute.
+  const int my_tok = wave * 16 + (lane & 15);  // MFMA column of this lane
+  const int kgrp = lane >> 4;                  // 0..3: which 8 of the 32 k's
+  constexpr int kCols = kStageK / 8, kRowsPerLoad = kBlock / kCols;
+  const int lrow = threadIdx.x / kCols, c8 = (threadIdx.x % kCols) * 8;
+  const uint16_t* wbase = a.W + (size_t)(tok0 + lrow) * a.d;
   const int ctx_per_pass = max(1, kPassRows / K);
-  const int my_tok = wave * 16 + (lane & 15);                 // MFMA column of this lane
-  const bool tok_ok = my_tok < ntok;
-  const uint16_t* wrow = a.W + (size_t)(tok0 + (tok_ok ? my_tok : 0)) * a.d;
-  const int kgrp = lane >> 4;                                 // 0..3: which 8 of the 32 k's
+  const int nstage = (a.d + kStageK - 1) / kStageK;
   for (int p0 = 0; p0 < nctx; p0 += ctx_per_pass) {
     const int np = min(ctx_per_pass, nctx - p0);
-    const int rows = np * K;  // <= kPassRows unless K > kPassRows
+    const int rows = np * K;
     for (int r0 = 0; r0 < rows; r0 += kPassRows) {
       const int nr = min(kPassRows, rows - r0);
-      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      for (int d0 = 0; d0 < a.d; d0 += kDChunk) {
-        const int dn = min(kDChunk, a.d - d0);
-        // Stage A rows [r0, r0+nr) x dims [d0, d0+dn) in LDS (zero padding).
-        __syncthreads();
-        for (int i = threadIdx.x; i < kPassRows * kDChunk / 8; i += kBlock) {
-          const int r = i / (kDChunk / 8), j8 = (i % (kDChunk / 8)) * 8;
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (r < nr && j8 < dn) {
-            const int rr = r0 + r;
-            const int ctx = sh_ctx[p0 + rr / K];
-            const int b = ctx >> 16, k = rr % K;
-            const uint16_t* src = a.h + ((size_t)b * K + k) * a.d + d0 + j8;
-            if (a.vec_ok && j8 + 8 <= dn) {
-              v = *reinterpret_cast<const u32x4*>(src);
-            } else {
-              uint32_t t4[4] = {0u, 0u, 0u, 0u};
-              for (int e = 0; e < 8; ++e)
-                if (j8 + e < dn) t4[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
-              v = u32x4{t4[0], t4[1], t4[2], t4[3]};
-            }
-          }
-          *reinterpret_cast<u32x4*>(&sh_a[r * kAStride + j8]) = v;
+      const uint16_t* arow[kALoads];
+#pragma unroll
+      for (int i = 0; i < kALoads; ++i) {
+        const int r = kRowsPerLoad * i + lrow;
+        arow[i] = nullptr;
+        if (r < nr) {
+          const int rr = r0 + r;
+          const int ctx = sh_ctx[p0 + rr / K];
+          arow[i] = a.h + ((size_t)(ctx >> 16) * K + rr % K) * a.d;
         }
-        __syncthreads();
-        // MFMA over this chunk, 32 k per instruction; this lane supplies
-        // W[my_tok][k..k+8).  Four k-steps of W are loaded before their MFMAs.
-        for (int kk0 = 0; kk0 < dn; kk0 += 4 * 32) {
-          u32x4 wv[4];
+      }
+      u32x4 wreg[kDepth][kWLoads], areg[kDepth][kALoads];
+      auto load_stage = [&](int st, u32x4 (&wr)[kWLoads], u32x4 (&ar)[kALoads]) {
+        const int k = st * kStageK + c8;
+        const bool live = st < nstage;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int kofs = kk0 + q * 32 + kgrp * 8;
-            wv[q] = u32x4{0u, 0u, 0u, 0u};
-            if (tok_ok && kofs < dn) {
-              if (a.vec_ok && kofs + 8 <= dn) {
-                wv[q] = *reinterpret_cast<const u32x4*>(wrow + d0 + kofs);
-              } else {
-                uint32_t t4[4] = {0u, 0u, 0u, 0u};
-                for (int e = 0; e < 8; ++e)
-                  if (kofs + e < dn) t4[e >> 1] |= (uint32_t)wrow[d0 + kofs + e] << (16 * (e & 1));
-                wv[q] = u32x4{t4[0], t4[1], t4[2], t4[3]};
-              }
-            }
-          }
+        for (int i = 0; i < kWLoads; ++i)
+          wr[i] = (live && kRowsPerLoad * i + lrow < ntok)
+                      ? load8(wbase + (size_t)(kRowsPerLoad * i) * a.d, k, a.d, a.vec_ok)
+                      : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int kofs = kk0 + q * 32 + kgrp * 8;
-            if (kk0 + q * 32 >= dn) break;
-            const bf16x8 bfrag = __builtin_bit_cast(bf16x8, wv[q]);
+        for (int i = 0; i < kALoads; ++i)
+          ar[i] = (live && arow[i]) ? load8(arow[i], k, a.d, a.vec_ok) : u32x4{0u, 0u, 0u, 0u};
+      };
+      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      const bool two = nr > 16;
 #pragma unroll
-            for (int mc = 0; mc < 2; ++mc) {
-              const u32x4 av = *reinterpret_cast<const u32x4*>(&sh_a[(mc * 16 + (lane & 15)) * kAStride + kofs]);
-              acc[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bfrag, acc[mc], 0, 0,
-                                                                0);
+      for (int j = 0; j < kDepth; ++j) load_stage(j, wreg[j], areg[j]);
+      for (int st0 = 0; st0 < nstage; st0 += kDepth) {
+#pragma unroll
+        for (int j = 0; j < kDepth; ++j) {
+          const int st = st0 + j;
+          if (st >= nstage) break;
+          __syncthreads();
+#pragma unroll
+          for (int i = 0; i < kWLoads; ++i)
+            *reinterpret_cast<u32x4*>(&sh_w[(kRowsPerLoad * i + lrow) * kLdsStride + c8]) = wreg[j][i];
+#pragma unroll
+          for (int i = 0; i < kALoads; ++i)
+            *reinterpret_cast<u32x4*>(&sh_a[(kRowsPerLoad * i + lrow) * kLdsStride + c8]) = areg[j][i];
+          __syncthreads();
+          load_stage(st + kDepth, wreg[j], areg[j]);
+#pragma unroll
+          for (int q = 0; q < kStageK / 32; ++q) {
+            const int kofs = q * 32 + kgrp * 8;
+            const u32x4 bv = *reinterpret_cast<const u32x4*>(&sh_w[my_tok * kLdsStride + kofs]);
+            const bf16x8 bfrag = __builtin_bit_cast(bf16x8, bv);
+            const u32x4 a0 = *reinterpret_cast<const u32x4*>(&sh_a[(lane & 15) * kLdsStride + kofs]);
+            acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), bfrag, acc[0], 0, 0, 0);
+            if (two) {
+              const u32x4 a1 = *reinterpret_cast<const u32x4*>(&sh_a[(16 + (lane & 15)) * kLdsStride + kofs]);
+              acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), bfrag, acc[1], 0, 0, 0);
             }
           }
         }
       }
       // Epilogue: lane holds D[m = 4*(lane/16) + i][n = lane%16] of each chunk.
-      if (tok_ok) {
+      if (my_tok < ntok) {
 #pragma unroll
         for (int mc = 0; mc < 2; ++mc) {
 #pragma unroll

@@ -143,8 +143,11 @@ def main():
     def span(i, j):
         return float(np.mean([evs[NE * s + i].elapsed_time(evs[NE * s + j]) for s in range(args.steps)]))
 
-    k_ms = {"stats_or_greedy": span(0, 1), "accept_or_finalize": span(1, 2), "sample": span(2, 3),
-            "pick": span(3, 4), "events_step": span(0, 4)}
+    if args.mode == "sample":
+        k_ms = {"stats": span(0, 1), "sample_with_accept": span(1, 2), "pick": span(2, 3),
+                "events_step": span(0, 4)}
+    else:
+        k_ms = {"greedy": span(0, 1), "greedy_finalize": span(1, 2), "events_step": span(0, 4)}
     acc = res[0].float()
     mean_tokens = float((acc[acc >= 0] + 1).mean()) if (acc >= 0).any() else float("nan")
 
@@ -153,11 +156,11 @@ def main():
     if args.mode == "sample":
         step_bytes = B * (2 * K + 1) * V * esz          # every logit read once
         dom_bytes = B * 2 * K * V * esz                 # rows 0..K-1 of target and draft
-        dom_name, dom_ms = "stats_kernel (row statistics)", k_ms["stats_or_greedy"]
+        dom_name, dom_ms = "stats_kernel (row statistics)", k_ms["stats"]
     else:
         step_bytes = B * (K + 1) * V * esz
         dom_bytes = step_bytes
-        dom_name, dom_ms = "greedy_kernel (per-tile argmax)", k_ms["stats_or_greedy"]
+        dom_name, dom_ms = "greedy_kernel (per-tile argmax)", k_ms["greedy"]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = traffic_from_profile() if (args.workload == "b256_k7_v262144_bf16" and args.mode == "sample") else None
 
@@ -257,7 +260,7 @@ def bench_shortlist(args, dev):
         return float(np.mean([evs[(NE + 2) * s + i].elapsed_time(evs[(NE + 2) * s + j]) for s in range(args.steps)]))
 
     head_ms = span(0, 1)
-    k_ms = {"head": head_ms, "stats": span(2, 3), "accept": span(3, 4), "sample": span(4, 5), "pick": span(5, 6),
+    k_ms = {"head": head_ms, "stats": span(2, 3), "sample_with_accept": span(3, 4), "pick": span(4, 5),
             "events_step": span(0, 6)}
     sel = torch.unique(hc.cluster_ids).numel()
     w_bytes = sel * cs * d * 2

@@ -112,9 +112,10 @@ spec_status_t spec_verify(const void* target_logits, const void* draft_logits,
  * spec_verify with kernel timing.  Identical work and launches; in addition
  * events[0..SPEC_TIMED_EVENTS-1] (hipEvent_t passed as void*, any may be NULL)
  * are recorded on `stream`.  SAMPLE mode: [0] before the row-statistics
- * kernel, [1] after it, [2] after the accept-decision kernel, [3] after the
- * sampling kernel, [4] after the token-pick kernel.  GREEDY mode: [0] before
- * the argmax kernel, [1] after it, [2], [3] and [4] after its finalize kernel.
+ * kernel, [1] after it, [2] after the sampling kernel (accept decisions and
+ * the sampled rows' tile sums), [3] and [4] after the token-pick kernel.
+ * GREEDY mode: [0] before the argmax kernel, [1] after it, [2], [3] and [4]
+ * after its finalize kernel.
  */
 spec_status_t spec_verify_timed(const void* target_logits, const void* draft_logits,
                                 const int32_t* draft_tokens, const float* uniforms,

@@ -82,11 +82,10 @@ spec_status_t verify_impl(const void* target_logits, const void* draft_logits, c
   if (sample) {
     e = sv::launch_stats(s, io, ws, st);
     record(1);
-    if (e == hipSuccess) e = sv::launch_accept(s, io, ws, st);
-    record(2);
     if (e == hipSuccess) e = sv::launch_sample(s, io, ws, st);
-    record(3);
+    record(2);
     if (e == hipSuccess) e = sv::launch_pick(s, io, ws, st);
+    record(3);
     record(4);
   } else {
     e = sv::launch_greedy(s, io, ws, st);

@@ -183,17 +183,17 @@ __device__ __forceinline__ float exp2_fast(float a) { return __builtin_amdgcn_ex
 // with d*s_lo, applied as the first-order factor (1 + lo*ln2).  What remains
 // is v_exp_f32's own error (< 0.8 ulp on gfx950) plus one rounding.  x - m is
 // exact for bf16 operands whose exponents are within 16 of each other.
-// Returns 0 for x = -inf and for results below 2^-200.
-__device__ __forceinline__ float exp2_accurate(float x, float m, float s_hi, float s_lo) {
+// d is clamped at dmin = -200/s_hi: anything below gives 2^-200, which
+// v_exp_f32 returns as 0, and x = -inf stays finite through the FMAs.
+__device__ __forceinline__ float exp2_accurate(float x, float m, float s_hi, float s_lo, float dmin) {
 #pragma clang fp contract(off)
   constexpr float kLn2 = 0.693147180559945309f;
-  const float d = x - m;
+  const float d = fmaxf(x - m, dmin);
   const float hi = d * s_hi;
   float lo = __builtin_fmaf(d, s_hi, -hi);
   lo = __builtin_fmaf(d, s_lo, lo);
   const float e = __builtin_amdgcn_exp2f(hi);
-  const float r = __builtin_fmaf(e, lo * kLn2, e);
-  return hi < -200.0f ? 0.0f : r;
+  return __builtin_fmaf(e, lo * kLn2, e);
 }
 
 }  // namespace sv

@@ -20,6 +20,15 @@ struct SampleTile {
   double g, h;     // the same sums restricted to the residual's positive set
 };
 
+// What the token pick needs about a sequence's sampled position n (written by
+// the sampling pass): statistics-pass maxima and normalisers of target and
+// draft row n (residual), and n itself (-1 for a faulty sequence).
+struct SampleRowInfo {
+  float m_t, m_d;
+  double za_t, za_d;
+  int n;
+};
+
 struct ArgTile {
   float v;
   int i;
@@ -38,9 +47,7 @@ struct VerifyShape {
 
 struct VerifyWorkspace {
   TileStat* part_a;     // [B][2K][NT]
-  float* row_m;         // [B][2K]
-  double* row_z;        // [B][2K]
-  int32_t* job;         // [B] position to sample, or -1 for a faulty sequence
+  SampleRowInfo* rows;  // [B]
   SampleTile* part_b;   // [B][NT_s]
   ArgTile* part_g;      // [B][K+1][NT]
 };
@@ -61,9 +68,8 @@ int tile_elems(int dtype);
 VerifyShape make_shape(int B, int K, int V, int dtype, bool aligned);
 size_t verify_workspace_layout(const VerifyShape& s, bool greedy, void* base, VerifyWorkspace* out);
 
-// SAMPLE: stats -> accept -> sample -> pick.  GREEDY: greedy -> greedy_finalize.
+// SAMPLE: stats -> sample (with accept decisions) -> pick.  GREEDY: greedy -> greedy_finalize.
 hipError_t launch_stats(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);
-hipError_t launch_accept(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);
 hipError_t launch_sample(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);
 hipError_t launch_pick(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);
 hipError_t launch_greedy(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);

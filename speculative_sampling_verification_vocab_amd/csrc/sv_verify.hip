@@ -1,22 +1,22 @@
 // Speculative-sampling verify kernels for gfx950.
 //
-// SAMPLE mode runs four kernels on the caller's stream.
+// SAMPLE mode runs three kernels on the caller's stream.
 //
 //  1. stats_kernel streams target rows 0..K-1 and draft rows 0..K-1 once.
 //     One wave owns one tile (8 KiB) of one row: 16-byte loads, a per-lane
 //     maximum, 2^((x - max) * log2(e)/T) with v_exp_f32, and a wave reduction
 //     to a (tile max, tile sum) partial.
-//  2. accept_kernel (one block per sequence) combines the partials into
+//  2. sample_kernel: every block first combines its sequence's partials into
 //     (max, Z) per row, evaluates P_t,i(d_i) and P_d,i(d_i) in double, takes
 //     every accept decision u < min(1, P_t/P_d) and finds the first rejection
 //     n (Speculative Decoding lesson, nextadmin.net, "Core algorithm" steps
-//     4-5, "Step 1").
-//  3. sample_kernel re-reads only what the output token at n needs: target
-//     and draft row n at a rejection (residual (P_t - P_d)_+, "Step 2"), or
-//     target row K when every draft was accepted (bonus token, step 6).  It
-//     recomputes every element with a compensated exponential and sums per
-//     tile in double.
-//  4. pick_kernel (one block per sequence) turns the tile masses into an
+//     4-5, "Step 1"); the sequence's first block writes those outputs.  The
+//     block then re-reads only what the output token at n needs: one tile of
+//     target and draft row n at a rejection (residual (P_t - P_d)_+, "Step 2"),
+//     or of target row K when every draft was accepted (bonus token, step 6),
+//     recomputing every element with a compensated exponential and summing in
+//     double.
+//  3. pick_kernel (one block per sequence) turns the tile masses into an
 //     inverse-CDF choice of tile, then scans that one tile in token-id order.
 //
 // Kernel boundaries order the passes: partial results cross XCDs through
@@ -41,19 +41,24 @@ namespace sv {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
+constexpr int kTilesPerWaveS = 4;  // sampling tiles per wave: amortises the per-block accept prologue
+constexpr int kTilesPerBlockS = kTilesPerWaveS * kWavesPerBlock;
 
-struct StatsArgs {
+struct VerifyArgs {
   const void* target;
   const void* draft;
   const int32_t* tokens;
   const float* uniforms;
-  int B, K, V, NT, NG;
-  float s_hi;  // log2(e)/T rounded to float
+  int B, K, V;
+  int NT, NG;            // statistics pass: tiles (kTile ids) and blocks per row
+  int NTs, NGs;          // sampling pass: tiles (kTileS ids) and blocks per row
+  float s_hi, s_lo;      // log2(e)/T as a float pair
+  float dmin;            // clamp for x - m in the accurate exponential: -200 / s_hi
+  double s64;            // log2(e)/T in double
   double T;
-  TileStat* part;
-  float* row_m;
-  double* row_z;
-  int32_t* job;
+  TileStat* part_a;      // [B][2K][NT]
+  SampleRowInfo* rows;   // [B] what pick_kernel needs about the sampled row pair
+  SampleTile* part_b;    // [B][NTs]
   int32_t* accepted_len;
   int32_t* out_tokens;
   float* p_t_out;
@@ -66,93 +71,11 @@ __device__ __forceinline__ const T* row_ptr(const void* base, size_t rows_before
 }
 
 // ---------------------------------------------------------------------------
-// Row statistics and accept decisions.
+// Row statistics.
 // ---------------------------------------------------------------------------
 
-template <typename T>
-__device__ void finalize_stats(const StatsArgs& a, int b) {
-  __shared__ float sh_m[2 * kMaxK];
-  __shared__ double sh_z[2 * kMaxK];
-  __shared__ int sh_acc[kMaxK];
-  __shared__ int sh_bad;
-  __shared__ int sh_n;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int K = a.K, R = 2 * K;
-  if (threadIdx.x == 0) sh_bad = 0;
-
-  for (int r = wave; r < R; r += kWavesPerBlock) {
-    const TileStat* p = a.part + ((size_t)b * R + r) * a.NT;
-    float m = kNegInf;
-    for (int t = lane; t < a.NT; t += kWave) m = fmaxf(m, p[t].m);
-    m = wave_max(m);
-    double z = 0.0;
-    if (m != kNegInf) {
-      for (int t = lane; t < a.NT; t += kWave) {
-        const TileStat q = p[t];
-        if (q.m != kNegInf) z += (double)q.s * (double)exp2_fast((q.m - m) * a.s_hi);
-      }
-    }
-    z = wave_sum(z);
-    if (lane == 0) {
-      sh_m[r] = m;
-      sh_z[r] = z;
-      a.row_m[(size_t)b * R + r] = m;
-      a.row_z[(size_t)b * R + r] = z;
-    }
-  }
-  __syncthreads();
-
-  double pt = __builtin_nan(""), pd = __builtin_nan("");
-  if ((int)threadIdx.x < K) {
-    const int i = threadIdx.x;
-    const int d = a.tokens[(size_t)b * K + i];
-    const float mt = sh_m[i], md = sh_m[K + i];
-    const double zt = sh_z[i], zd = sh_z[K + i];
-    const bool bad = d < 0 || d >= a.V || !isfinite(mt) || !isfinite(md) || !(zt > 0.0) || !isfinite(zt) ||
-                     !(zd > 0.0) || !isfinite(zd);
-    int acc = 0;
-    if (!bad) {
-      const T* trow = row_ptr<T>(a.target, (size_t)b * (K + 1) + i, a.V);
-      const T* drow = row_ptr<T>(a.draft, (size_t)b * K + i, a.V);
-      const double xt = (double)to_f32(trow[d]);
-      const double xd = (double)to_f32(drow[d]);
-      pt = exp((xt - (double)mt) / a.T) / zt;
-      pd = exp((xd - (double)md) / a.T) / zd;
-      const double ratio = pd > 0.0 ? pt / pd : __builtin_inf();
-      const double thr = ratio < 1.0 ? ratio : 1.0;
-      acc = (double)a.uniforms[((size_t)b * (K + 1) + i) * 2] < thr;
-    } else {
-      atomicOr(&sh_bad, 1);
-    }
-    sh_acc[i] = acc;
-  }
-  __syncthreads();
-  const bool bad = sh_bad != 0;
-  if ((int)threadIdx.x < K) {
-    const int i = threadIdx.x;
-    if (a.p_t_out) a.p_t_out[(size_t)b * K + i] = bad ? __builtin_nanf("") : (float)pt;
-    if (a.p_d_out) a.p_d_out[(size_t)b * K + i] = bad ? __builtin_nanf("") : (float)pd;
-  }
-  if (threadIdx.x == 0) {
-    int n = K;
-    for (int i = 0; i < K; ++i)
-      if (!sh_acc[i]) {
-        n = i;
-        break;
-      }
-    if (bad) n = -1;
-    sh_n = n;
-    a.job[b] = n;
-    a.accepted_len[b] = n;
-  }
-  __syncthreads();
-  const int n = sh_n;
-  for (int i = threadIdx.x; i <= K; i += kBlock)
-    a.out_tokens[(size_t)b * (K + 1) + i] = (n >= 0 && i < n) ? a.tokens[(size_t)b * K + i] : -1;
-}
-
 template <typename T, bool kAligned>
-__global__ void __launch_bounds__(kBlock) stats_kernel(StatsArgs a) {
+__global__ void __launch_bounds__(kBlock) stats_kernel(VerifyArgs a) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int K = a.K, R = 2 * K;
   const int g = blockIdx.x % a.NG;
@@ -174,68 +97,118 @@ __global__ void __launch_bounds__(kBlock) stats_kernel(StatsArgs a) {
     const float M = wave_max(ml);
     const float scaled = ml == kNegInf ? 0.0f : sl * exp2_fast((ml - M) * a.s_hi);
     const float S = wave_sum(scaled);
-    if (lane == 0) a.part[((size_t)b * R + r) * a.NT + t] = TileStat{M, S};
+    if (lane == 0) a.part_a[((size_t)b * R + r) * a.NT + t] = TileStat{M, S};
   }
 }
 
-// One block per sequence, after stats_kernel: combine the tile partials and
-// take the accept decisions.
+// ---------------------------------------------------------------------------
+// Accept decisions of one sequence (run by every block of the sampling pass).
+// Combines the statistics partials into (max, Z) per row, evaluates P_t(d_i)
+// and P_d(d_i) in double and finds the first rejection n.  With `write` the
+// block also writes accepted_len, the accepted tokens, the probability
+// outputs and the row data pick_kernel needs.  Returns n, or -1 for a faulty
+// sequence.
+// ---------------------------------------------------------------------------
+
 template <typename T>
-__global__ void __launch_bounds__(kBlock) accept_kernel(StatsArgs a) {
-  finalize_stats<T>(a, blockIdx.x);
-}
-
-// ---------------------------------------------------------------------------
-// Sampling: residual at the first rejection, or the bonus token.
-// ---------------------------------------------------------------------------
-
-struct SampleArgs {
-  const void* target;
-  const void* draft;
-  const float* uniforms;
-  int B, K, V, NT, NG;  // NT, NG count sampling-pass tiles (kTileS ids) and blocks
-  float s_hi, s_lo;     // log2(e)/T as a float pair
-  double s64;           // log2(e)/T in double
-  const float* row_m;
-  const double* row_z;
-  const int32_t* job;
-  SampleTile* part;
-  int32_t* accepted_len;
-  int32_t* out_tokens;
-};
-
-// What the sampling of one sequence needs, shared by the tile pass and the pick.
-struct SampleRow {
-  int n;
-  bool resid;
-  float m_t, m_d;     // statistics-pass row maxima (residual)
-  double za_t, za_d;  // statistics-pass normalisers: decide the positive set only
-};
-
-// Position to sample and the statistics-pass row data it needs; false for a
-// faulty sequence (the statistics pass already wrote its outputs).
-__device__ __forceinline__ bool load_sample_row(const SampleArgs& a, int b, SampleRow& sr) {
-  const int K = a.K;
-  sr.n = K == 0 ? 0 : a.job[b];
-  if (sr.n < 0) return false;
-  sr.resid = sr.n < K;
-  sr.m_t = sr.m_d = 0.0f;
-  sr.za_t = sr.za_d = 1.0;
-  if (sr.resid) {
-    const size_t R = 2 * (size_t)K;
-    sr.m_t = a.row_m[b * R + sr.n];
-    sr.m_d = a.row_m[b * R + K + sr.n];
-    sr.za_t = a.row_z[b * R + sr.n];
-    sr.za_d = a.row_z[b * R + K + sr.n];
+__device__ int accept_sequence(const VerifyArgs& a, int b, bool write, SampleRowInfo* info) {
+  __shared__ float sh_m[2 * kMaxK];
+  __shared__ double sh_z[2 * kMaxK];
+  __shared__ int sh_acc[kMaxK];
+  __shared__ int sh_bad;
+  __shared__ int sh_n;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int K = a.K, R = 2 * K;
+  if (K == 0) {
+    *info = SampleRowInfo{0.0f, 0.0f, 1.0, 1.0};
+    return 0;
   }
-  return true;
+  if (threadIdx.x == 0) sh_bad = 0;
+  // The drafted logits do not depend on the statistics: fetch them first.
+  double xt = 0.0, xd = 0.0;
+  int d = -1;
+  if ((int)threadIdx.x < K) {
+    const int i = threadIdx.x;
+    d = a.tokens[(size_t)b * K + i];
+    if (d >= 0 && d < a.V) {
+      xt = (double)to_f32(row_ptr<T>(a.target, (size_t)b * (K + 1) + i, a.V)[d]);
+      xd = (double)to_f32(row_ptr<T>(a.draft, (size_t)b * K + i, a.V)[d]);
+    }
+  }
+  for (int r = wave; r < R; r += kWavesPerBlock) {
+    const TileStat* p = a.part_a + ((size_t)b * R + r) * a.NT;
+    float m = kNegInf;
+    for (int t = lane; t < a.NT; t += kWave) m = fmaxf(m, p[t].m);
+    m = wave_max(m);
+    double z = 0.0;
+    if (m != kNegInf) {
+      for (int t = lane; t < a.NT; t += kWave) {
+        const TileStat q = p[t];
+        if (q.m != kNegInf) z += (double)q.s * (double)exp2_fast((q.m - m) * a.s_hi);
+      }
+    }
+    z = wave_sum(z);
+    if (lane == 0) {
+      sh_m[r] = m;
+      sh_z[r] = z;
+    }
+  }
+  __syncthreads();
+
+  double pt = __builtin_nan(""), pd = __builtin_nan("");
+  if ((int)threadIdx.x < K) {
+    const int i = threadIdx.x;
+    const float mt = sh_m[i], md = sh_m[K + i];
+    const double zt = sh_z[i], zd = sh_z[K + i];
+    const bool bad = d < 0 || d >= a.V || !isfinite(mt) || !isfinite(md) || !(zt > 0.0) || !isfinite(zt) ||
+                     !(zd > 0.0) || !isfinite(zd);
+    int acc = 0;
+    if (!bad) {
+      pt = exp((xt - (double)mt) / a.T) / zt;
+      pd = exp((xd - (double)md) / a.T) / zd;
+      const double ratio = pd > 0.0 ? pt / pd : __builtin_inf();
+      const double thr = ratio < 1.0 ? ratio : 1.0;
+      acc = (double)a.uniforms[((size_t)b * (K + 1) + i) * 2] < thr;
+    } else {
+      atomicOr(&sh_bad, 1);
+    }
+    sh_acc[i] = acc;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int n = K;
+    for (int i = 0; i < K; ++i)
+      if (!sh_acc[i]) {
+        n = i;
+        break;
+      }
+    sh_n = sh_bad ? -1 : n;
+  }
+  __syncthreads();
+  const int n = sh_n;
+  if (n >= 0 && n < K) *info = SampleRowInfo{sh_m[n], sh_m[K + n], sh_z[n], sh_z[K + n]};
+  else *info = SampleRowInfo{0.0f, 0.0f, 1.0, 1.0};
+  if (write) {
+    if ((int)threadIdx.x < K) {
+      const int i = threadIdx.x;
+      if (a.p_t_out) a.p_t_out[(size_t)b * K + i] = n < 0 ? __builtin_nanf("") : (float)pt;
+      if (a.p_d_out) a.p_d_out[(size_t)b * K + i] = n < 0 ? __builtin_nanf("") : (float)pd;
+    }
+    for (int i = threadIdx.x; i <= K; i += kBlock)
+      a.out_tokens[(size_t)b * (K + 1) + i] = (n >= 0 && i < n) ? a.tokens[(size_t)b * K + i] : -1;
+    if (threadIdx.x == 0) {
+      a.accepted_len[b] = n;
+      a.rows[b] = SampleRowInfo{info->m_t, info->m_d, info->za_t, info->za_d, n};
+    }
+  }
+  return n;
 }
 
 // Per-tile ratio that decides the residual's positive set: element v of a tile
 // with maxima (mt, md) is in the set iff e_t * rho > e_d, i.e. P_t(v) > P_d(v)
 // with the statistics-pass normalisers.  Both sampling kernels evaluate this
 // same function, so they agree on the set.
-__device__ __forceinline__ float tile_rho(float mt, float md, const SampleRow& sr, double s64) {
+__device__ __forceinline__ float tile_rho(float mt, float md, const SampleRowInfo& sr, double s64) {
 #pragma clang fp contract(off)
   if (mt == kNegInf) return 0.0f;
   if (md == kNegInf) return 1e30f;
@@ -247,85 +220,96 @@ __device__ __forceinline__ float tile_rho(float mt, float md, const SampleRow& s
 
 // Accurate 2^((x - tile max) * s) for a whole tile slice; 0 when the tile is all -inf.
 template <int N>
-__device__ __forceinline__ void tile_exp(const float (&x)[N], float m, float s_hi, float s_lo, float (&e)[N]) {
+__device__ __forceinline__ void tile_exp(const float (&x)[N], float m, const VerifyArgs& a, float (&e)[N]) {
   if (m == kNegInf) {
 #pragma unroll
     for (int i = 0; i < N; ++i) e[i] = 0.0f;
   } else {
 #pragma unroll
-    for (int i = 0; i < N; ++i) e[i] = exp2_accurate(x[i], m, s_hi, s_lo);
+    for (int i = 0; i < N; ++i) e[i] = exp2_accurate(x[i], m, a.s_hi, a.s_lo, a.dmin);
   }
 }
 
+// ---------------------------------------------------------------------------
+// Sampling pass: accept decisions, then the tile sums of the sampled row(s).
+// ---------------------------------------------------------------------------
+
 template <typename T, bool kAligned>
-__global__ void __launch_bounds__(kBlock) sample_kernel(SampleArgs a) {
+__global__ void __launch_bounds__(kBlock) sample_kernel(VerifyArgs a) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int K = a.K;
-  const int g = blockIdx.x % a.NG;
-  const int b = blockIdx.x / a.NG;
-  SampleRow sr;
-  if (!load_sample_row(a, b, sr)) return;
-  const T* trow = row_ptr<T>(a.target, (size_t)b * (K + 1) + sr.n, a.V);
-  const int t = g * kWavesPerBlock + wave;
-  if (t >= a.NT) return;
+  const int g = blockIdx.x % a.NGs;
+  const int b = blockIdx.x / a.NGs;
+  SampleRowInfo sr;
+  const int n = accept_sequence<T>(a, b, g == 0, &sr);
+  if (n < 0) return;  // faulty sequence: outputs already written
+  const bool resid = n < K;
+  const T* trow = row_ptr<T>(a.target, (size_t)b * (K + 1) + n, a.V);
+  const T* drow = resid ? row_ptr<T>(a.draft, (size_t)b * K + n, a.V) : nullptr;
   constexpr int P = kPerLaneS<T>;
-  float x[P], e[P];
-  load_tile<T, kAligned, kLoadsS>(trow, a.V, t, lane, x);
-  const float mt = wave_max(lane_max(x));
-  double zt = 0.0, zd = 0.0, gs = 0.0, hs = 0.0;
-  float md = kNegInf;
-  if (!sr.resid) {
-    tile_exp(x, mt, a.s_hi, a.s_lo, e);
+  // The block covers kTilesPerBlockS consecutive tiles, interleaved over its
+  // waves so that the four waves read neighbouring tiles at the same time.
+  for (int j = 0; j < kTilesPerWaveS; ++j) {
+    const int t = g * kTilesPerBlockS + j * kWavesPerBlock + wave;
+    if (t >= a.NTs) break;
+    float x[P], e[P];
+    load_tile<T, kAligned, kLoadsS>(trow, a.V, t, lane, x);
+    const float mt = wave_max(lane_max(x));
+    double zt = 0.0, zd = 0.0, gs = 0.0, hs = 0.0;
+    float md = kNegInf;
+    if (!resid) {
+      tile_exp(x, mt, a, e);
 #pragma unroll
-    for (int i = 0; i < P; ++i) zt += (double)e[i];
-  } else {
-    const T* drow = row_ptr<T>(a.draft, (size_t)b * K + sr.n, a.V);
-    float y[P], f[P];
-    load_tile<T, kAligned, kLoadsS>(drow, a.V, t, lane, y);
-    md = wave_max(lane_max(y));
-    tile_exp(x, mt, a.s_hi, a.s_lo, e);
-    tile_exp(y, md, a.s_hi, a.s_lo, f);
-    const float rho = tile_rho(mt, md, sr, a.s64);
+      for (int i = 0; i < P; ++i) zt += (double)e[i];
+    } else {
+      float y[P], f[P];
+      load_tile<T, kAligned, kLoadsS>(drow, a.V, t, lane, y);
+      md = wave_max(lane_max(y));
+      tile_exp(x, mt, a, e);
+      tile_exp(y, md, a, f);
+      const float rho = tile_rho(mt, md, sr, a.s64);
 #pragma unroll
-    for (int i = 0; i < P; ++i) {
-      const double et = (double)e[i], ed = (double)f[i];
-      const bool pos = e[i] * rho > f[i];
-      zt += et;
-      zd += ed;
-      gs += pos ? et : 0.0;
-      hs += pos ? ed : 0.0;
+      for (int i = 0; i < P; ++i) {
+        const double et = (double)e[i], ed = (double)f[i];
+        const double in = e[i] * rho > f[i] ? 1.0 : 0.0;
+        zt += et;
+        zd += ed;
+        gs = __builtin_fma(et, in, gs);
+        hs = __builtin_fma(ed, in, hs);
+      }
     }
+    zt = wave_sum(zt);
+    zd = wave_sum(zd);
+    gs = wave_sum(gs);
+    hs = wave_sum(hs);
+    if (lane == 0) a.part_b[(size_t)b * a.NTs + t] = SampleTile{(double)mt, (double)md, zt, zd, gs, hs};
   }
-  zt = wave_sum(zt);
-  zd = wave_sum(zd);
-  gs = wave_sum(gs);
-  hs = wave_sum(hs);
-  if (lane == 0) a.part[(size_t)b * a.NT + t] = SampleTile{(double)mt, (double)md, zt, zd, gs, hs};
 }
 
 // One block per sequence, after sample_kernel: the inverse-CDF choice of tile
 // from the tile masses, then a four-wave scan of that tile in token-id order.
 template <typename T, bool kAligned>
-__global__ void __launch_bounds__(kBlock) pick_kernel(SampleArgs a) {
+__global__ void __launch_bounds__(kBlock) pick_kernel(VerifyArgs a) {
   __shared__ double sh_d[kWavesPerBlock];
   __shared__ float sh_f[kWavesPerBlock];
   __shared__ int sh_i[kWavesPerBlock];
   __shared__ double sh_scan[kWavesPerBlock];
   __shared__ double sh_cbefore;
   const int b = blockIdx.x;
-  SampleRow sr;
-  if (!load_sample_row(a, b, sr)) return;
+  const SampleRowInfo sr = a.rows[b];
+  const int K = a.K, NT = a.NTs, n = K == 0 ? 0 : sr.n;
+  if (n < 0) return;
+  const bool resid = n < K;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int K = a.K, NT = a.NT, n = sr.n;
   const T* trow = row_ptr<T>(a.target, (size_t)b * (K + 1) + n, a.V);
-  const T* drow = sr.resid ? row_ptr<T>(a.draft, (size_t)b * K + n, a.V) : nullptr;
-  const SampleTile* P = a.part + (size_t)b * NT;
+  const T* drow = resid ? row_ptr<T>(a.draft, (size_t)b * K + n, a.V) : nullptr;
+  const SampleTile* P = a.part_b + (size_t)b * NT;
   constexpr double kNegInfD = -__builtin_inf();
 
   // Reference maxima: statistics-pass maxima for a residual pair, the maximum
   // over tiles for the bonus row (the statistics pass does not read row K).
   float mref_t = sr.m_t;
-  if (!sr.resid) {
+  if (!resid) {
     float mm = kNegInf;
     for (int tt = threadIdx.x; tt < NT; tt += kBlock) mm = fmaxf(mm, (float)P[tt].mt);
     mref_t = block_max(mm, sh_f);
@@ -336,12 +320,12 @@ __global__ void __launch_bounds__(kBlock) pick_kernel(SampleArgs a) {
     for (int tt = threadIdx.x; tt < NT; tt += kBlock) {
       const SampleTile q = P[tt];
       if (q.mt != kNegInfD) zbt += q.zt * exp2((q.mt - (double)mref_t) * a.s64);
-      if (sr.resid && q.md != kNegInfD) zbd += q.zd * exp2((q.md - (double)sr.m_d) * a.s64);
+      if (resid && q.md != kNegInfD) zbd += q.zd * exp2((q.md - (double)sr.m_d) * a.s64);
     }
   }
   zbt = block_sum(zbt, sh_d);
-  if (sr.resid) zbd = block_sum(zbd, sh_d);
-  if (!isfinite(mref_t) || !(zbt > 0.0) || !isfinite(zbt) || (sr.resid && (!(zbd > 0.0) || !isfinite(zbd)))) {
+  if (resid) zbd = block_sum(zbd, sh_d);
+  if (!isfinite(mref_t) || !(zbt > 0.0) || !isfinite(zbt) || (resid && (!(zbd > 0.0) || !isfinite(zbd)))) {
     // A sampled row without a finite maximum: the sequence is faulty.
     for (int i = threadIdx.x; i <= K; i += kBlock) a.out_tokens[(size_t)b * (K + 1) + i] = -1;
     if (threadIdx.x == 0) a.accepted_len[b] = -1;
@@ -353,7 +337,7 @@ __global__ void __launch_bounds__(kBlock) pick_kernel(SampleArgs a) {
   auto scale_d = [&](double md) { return md == kNegInfD ? 0.0 : exp2((md - (double)sr.m_d) * a.s64) / zbd; };
   auto tile_mass = [&](int tt, bool fallback) -> double {
     const SampleTile q = P[tt];
-    if (!sr.resid || fallback) return q.zt * scale_t(q.mt);
+    if (!resid || fallback) return q.zt * scale_t(q.mt);
     return q.g * scale_t(q.mt) - q.h * scale_d(q.md);
   };
 
@@ -361,7 +345,7 @@ __global__ void __launch_bounds__(kBlock) pick_kernel(SampleArgs a) {
   for (int tt = threadIdx.x; tt < NT; tt += kBlock) S += tile_mass(tt, false);
   S = block_sum(S, sh_d);
   bool fallback = false;
-  if (sr.resid && !(S > 0.0)) {
+  if (resid && !(S > 0.0)) {
     // Rejection with no residual mass left by rounding: sample P_t instead.
     fallback = true;
     S = 0.0;
@@ -419,7 +403,7 @@ __global__ void __launch_bounds__(kBlock) pick_kernel(SampleArgs a) {
   // the tile pass computed them.
   constexpr int V8 = Elem<T>::kVec;
   static_assert(kLoadsS == kWavesPerBlock, "one load of the tile per wave");
-  const bool use_d = sr.resid && !fallback;
+  const bool use_d = resid && !fallback;
   float x[V8], y[V8], e[V8], f[V8];
   load_tile<T, kAligned, kLoadsS>(trow, a.V, jstar, lane, x, wave);
   const float mt = block_max(lane_max(x), sh_f);
@@ -430,10 +414,10 @@ __global__ void __launch_bounds__(kBlock) pick_kernel(SampleArgs a) {
   }
   const double gt = scale_t((double)mt);
   const double gd = use_d ? scale_d((double)md) : 0.0;
-  tile_exp(x, mt, a.s_hi, a.s_lo, e);
+  tile_exp(x, mt, a, e);
   double w[V8];
   if (use_d) {
-    tile_exp(y, md, a.s_hi, a.s_lo, f);
+    tile_exp(y, md, a, f);
     const float rho = tile_rho(mt, md, sr, a.s64);
 #pragma unroll
     for (int k = 0; k < V8; ++k) w[k] = e[k] * rho > f[k] ? (double)e[k] * gt - (double)f[k] * gd : 0.0;
@@ -599,28 +583,26 @@ VerifyShape make_shape(int B, int K, int V, int dtype, bool aligned) {
   s.NG = (s.NT + kWavesPerBlock - 1) / kWavesPerBlock;
   const int tile_s = dtype == 1 ? kTileS<uint16_t> : kTileS<float>;
   s.NT_s = (V + tile_s - 1) / tile_s;
-  s.NG_s = (s.NT_s + kWavesPerBlock - 1) / kWavesPerBlock;
+  s.NG_s = (s.NT_s + kTilesPerBlockS - 1) / kTilesPerBlockS;
   return s;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t verify_workspace_layout(const VerifyShape& s, bool greedy, void* base, VerifyWorkspace* out) {
-  const size_t B = (size_t)s.B, K = (size_t)s.K, NT = (size_t)s.NT;
+  const size_t B = (size_t)s.B, K = (size_t)s.K;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
     off = align256(off + bytes);
     return at;
   };
-  size_t o_pa = 0, o_rm = 0, o_rz = 0, o_job = 0, o_pb = 0, o_pg = 0;
+  size_t o_pa = 0, o_rows = 0, o_pb = 0, o_pg = 0;
   if (greedy) {
-    o_pg = take(B * (K + 1) * NT * sizeof(ArgTile));
+    o_pg = take(B * (K + 1) * (size_t)s.NT * sizeof(ArgTile));
   } else {
-    o_pa = take(B * 2 * K * NT * sizeof(TileStat));
-    o_rm = take(B * 2 * K * sizeof(float));
-    o_rz = take(B * 2 * K * sizeof(double));
-    o_job = take(B * sizeof(int32_t));
+    o_pa = take(B * 2 * K * (size_t)s.NT * sizeof(TileStat));
+    o_rows = take(B * sizeof(SampleRowInfo));
     o_pb = take(B * (size_t)s.NT_s * sizeof(SampleTile));
   }
   if (out && base) {
@@ -630,9 +612,7 @@ size_t verify_workspace_layout(const VerifyShape& s, bool greedy, void* base, Ve
       w.part_g = reinterpret_cast<ArgTile*>(p + o_pg);
     } else {
       w.part_a = reinterpret_cast<TileStat*>(p + o_pa);
-      w.row_m = reinterpret_cast<float*>(p + o_rm);
-      w.row_z = reinterpret_cast<double*>(p + o_rz);
-      w.job = reinterpret_cast<int32_t*>(p + o_job);
+      w.rows = reinterpret_cast<SampleRowInfo*>(p + o_rows);
       w.part_b = reinterpret_cast<SampleTile*>(p + o_pb);
     }
     *out = w;
@@ -640,8 +620,8 @@ size_t verify_workspace_layout(const VerifyShape& s, bool greedy, void* base, Ve
   return off;
 }
 
-static StatsArgs stats_args(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws) {
-  StatsArgs a{};
+static VerifyArgs verify_args(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws) {
+  VerifyArgs a{};
   a.target = io.target;
   a.draft = io.draft;
   a.tokens = io.tokens;
@@ -651,12 +631,16 @@ static StatsArgs stats_args(const VerifyShape& s, const VerifyIO& io, const Veri
   a.V = s.V;
   a.NT = s.NT;
   a.NG = s.NG;
-  a.s_hi = (float)log2e_over(io.temperature);
+  a.NTs = s.NT_s;
+  a.NGs = s.NG_s;
+  a.s64 = log2e_over(io.temperature);
+  a.s_hi = (float)a.s64;
+  a.s_lo = (float)(a.s64 - (double)a.s_hi);
+  a.dmin = (float)(-200.0 / (double)a.s_hi);
   a.T = (double)io.temperature;
-  a.part = ws.part_a;
-  a.row_m = ws.row_m;
-  a.row_z = ws.row_z;
-  a.job = ws.job;
+  a.part_a = ws.part_a;
+  a.rows = ws.rows;
+  a.part_b = ws.part_b;
   a.accepted_len = io.accepted_len;
   a.out_tokens = io.out_tokens;
   a.p_t_out = io.p_target;
@@ -664,47 +648,17 @@ static StatsArgs stats_args(const VerifyShape& s, const VerifyIO& io, const Veri
   return a;
 }
 
-static SampleArgs sample_args(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws) {
-  SampleArgs a{};
-  a.target = io.target;
-  a.draft = io.draft;
-  a.uniforms = io.uniforms;
-  a.B = s.B;
-  a.K = s.K;
-  a.V = s.V;
-  a.NT = s.NT_s;
-  a.NG = s.NG_s;
-  a.s64 = log2e_over(io.temperature);
-  a.s_hi = (float)a.s64;
-  a.s_lo = (float)(a.s64 - (double)a.s_hi);
-  a.row_m = ws.row_m;
-  a.row_z = ws.row_z;
-  a.job = ws.job;
-  a.part = ws.part_b;
-  a.accepted_len = io.accepted_len;
-  a.out_tokens = io.out_tokens;
-  return a;
-}
-
 hipError_t launch_stats(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {
   if (s.B == 0 || s.K == 0) return hipSuccess;
-  const StatsArgs a = stats_args(s, io, ws);
+  const VerifyArgs a = verify_args(s, io, ws);
   const dim3 grid((unsigned)((size_t)s.B * 2 * s.K * s.NG));
   return dispatch4(s.dtype, s.aligned, grid, st, stats_kernel<uint16_t, true>, stats_kernel<uint16_t, false>,
                    stats_kernel<float, true>, stats_kernel<float, false>, a);
 }
 
-hipError_t launch_accept(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {
-  if (s.B == 0 || s.K == 0) return hipSuccess;
-  const StatsArgs a = stats_args(s, io, ws);
-  if (s.dtype == 1) hipLaunchKernelGGL(accept_kernel<uint16_t>, dim3(s.B), dim3(kBlock), 0, st, a);
-  else hipLaunchKernelGGL(accept_kernel<float>, dim3(s.B), dim3(kBlock), 0, st, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_sample(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {
   if (s.B == 0) return hipSuccess;
-  const SampleArgs a = sample_args(s, io, ws);
+  const VerifyArgs a = verify_args(s, io, ws);
   const dim3 grid((unsigned)((size_t)s.B * s.NG_s));
   return dispatch4(s.dtype, s.aligned, grid, st, sample_kernel<uint16_t, true>, sample_kernel<uint16_t, false>,
                    sample_kernel<float, true>, sample_kernel<float, false>, a);
@@ -712,7 +666,7 @@ hipError_t launch_sample(const VerifyShape& s, const VerifyIO& io, const VerifyW
 
 hipError_t launch_pick(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {
   if (s.B == 0) return hipSuccess;
-  const SampleArgs a = sample_args(s, io, ws);
+  const VerifyArgs a = verify_args(s, io, ws);
   return dispatch4(s.dtype, s.aligned, dim3(s.B), st, pick_kernel<uint16_t, true>, pick_kernel<uint16_t, false>,
                    pick_kernel<float, true>, pick_kernel<float, false>, a);
 }

@@ -65,6 +65,35 @@ def traffic_from_profile():
     return float(m_tr.group(1))
 
 
+def cpu_baseline(case, res, args, K):
+    """The fp64 C oracle on the host cores, timed on a bounded sample of the
+    same batch: the first --cpu-sample sequences, repeated until about
+    --cpu-seconds of thread time has been spent (at most 20 repetitions)."""
+    import numpy as np
+
+    import oracle
+    B = case.B
+    nb = min(args.cpu_sample, B)
+    sl = slice(0, nb)
+    greedy = args.mode == "greedy"
+    tgt_h = case.target[sl].cpu()
+    dr_h = None if greedy else case.draft[sl].cpu()
+    tok_h = case.draft_tokens[sl].cpu()
+    uni_h = None if greedy else case.uniforms[sl].cpu()
+    threads = oracle.default_threads()
+    mode = oracle.GREEDY if greedy else oracle.SAMPLE
+    reps, wall = 0, 0.0
+    while reps < 20 and (reps == 0 or wall * threads < args.cpu_seconds):
+        t1 = time.perf_counter()
+        orc = oracle.verify(tgt_h, dr_h, tok_h, uni_h, case.temperature, mode=mode, threads=threads)
+        wall += time.perf_counter() - t1
+        reps += 1
+    agree = int(np.sum(orc["accepted_len"] == res[0][sl].cpu().numpy()))
+    return {"value": reps * nb * (K + 1) / wall, "unit": "positions/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {nb} of {B} sequences of the same batch x {reps} repetitions, fp64 C oracle, "
+                      f"{threads} threads, {wall:.2f} s wall; accepted_len agrees on {agree}/{nb}"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -72,7 +101,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="b256_k7_v262144_bf16")
     ap.add_argument("--mode", default="sample", choices=["sample", "greedy"])
-    ap.add_argument("--cpu-sample", type=int, default=32, help="sequences timed on the CPU oracle")
+    ap.add_argument("--cpu-sample", type=int, default=256, help="sequences timed on the CPU oracle")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="thread-seconds of oracle work to time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run one plain device copy of this many GiB (PMC scaling reference)")
@@ -111,8 +141,8 @@ def main():
 
     ws = sv.Workspace(dev)
     stream = torch.cuda.current_stream(dev)
-
-    NE = sv.TIMED_EVENTS
+    L = sv.spec_verify_launch_count(B, K, V, case.target.dtype, args.mode)
+    NE = L + 1
 
     def mk_events(n):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(NE * n)]
@@ -143,11 +173,8 @@ def main():
     def span(i, j):
         return float(np.mean([evs[NE * s + i].elapsed_time(evs[NE * s + j]) for s in range(args.steps)]))
 
-    if args.mode == "sample":
-        k_ms = {"stats": span(0, 1), "sample_with_accept": span(1, 2), "pick": span(2, 3),
-                "events_step": span(0, 4)}
-    else:
-        k_ms = {"greedy": span(0, 1), "greedy_finalize": span(1, 2), "events_step": span(0, 4)}
+    launch_ms = [span(k, k + 1) for k in range(L)]
+    k_ms = {"launches": launch_ms, "events_step": span(0, L)}
     acc = res[0].float()
     mean_tokens = float((acc[acc >= 0] + 1).mean()) if (acc >= 0).any() else float("nan")
 
@@ -155,33 +182,18 @@ def main():
     value = positions / (ms_step * 1e-3)
     if args.mode == "sample":
         step_bytes = B * (2 * K + 1) * V * esz          # every logit read once
-        dom_bytes = B * 2 * K * V * esz                 # rows 0..K-1 of target and draft
-        dom_name, dom_ms = "stats_kernel (row statistics)", k_ms["stats"]
+        dom_bytes = B * 2 * K * V * esz                 # launch 0: rows 0..K-1 of target and draft
+        dom_name, dom_ms = "stats_kernel (per-tile max and exp sums of the proposal rows)", launch_ms[0]
     else:
         step_bytes = B * (K + 1) * V * esz
         dom_bytes = step_bytes
-        dom_name, dom_ms = "greedy_kernel (per-tile argmax)", k_ms["greedy"]
+        dom_name, dom_ms = "greedy_kernel (per-tile argmax)", launch_ms[0]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = traffic_from_profile() if (args.workload == "b256_k7_v262144_bf16" and args.mode == "sample") else None
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        nb = min(args.cpu_sample, B)
-        sl = slice(0, nb)
-        tgt_h = case.target[sl].cpu()
-        dr_h = case.draft[sl].cpu() if args.mode == "sample" else None
-        tok_h = case.draft_tokens[sl].cpu()
-        uni_h = case.uniforms[sl].cpu()
-        threads = oracle.default_threads()
-        t1 = time.perf_counter()
-        orc = oracle.verify(tgt_h, dr_h, tok_h, uni_h, case.temperature,
-                            mode=oracle.GREEDY if args.mode == "greedy" else oracle.SAMPLE, threads=threads)
-        cpu_s = time.perf_counter() - t1
-        agree = int(np.sum(orc["accepted_len"] == res[0][sl].cpu().numpy()))
-        cpu = {"value": nb * (K + 1) / cpu_s, "unit": "positions/s", "cores": threads, "kind": "oracle",
-               "sample": f"first {nb} of {B} sequences of the same batch, fp64 C oracle, {threads} threads, "
-                         f"{cpu_s:.2f} s wall; accepted_len agrees on {agree}/{nb}"}
+        cpu = cpu_baseline(case, res, args, K)
 
     out = {
         "metric": "verified draft positions/sec (B*(K+1)) and achieved HBM GB/s vs peak",
@@ -231,7 +243,8 @@ def bench_shortlist(args, dev):
     uni = verify_uniforms(B, K, (0, 5, 0, 3, 0), dev)
     ws = sv.Workspace(dev)
     stream = torch.cuda.current_stream(dev)
-    NE = sv.TIMED_EVENTS
+    L = sv.spec_verify_launch_count(B, K + 1 - 1, V, torch.bfloat16, "sample")
+    NE = L + 1
 
     def step(evs=None):
         if evs is not None:
@@ -260,8 +273,8 @@ def bench_shortlist(args, dev):
         return float(np.mean([evs[(NE + 2) * s + i].elapsed_time(evs[(NE + 2) * s + j]) for s in range(args.steps)]))
 
     head_ms = span(0, 1)
-    k_ms = {"head": head_ms, "stats": span(2, 3), "sample_with_accept": span(3, 4), "pick": span(4, 5),
-            "events_step": span(0, 6)}
+    k_ms = {"head": head_ms, "verify_launches": [span(2 + k, 3 + k) for k in range(L)],
+            "events_step": span(0, 2 + L)}
     sel = torch.unique(hc.cluster_ids).numel()
     w_bytes = sel * cs * d * 2
     head_bytes = w_bytes + B * K * d * 2 + B * K * V * 2          # W of the selected clusters, h, dense bf16 out

@@ -43,7 +43,6 @@ extern "C" {
 
 #define SPEC_ABI_VERSION 1
 #define SPEC_MAX_K 64
-#define SPEC_TIMED_EVENTS 5
 
 typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
 typedef enum { SPEC_MODE_SAMPLE = 0, SPEC_MODE_GREEDY = 1 } spec_mode_t;
@@ -109,13 +108,19 @@ spec_status_t spec_verify(const void* target_logits, const void* draft_logits,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Number of kernel launches spec_verify makes for this shape (0 for an empty
+ * or invalid shape).  SAMPLE mode: 3 (row statistics; accept decisions and
+ * the sampled rows' tile sums; token pick).  GREEDY mode: 2 (per-tile argmax,
+ * then per-sequence finalize).
+ */
+int32_t spec_verify_launch_count(int32_t B, int32_t K, int32_t V, spec_dtype_t dtype, spec_mode_t mode);
+
+/*
  * spec_verify with kernel timing.  Identical work and launches; in addition
- * events[0..SPEC_TIMED_EVENTS-1] (hipEvent_t passed as void*, any may be NULL)
- * are recorded on `stream`.  SAMPLE mode: [0] before the row-statistics
- * kernel, [1] after it, [2] after the sampling kernel (accept decisions and
- * the sampled rows' tile sums), [3] and [4] after the token-pick kernel.
- * GREEDY mode: [0] before the argmax kernel, [1] after it, [2], [3] and [4]
- * after its finalize kernel.
+ * events[k] (a hipEvent_t passed as void*) is recorded on `stream` before
+ * launch k for k < spec_verify_launch_count(), and events[launch count] after
+ * the last launch.  Entries at or beyond n_events, and NULL entries, are
+ * skipped.
  */
 spec_status_t spec_verify_timed(const void* target_logits, const void* draft_logits,
                                 const int32_t* draft_tokens, const float* uniforms,
@@ -124,7 +129,7 @@ spec_status_t spec_verify_timed(const void* target_logits, const void* draft_log
                                 int32_t* accepted_len, int32_t* out_tokens,
                                 float* p_target_at_draft, float* p_draft_at_draft,
                                 void* workspace, size_t workspace_bytes, void* stream,
-                                void* const* events);
+                                void* const* events, int32_t n_events);
 
 /*
  * Shortlisted drafter head (DynaSpec summary, "Model architecture", items 1,

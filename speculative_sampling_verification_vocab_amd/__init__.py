@@ -18,12 +18,11 @@ import torch
 from . import _native
 from ._native import SpecVerifyError  # noqa: F401
 
-__all__ = ["spec_verify", "spec_verify_workspace_bytes", "spec_draft_head_shortlist",
+__all__ = ["spec_verify", "spec_verify_workspace_bytes", "spec_verify_launch_count", "spec_draft_head_shortlist",
            "Workspace", "SpecVerifyError", "abi_version"]
 
 _DTYPES = {torch.bfloat16: _native.SPEC_BF16, torch.float32: _native.SPEC_F32}
 _MODES = {"sample": _native.SPEC_MODE_SAMPLE, "greedy": _native.SPEC_MODE_GREEDY}
-TIMED_EVENTS = 5
 
 
 def abi_version() -> int:
@@ -48,6 +47,11 @@ def _stream_handle(device: torch.device, stream=None):
 
 def spec_verify_workspace_bytes(B: int, K: int, V: int, dtype: torch.dtype, mode: str = "sample") -> int:
     return int(_native.load().spec_verify_workspace_bytes(B, K, V, _DTYPES[dtype], _MODES[mode]))
+
+
+def spec_verify_launch_count(B: int, K: int, V: int, dtype: torch.dtype, mode: str = "sample") -> int:
+    """Kernel launches of one spec_verify call (timing events needed: this + 1)."""
+    return int(_native.load().spec_verify_launch_count(B, K, V, _DTYPES[dtype], _MODES[mode]))
 
 
 class Workspace:
@@ -84,8 +88,8 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_token
     target [B, K+1, V] and draft [B, K, V] (bf16 or float32), draft_tokens int32
     [B, K], uniforms float32 [B, K+1, 2].  Returns (accepted_len int32 [B],
     out_tokens int32 [B, K+1]) and, with return_probs, also (P_t(d), P_d(d))
-    float32 [B, K].  `events`: up to five recorded torch.cuda.Event objects,
-    re-recorded around the kernels (see spec_verify_timed in the C header).
+    float32 [B, K].  `events`: recorded torch.cuda.Event objects, re-recorded
+    before each kernel launch and after the last (see spec_verify_timed).
     """
     if mode not in _MODES:
         raise ValueError(f"mode must be one of {list(_MODES)}")
@@ -128,9 +132,9 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_token
             B, K, V, dt, ctypes.c_float(temperature if mode == "sample" else 0.0), _MODES[mode],
             _ptr(acc), _ptr(out), _ptr(pt), _ptr(pd), _ptr(ws), ws.numel(), _stream_handle(dev, stream)]
     if events is not None:
-        evs = list(events) + [None] * (TIMED_EVENTS - len(events))
-        arr = (ctypes.c_void_p * TIMED_EVENTS)(*[e.cuda_event if e is not None else None for e in evs])
-        st = lib.spec_verify_timed(*args, arr)
+        evs = list(events)
+        arr = (ctypes.c_void_p * max(1, len(evs)))(*[e.cuda_event if e is not None else None for e in evs])
+        st = lib.spec_verify_timed(*args, arr, len(evs))
     else:
         st = lib.spec_verify(*args)
     _native.check(st, "spec_verify")

@@ -51,8 +51,10 @@ def load() -> ctypes.CDLL:
                        P, P, P, P, P, sz, P]
         lib.spec_verify.argtypes = verify_args
         lib.spec_verify.restype = ctypes.c_int
-        lib.spec_verify_timed.argtypes = verify_args + [P]
+        lib.spec_verify_timed.argtypes = verify_args + [P, i32]
         lib.spec_verify_timed.restype = ctypes.c_int
+        lib.spec_verify_launch_count.argtypes = [i32, i32, i32, ctypes.c_int, ctypes.c_int]
+        lib.spec_verify_launch_count.restype = i32
         lib.spec_draft_head_shortlist.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, P, P,
                                                   ctypes.c_int, P, sz, P]
         lib.spec_draft_head_shortlist.restype = ctypes.c_int

@@ -28,7 +28,7 @@ spec_status_t check_shape(int32_t B, int32_t K, int32_t V, spec_dtype_t dtype, s
   const sv::VerifyShape s = sv::make_shape(B, K, V, dtype == SPEC_BF16 ? 1 : 0, false);
   const size_t per_seq_rows = mode == SPEC_MODE_GREEDY ? (size_t)(K + 1) : (size_t)(2 * K);
   if ((size_t)B * per_seq_rows * (size_t)s.NG > kMaxGrid) return SPEC_ERR_UNSUPPORTED;
-  if ((size_t)B * (size_t)s.NG_s > kMaxGrid) return SPEC_ERR_UNSUPPORTED;
+  if ((size_t)B * (2 * (size_t)K * s.NG + s.NG_s + 1) > kMaxGrid) return SPEC_ERR_UNSUPPORTED;
   return SPEC_OK;
 }
 
@@ -36,17 +36,17 @@ spec_status_t verify_impl(const void* target_logits, const void* draft_logits, c
                           const float* uniforms, int32_t B, int32_t K, int32_t V, spec_dtype_t dtype,
                           float temperature, spec_mode_t mode, int32_t* accepted_len, int32_t* out_tokens,
                           float* p_target_at_draft, float* p_draft_at_draft, void* workspace,
-                          size_t workspace_bytes, void* stream, void* const* events) {
+                          size_t workspace_bytes, void* stream, void* const* events, int n_events) {
   const spec_status_t sc = check_shape(B, K, V, dtype, mode);
   if (sc != SPEC_OK) return sc;
   const bool sample = mode == SPEC_MODE_SAMPLE;
   if (sample && !(temperature > 0.0f && isfinite(temperature))) return SPEC_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   auto record = [&](int i) {
-    if (events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
+    if (events && i < n_events && events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
   };
   if (B == 0) {
-    for (int i = 0; i < SPEC_TIMED_EVENTS; ++i) record(i);
+    record(0);
     return SPEC_OK;
   }
   if (!target_logits || !accepted_len || !out_tokens) return SPEC_ERR_INVALID_ARG;
@@ -77,23 +77,15 @@ spec_status_t verify_impl(const void* target_logits, const void* draft_logits, c
   io.p_draft = p_draft_at_draft;
 
   (void)hipGetLastError();  // clear a stale error so the checks below see only ours
-  record(0);
   hipError_t e = hipSuccess;
   if (sample) {
-    e = sv::launch_stats(s, io, ws, st);
-    record(1);
-    if (e == hipSuccess) e = sv::launch_sample(s, io, ws, st);
-    record(2);
-    if (e == hipSuccess) e = sv::launch_pick(s, io, ws, st);
-    record(3);
-    record(4);
+    e = sv::launch_sample_pipeline(s, io, ws, st, events, n_events);
   } else {
+    record(0);
     e = sv::launch_greedy(s, io, ws, st);
     record(1);
     if (e == hipSuccess) e = sv::launch_greedy_finalize(s, io, ws, st);
     record(2);
-    record(3);
-    record(4);
   }
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
@@ -128,17 +120,23 @@ spec_status_t spec_verify(const void* target_logits, const void* draft_logits, c
                           size_t workspace_bytes, void* stream) {
   return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, B, K, V, dtype, temperature, mode,
                      accepted_len, out_tokens, p_target_at_draft, p_draft_at_draft, workspace, workspace_bytes,
-                     stream, nullptr);
+                     stream, nullptr, 0);
 }
 
 spec_status_t spec_verify_timed(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
                                 const float* uniforms, int32_t B, int32_t K, int32_t V, spec_dtype_t dtype,
                                 float temperature, spec_mode_t mode, int32_t* accepted_len, int32_t* out_tokens,
                                 float* p_target_at_draft, float* p_draft_at_draft, void* workspace,
-                                size_t workspace_bytes, void* stream, void* const* events) {
+                                size_t workspace_bytes, void* stream, void* const* events, int32_t n_events) {
   return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, B, K, V, dtype, temperature, mode,
                      accepted_len, out_tokens, p_target_at_draft, p_draft_at_draft, workspace, workspace_bytes,
-                     stream, events);
+                     stream, events, n_events);
+}
+
+int32_t spec_verify_launch_count(int32_t B, int32_t K, int32_t V, spec_dtype_t dtype, spec_mode_t mode) {
+  if (check_shape(B, K, V, dtype, mode) != SPEC_OK || B == 0) return 0;
+  if (mode == SPEC_MODE_GREEDY) return 2;
+  return sv::sample_launches(sv::make_shape(B, K, V, dtype == SPEC_BF16 ? 1 : 0, false));
 }
 
 spec_status_t spec_draft_head_shortlist(const void* h, const void* W, const int32_t* cluster_ids, int32_t B,

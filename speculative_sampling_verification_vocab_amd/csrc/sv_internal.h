@@ -68,10 +68,13 @@ int tile_elems(int dtype);
 VerifyShape make_shape(int B, int K, int V, int dtype, bool aligned);
 size_t verify_workspace_layout(const VerifyShape& s, bool greedy, void* base, VerifyWorkspace* out);
 
-// SAMPLE: stats -> sample (with accept decisions) -> pick.  GREEDY: greedy -> greedy_finalize.
-hipError_t launch_stats(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);
-hipError_t launch_sample(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);
-hipError_t launch_pick(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);
+// SAMPLE: three launches (statistics, sampling with accept decisions, pick).
+// events[k] (if present, k < n_events) is recorded before launch k and
+// events[3] after the last one.
+int sample_launches(const VerifyShape& s);
+hipError_t launch_sample_pipeline(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws,
+                                  hipStream_t st, void* const* events, int n_events);
+// GREEDY: greedy -> greedy_finalize.
 hipError_t launch_greedy(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);
 hipError_t launch_greedy_finalize(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws,
                                   hipStream_t st);

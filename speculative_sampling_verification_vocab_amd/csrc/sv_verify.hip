@@ -74,14 +74,15 @@ __device__ __forceinline__ const T* row_ptr(const void* base, size_t rows_before
 // Row statistics.
 // ---------------------------------------------------------------------------
 
+// Block `blk` of the statistics pass over the sequences starting at b0.
 template <typename T, bool kAligned>
-__global__ void __launch_bounds__(kBlock) stats_kernel(VerifyArgs a) {
+__device__ __forceinline__ void stats_block(const VerifyArgs& a, int blk, int b0) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int K = a.K, R = 2 * K;
-  const int g = blockIdx.x % a.NG;
-  const int rb = blockIdx.x / a.NG;
+  const int g = blk % a.NG;
+  const int rb = blk / a.NG;
   const int r = rb % R;
-  const int b = rb / R;
+  const int b = b0 + rb / R;
   const T* row = r < K ? row_ptr<T>(a.target, (size_t)b * (K + 1) + r, a.V)
                        : row_ptr<T>(a.draft, (size_t)b * K + (r - K), a.V);
   const int t = g * kWavesPerBlock + wave;
@@ -234,12 +235,13 @@ __device__ __forceinline__ void tile_exp(const float (&x)[N], float m, const Ver
 // Sampling pass: accept decisions, then the tile sums of the sampled row(s).
 // ---------------------------------------------------------------------------
 
+// Block `blk` of the sampling pass over the sequences starting at b0.
 template <typename T, bool kAligned>
-__global__ void __launch_bounds__(kBlock) sample_kernel(VerifyArgs a) {
+__device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk, int b0) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int K = a.K;
-  const int g = blockIdx.x % a.NGs;
-  const int b = blockIdx.x / a.NGs;
+  const int g = blk % a.NGs;
+  const int b = b0 + blk / a.NGs;
   SampleRowInfo sr;
   const int n = accept_sequence<T>(a, b, g == 0, &sr);
   if (n < 0) return;  // faulty sequence: outputs already written
@@ -288,14 +290,14 @@ __global__ void __launch_bounds__(kBlock) sample_kernel(VerifyArgs a) {
 
 // One block per sequence, after sample_kernel: the inverse-CDF choice of tile
 // from the tile masses, then a four-wave scan of that tile in token-id order.
+// Token pick of sequence b.
 template <typename T, bool kAligned>
-__global__ void __launch_bounds__(kBlock) pick_kernel(VerifyArgs a) {
+__device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
   __shared__ double sh_d[kWavesPerBlock];
   __shared__ float sh_f[kWavesPerBlock];
   __shared__ int sh_i[kWavesPerBlock];
   __shared__ double sh_scan[kWavesPerBlock];
   __shared__ double sh_cbefore;
-  const int b = blockIdx.x;
   const SampleRowInfo sr = a.rows[b];
   const int K = a.K, NT = a.NTs, n = K == 0 ? 0 : sr.n;
   if (n < 0) return;
@@ -457,6 +459,21 @@ __global__ void __launch_bounds__(kBlock) pick_kernel(VerifyArgs a) {
     if (token < 0)
       for (int i = 0; i <= K; ++i) a.out_tokens[(size_t)b * (K + 1) + i] = -1;
   }
+}
+
+template <typename T, bool kAligned>
+__global__ void __launch_bounds__(kBlock) stats_kernel(VerifyArgs a) {
+  stats_block<T, kAligned>(a, blockIdx.x, 0);
+}
+
+template <typename T, bool kAligned>
+__global__ void __launch_bounds__(kBlock) sample_kernel(VerifyArgs a) {
+  sample_block<T, kAligned>(a, blockIdx.x, 0);
+}
+
+template <typename T, bool kAligned>
+__global__ void __launch_bounds__(kBlock) pick_kernel(VerifyArgs a) {
+  pick_block<T, kAligned>(a, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -648,27 +665,31 @@ static VerifyArgs verify_args(const VerifyShape& s, const VerifyIO& io, const Ve
   return a;
 }
 
-hipError_t launch_stats(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {
-  if (s.B == 0 || s.K == 0) return hipSuccess;
-  const VerifyArgs a = verify_args(s, io, ws);
-  const dim3 grid((unsigned)((size_t)s.B * 2 * s.K * s.NG));
-  return dispatch4(s.dtype, s.aligned, grid, st, stats_kernel<uint16_t, true>, stats_kernel<uint16_t, false>,
-                   stats_kernel<float, true>, stats_kernel<float, false>, a);
-}
+int sample_launches(const VerifyShape& s) { return s.B == 0 ? 0 : 3; }
 
-hipError_t launch_sample(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {
+hipError_t launch_sample_pipeline(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws,
+                                  hipStream_t st, void* const* events, int n_events) {
   if (s.B == 0) return hipSuccess;
   const VerifyArgs a = verify_args(s, io, ws);
-  const dim3 grid((unsigned)((size_t)s.B * s.NG_s));
-  return dispatch4(s.dtype, s.aligned, grid, st, sample_kernel<uint16_t, true>, sample_kernel<uint16_t, false>,
-                   sample_kernel<float, true>, sample_kernel<float, false>, a);
-}
-
-hipError_t launch_pick(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {
-  if (s.B == 0) return hipSuccess;
-  const VerifyArgs a = verify_args(s, io, ws);
-  return dispatch4(s.dtype, s.aligned, dim3(s.B), st, pick_kernel<uint16_t, true>, pick_kernel<uint16_t, false>,
-                   pick_kernel<float, true>, pick_kernel<float, false>, a);
+  auto record = [&](int k) {
+    if (events && k < n_events && events[k]) (void)hipEventRecord(static_cast<hipEvent_t>(events[k]), st);
+  };
+  hipError_t e = hipSuccess;
+  record(0);
+  if (s.K > 0)
+    e = dispatch4(s.dtype, s.aligned, dim3((unsigned)((size_t)s.B * 2 * s.K * s.NG)), st,
+                  stats_kernel<uint16_t, true>, stats_kernel<uint16_t, false>, stats_kernel<float, true>,
+                  stats_kernel<float, false>, a);
+  record(1);
+  if (e == hipSuccess)
+    e = dispatch4(s.dtype, s.aligned, dim3((unsigned)((size_t)s.B * s.NG_s)), st, sample_kernel<uint16_t, true>,
+                  sample_kernel<uint16_t, false>, sample_kernel<float, true>, sample_kernel<float, false>, a);
+  record(2);
+  if (e == hipSuccess)
+    e = dispatch4(s.dtype, s.aligned, dim3((unsigned)s.B), st, pick_kernel<uint16_t, true>,
+                  pick_kernel<uint16_t, false>, pick_kernel<float, true>, pick_kernel<float, false>, a);
+  record(3);
+  return e;
 }
 
 hipError_t launch_greedy(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st) {

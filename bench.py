@@ -36,31 +36,33 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HEAD_WORKLOAD = "shortlist_head_b32_k4_d4096_v128256"
 PROFILE_PMC = os.path.join(ROOT, "profiles", "stats_kernel_b256_k7_v262144_bf16_pmc.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "speculative_sampling_verification_vocab_amd", "csrc", f)
-                  for f in ("sv_verify.hip", "sv_common.h")]
+HEAD_PROFILE_PMC = os.path.join(ROOT, "profiles", "head_mfma_kernel_shortlist_b32_k4_d4096_v128256_pmc.md")
+CSRC = os.path.join(ROOT, "speculative_sampling_verification_vocab_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("sv_verify.hip", "sv_common.h")]
+HEAD_SOURCES = [os.path.join(CSRC, f) for f in ("sv_head.hip", "sv_common.h")]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
+def source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile():
-    """HBM bytes per stats-kernel launch from the committed PMC summary, if it
-    was taken on the current kernel source."""
-    if not os.path.exists(PROFILE_PMC):
+def traffic_from_profile(path=PROFILE_PMC, sources=KERNEL_SOURCES):
+    """HBM bytes per launch of the dominant kernel from a committed PMC
+    summary, if it was taken on the current kernel source."""
+    if not os.path.exists(path):
         return None
-    txt = open(PROFILE_PMC).read()
+    txt = open(path).read()
     m_hash = re.search(r"source_sha256:\s*([0-9a-f]+)", txt)
     m_tr = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m_hash or not m_tr or m_hash.group(1) != source_hash():
+    if not m_hash or not m_tr or m_hash.group(1) != source_hash(sources):
         return None
     return float(m_tr.group(1))
 
@@ -120,15 +122,6 @@ def main():
     from workloads import workload_case
 
     dev = torch.device("cuda", 0)
-    if args.workload == HEAD_WORKLOAD:
-        return bench_shortlist(args, dev)
-    t0 = time.time()
-    case = workload_case(args.workload, device=dev, greedy=args.mode == "greedy")
-    torch.cuda.synchronize()
-    B, K, V = case.B, case.K, case.V
-    esz = 2 if case.dtype == "bf16" else 4
-    log(f"inputs generated in {time.time() - t0:.1f}s: B={B} K={K} V={V} {case.dtype} T={case.temperature}")
-
     if args.calibrate_copy_gib > 0:
         n = int(args.calibrate_copy_gib * (1 << 30)) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -138,6 +131,14 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy: {n * 4} bytes read, {n * 4} bytes written")
         del a, b
+    if args.workload == HEAD_WORKLOAD:
+        return bench_shortlist(args, dev)
+    t0 = time.time()
+    case = workload_case(args.workload, device=dev, greedy=args.mode == "greedy")
+    torch.cuda.synchronize()
+    B, K, V = case.B, case.K, case.V
+    esz = 2 if case.dtype == "bf16" else 4
+    log(f"inputs generated in {time.time() - t0:.1f}s: B={B} K={K} V={V} {case.dtype} T={case.temperature}")
 
     ws = sv.Workspace(dev)
     stream = torch.cuda.current_stream(dev)
@@ -294,7 +295,8 @@ def bench_shortlist(args, dev):
         "kernels_ms": k_ms,
         "mean_tokens_per_verify": float((acc[acc >= 0] + 1).mean()),
         "roofline": {"bound": "hbm", "kernel": "head_mfma_kernel (shortlist gather-GEMM)", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profile(HEAD_PROFILE_PMC, HEAD_SOURCES),
                      "algorithmic_bytes_per_launch": head_bytes},
         "mfma": {"achieved_tflops": tflops, "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                  "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "flops_per_launch": flops,

@@ -89,6 +89,61 @@ __device__ __forceinline__ void load_tile(const T* __restrict__ row, int V, int 
   }
 }
 
+// The same tile slice kept in its storage format: NL 16-byte vectors per lane
+// (8 bf16 or 4 f32 each), -inf beyond V.  Kernels that hold a tile across a
+// long computation keep it packed (half the registers for bf16) and unpack an
+// element when they use it with raw_elem; the values are bit-identical to
+// load_tile's.
+template <typename T, bool kAligned, int L, int NL>
+__device__ __forceinline__ void load_raw(const T* __restrict__ row, int V, int t, int lane, u32x4 (&raw)[NL]) {
+  constexpr int V8 = Elem<T>::kVec;
+  static_assert(NL <= L, "tile slice");
+  const int base = t * (kWave * L * V8) + lane * V8;
+  constexpr uint32_t kNinf = sizeof(T) == 2 ? 0xff80ff80u : 0xff800000u;
+  if constexpr (kAligned) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int off = base + j * (kWave * V8);
+      raw[j] = off < V ? *reinterpret_cast<const u32x4*>(row + off) : u32x4{kNinf, kNinf, kNinf, kNinf};
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (sizeof(T) == 2) {
+          const int off = base + j * (kWave * V8) + 2 * q;
+          const uint32_t lo = off < V ? (uint32_t)row[off] : 0xff80u;
+          const uint32_t hi = off + 1 < V ? (uint32_t)row[off + 1] : 0xff80u;
+          raw[j][q] = lo | (hi << 16);
+        } else {
+          const int off = base + j * (kWave * V8) + q;
+          raw[j][q] = off < V ? __float_as_uint(row[off]) : kNinf;
+        }
+      }
+    }
+  }
+}
+
+// Element e (0 .. NL*kVec-1, in the lane's token-id order) of a packed slice.
+template <typename T, int NL>
+__device__ __forceinline__ float raw_elem(const u32x4 (&raw)[NL], int e) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w = raw[e / 8][(e % 8) / 2];
+    return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+  } else {
+    return __uint_as_float(raw[e / 4][e % 4]);
+  }
+}
+
+template <typename T, int NL>
+__device__ __forceinline__ float raw_lane_max(const u32x4 (&raw)[NL]) {
+  float m = raw_elem<T>(raw, 0);
+#pragma unroll
+  for (int e = 1; e < NL * Elem<T>::kVec; ++e) m = fmaxf(m, raw_elem<T>(raw, e));
+  return m;
+}
+
 template <int N>
 __device__ __forceinline__ float lane_max(const float (&x)[N]) {
   float m = x[0];

@@ -43,6 +43,7 @@ struct VerifyShape {
   int NG;        // blocks (4 tiles each) per row
   int NT_s;      // sampling-pass tiles per row
   int NG_s;      // sampling-pass blocks per row
+  int TPW_s;     // sampling-pass tiles per wave
 };
 
 struct VerifyWorkspace {

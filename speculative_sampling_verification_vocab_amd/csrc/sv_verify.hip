@@ -11,11 +11,12 @@
 //     every accept decision u < min(1, P_t/P_d) and finds the first rejection
 //     n (Speculative Decoding lesson, nextadmin.net, "Core algorithm" steps
 //     4-5, "Step 1"); the sequence's first block writes those outputs.  The
-//     block then re-reads only what the output token at n needs: one tile of
+//     block then re-reads only what the output token at n needs: its tiles of
 //     target and draft row n at a rejection (residual (P_t - P_d)_+, "Step 2"),
 //     or of target row K when every draft was accepted (bonus token, step 6),
 //     recomputing every element with a compensated exponential and summing in
-//     double.
+//     double.  Small batches use one tile per wave, large ones up to eight so
+//     that the prologue is paid less often.
 //  3. pick_kernel (one block per sequence) turns the tile masses into an
 //     inverse-CDF choice of tile, then scans that one tile in token-id order.
 //
@@ -25,7 +26,10 @@
 // The statistics pass is deliberately cheap (its normalisers only decide
 // accept tests, ~1e-7 relative is ample); the sampling pass recomputes the
 // normalisers of the row pair it samples from with the accurate exponential,
-// so the inverse-CDF boundaries carry only per-element rounding.
+// so the inverse-CDF boundaries carry only per-element rounding.  At a
+// rejection it takes the statistics pass's tile maxima as its exponent
+// references, so it needs no reduction before the exponentials and both
+// sampling kernels read the same references.
 //
 // GREEDY mode runs greedy_kernel (argmax per tile, first index on ties) and
 // greedy_finalize_kernel (argmax per row and the longest prefix of drafts equal
@@ -41,8 +45,10 @@ namespace sv {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr int kTilesPerWaveS = 4;  // sampling tiles per wave: amortises the per-block accept prologue
-constexpr int kTilesPerBlockS = kTilesPerWaveS * kWavesPerBlock;
+// Sampling tiles per wave: several amortise the per-block accept prologue
+// over more work; small batches take fewer so the grid still fills the chip.
+constexpr int kMaxTilesPerWaveS = 8;
+constexpr int kSampleBlocksWanted = 1024;  // 4 per CU
 
 struct VerifyArgs {
   const void* target;
@@ -52,6 +58,7 @@ struct VerifyArgs {
   int B, K, V;
   int NT, NG;            // statistics pass: tiles (kTile ids) and blocks per row
   int NTs, NGs;          // sampling pass: tiles (kTileS ids) and blocks per row
+  int TPWs;              // sampling pass: tiles per wave
   float s_hi, s_lo;      // log2(e)/T as a float pair
   float dmin;            // clamp for x - m in the accurate exponential: -200 / s_hi
   double s64;            // log2(e)/T in double
@@ -74,31 +81,40 @@ __device__ __forceinline__ const T* row_ptr(const void* base, size_t rows_before
 // Row statistics.
 // ---------------------------------------------------------------------------
 
-// Block `blk` of the statistics pass over the sequences starting at b0.
+// (tile max, tile sum) of one statistics tile.
+template <typename T>
+__device__ __forceinline__ void stats_tile(const VerifyArgs& a, const float (&x)[kPerLane<T>], TileStat* out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const float ml = lane_max(x);
+  float sl = 0.0f;
+  if (ml != kNegInf) {
+#pragma unroll
+    for (int e = 0; e < kPerLane<T>; ++e) sl += exp2_fast((x[e] - ml) * a.s_hi);
+  }
+  const float M = wave_max(ml);
+  const float scaled = ml == kNegInf ? 0.0f : sl * exp2_fast((ml - M) * a.s_hi);
+  const float S = wave_sum(scaled);
+  if (lane == 0) *out = TileStat{M, S};
+}
+
+// Block `blk` of the statistics pass: one tile per wave, all of its loads
+// issued at once.  (Several tiles per wave with the next one loaded during the
+// reduction measured 2-6 % slower: the extra registers cost occupancy.)
 template <typename T, bool kAligned>
-__device__ __forceinline__ void stats_block(const VerifyArgs& a, int blk, int b0) {
+__device__ __forceinline__ void stats_block(const VerifyArgs& a, int blk) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int K = a.K, R = 2 * K;
   const int g = blk % a.NG;
   const int rb = blk / a.NG;
   const int r = rb % R;
-  const int b = b0 + rb / R;
+  const int b = rb / R;
   const T* row = r < K ? row_ptr<T>(a.target, (size_t)b * (K + 1) + r, a.V)
                        : row_ptr<T>(a.draft, (size_t)b * K + (r - K), a.V);
   const int t = g * kWavesPerBlock + wave;
   if (t < a.NT) {
     float x[kPerLane<T>];
     load_tile<T, kAligned, kLoads>(row, a.V, t, lane, x);
-    const float ml = lane_max(x);
-    float sl = 0.0f;
-    if (ml != kNegInf) {
-#pragma unroll
-      for (int e = 0; e < kPerLane<T>; ++e) sl += exp2_fast((x[e] - ml) * a.s_hi);
-    }
-    const float M = wave_max(ml);
-    const float scaled = ml == kNegInf ? 0.0f : sl * exp2_fast((ml - M) * a.s_hi);
-    const float S = wave_sum(scaled);
-    if (lane == 0) a.part_a[((size_t)b * R + r) * a.NT + t] = TileStat{M, S};
+    stats_tile<T>(a, x, a.part_a + ((size_t)b * R + r) * a.NT + t);
   }
 }
 
@@ -110,6 +126,15 @@ __device__ __forceinline__ void stats_block(const VerifyArgs& a, int blk, int b0
 // outputs and the row data pick_kernel needs.  Returns n, or -1 for a faulty
 // sequence.
 // ---------------------------------------------------------------------------
+
+// Combines one row's statistics partials into (max, Z): Z = sum over tiles of
+// s * 2^((m_tile - max) * log2e/T), summed in double.
+__device__ __forceinline__ void combine_row(const TileStat q, const VerifyArgs& a, float& m, double& z) {
+  m = wave_max(q.m);
+  z = 0.0;
+  if (m != kNegInf && q.m != kNegInf) z = (double)q.s * (double)exp2_fast((q.m - m) * a.s_hi);
+  z = wave_sum(z);
+}
 
 template <typename T>
 __device__ int accept_sequence(const VerifyArgs& a, int b, bool write, SampleRowInfo* info) {
@@ -125,33 +150,63 @@ __device__ int accept_sequence(const VerifyArgs& a, int b, bool write, SampleRow
     return 0;
   }
   if (threadIdx.x == 0) sh_bad = 0;
-  // The drafted logits do not depend on the statistics: fetch them first.
+  // Loads that do not depend on the statistics go first: the drafted
+  // tokens, their logits and the accept uniforms.
   double xt = 0.0, xd = 0.0;
+  float u = 0.0f;
   int d = -1;
   if ((int)threadIdx.x < K) {
     const int i = threadIdx.x;
     d = a.tokens[(size_t)b * K + i];
+    u = a.uniforms[((size_t)b * (K + 1) + i) * 2];
     if (d >= 0 && d < a.V) {
       xt = (double)to_f32(row_ptr<T>(a.target, (size_t)b * (K + 1) + i, a.V)[d]);
       xd = (double)to_f32(row_ptr<T>(a.draft, (size_t)b * K + i, a.V)[d]);
     }
   }
-  for (int r = wave; r < R; r += kWavesPerBlock) {
-    const TileStat* p = a.part_a + ((size_t)b * R + r) * a.NT;
-    float m = kNegInf;
-    for (int t = lane; t < a.NT; t += kWave) m = fmaxf(m, p[t].m);
-    m = wave_max(m);
-    double z = 0.0;
-    if (m != kNegInf) {
-      for (int t = lane; t < a.NT; t += kWave) {
-        const TileStat q = p[t];
-        if (q.m != kNegInf) z += (double)q.s * (double)exp2_fast((q.m - m) * a.s_hi);
+  // Row (max, Z).  Wave w owns rows w, w+4, ...  When each row has at most 64
+  // tiles and a wave at most kRowsPerWave rows, every partial is loaded
+  // before the first reduction, so the block waits for one memory round trip.
+  constexpr int kRowsPerWave = 8;
+  const int rows_w = (R - wave + kWavesPerBlock - 1) / kWavesPerBlock;
+  const TileStat* pb = a.part_a + (size_t)b * R * a.NT;
+  if (a.NT <= kWave && rows_w <= kRowsPerWave) {
+    TileStat q[kRowsPerWave];
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) {
+      q[j] = TileStat{kNegInf, 0.0f};
+      if (j < rows_w && lane < a.NT) q[j] = pb[(size_t)(wave + j * kWavesPerBlock) * a.NT + lane];
+    }
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) {
+      if (j < rows_w) {
+        float m;
+        double z;
+        combine_row(q[j], a, m, z);
+        if (lane == 0) {
+          sh_m[wave + j * kWavesPerBlock] = m;
+          sh_z[wave + j * kWavesPerBlock] = z;
+        }
       }
     }
-    z = wave_sum(z);
-    if (lane == 0) {
-      sh_m[r] = m;
-      sh_z[r] = z;
+  } else {
+    for (int r = wave; r < R; r += kWavesPerBlock) {
+      const TileStat* p = pb + (size_t)r * a.NT;
+      float m = kNegInf;
+      for (int t = lane; t < a.NT; t += kWave) m = fmaxf(m, p[t].m);
+      m = wave_max(m);
+      double z = 0.0;
+      if (m != kNegInf) {
+        for (int t = lane; t < a.NT; t += kWave) {
+          const TileStat q = p[t];
+          if (q.m != kNegInf) z += (double)q.s * (double)exp2_fast((q.m - m) * a.s_hi);
+        }
+      }
+      z = wave_sum(z);
+      if (lane == 0) {
+        sh_m[r] = m;
+        sh_z[r] = z;
+      }
     }
   }
   __syncthreads();
@@ -169,7 +224,7 @@ __device__ int accept_sequence(const VerifyArgs& a, int b, bool write, SampleRow
       pd = exp((xd - (double)md) / a.T) / zd;
       const double ratio = pd > 0.0 ? pt / pd : __builtin_inf();
       const double thr = ratio < 1.0 ? ratio : 1.0;
-      acc = (double)a.uniforms[((size_t)b * (K + 1) + i) * 2] < thr;
+      acc = (double)u < thr;
     } else {
       atomicOr(&sh_bad, 1);
     }
@@ -190,14 +245,15 @@ __device__ int accept_sequence(const VerifyArgs& a, int b, bool write, SampleRow
   if (n >= 0 && n < K) *info = SampleRowInfo{sh_m[n], sh_m[K + n], sh_z[n], sh_z[K + n]};
   else *info = SampleRowInfo{0.0f, 0.0f, 1.0, 1.0};
   if (write) {
-    if ((int)threadIdx.x < K) {
-      const int i = threadIdx.x;
+    const int i = threadIdx.x;
+    if (i < K) {
       if (a.p_t_out) a.p_t_out[(size_t)b * K + i] = n < 0 ? __builtin_nanf("") : (float)pt;
       if (a.p_d_out) a.p_d_out[(size_t)b * K + i] = n < 0 ? __builtin_nanf("") : (float)pd;
     }
-    for (int i = threadIdx.x; i <= K; i += kBlock)
-      a.out_tokens[(size_t)b * (K + 1) + i] = (n >= 0 && i < n) ? a.tokens[(size_t)b * K + i] : -1;
-    if (threadIdx.x == 0) {
+    // Thread i holds draft token i; position n and the padding get -1 here,
+    // pick_kernel overwrites position n with the sampled token.
+    if (i <= K) a.out_tokens[(size_t)b * (K + 1) + i] = (n >= 0 && i < n) ? d : -1;
+    if (i == 0) {
       a.accepted_len[b] = n;
       a.rows[b] = SampleRowInfo{info->m_t, info->m_d, info->za_t, info->za_d, n};
     }
@@ -219,7 +275,7 @@ __device__ __forceinline__ float tile_rho(float mt, float md, const SampleRowInf
   return (float)r;
 }
 
-// Accurate 2^((x - tile max) * s) for a whole tile slice; 0 when the tile is all -inf.
+// Accurate 2^((x - m) * s) for a whole tile slice; 0 when m is -inf (the tile is all -inf).
 template <int N>
 __device__ __forceinline__ void tile_exp(const float (&x)[N], float m, const VerifyArgs& a, float (&e)[N]) {
   if (m == kNegInf) {
@@ -231,102 +287,214 @@ __device__ __forceinline__ void tile_exp(const float (&x)[N], float m, const Ver
   }
 }
 
+// Value of v in lane l (l the same in every lane of the wave).
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), __builtin_amdgcn_readfirstlane(l)));
+}
+
 // ---------------------------------------------------------------------------
 // Sampling pass: accept decisions, then the tile sums of the sampled row(s).
+//
+// At a rejection the exponent reference of each sampling tile is the
+// statistics pass's maximum of the (twice as long) statistics tile holding it,
+// for both rows: no reduction is needed before the exponentials, and the
+// positive-set ratio is one value per statistics tile.  The bonus row is not
+// read by the statistics pass, so its tiles use their own maxima.
 // ---------------------------------------------------------------------------
 
-// Block `blk` of the sampling pass over the sequences starting at b0.
+template <typename T>
+constexpr int kSubTiles = kTile<T> / kTileS<T>;  // sampling tiles per statistics tile
+
+// Residual tile sums of tile t from packed slices cx (target) and cy (draft)
+// with references (mt, md) and positive-set ratio rho.
+template <typename T, int NL>
+__device__ __forceinline__ void residual_tile(const VerifyArgs& a, int b, int t, float mt, float md, float rho,
+                                              const u32x4 (&cx)[NL], const u32x4 (&cy)[NL]) {
+  constexpr int P = NL * Elem<T>::kVec;
+  const int lane = threadIdx.x & (kWave - 1);
+  double zt = 0.0, zd = 0.0, gs = 0.0, hs = 0.0;
+  // A reference of -inf means the whole statistics tile is -inf: x - m is NaN
+  // there, the clamp in exp2_accurate turns it into 2^-200, and v_exp_f32
+  // returns 0.
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const float e = exp2_accurate(raw_elem<T>(cx, i), mt, a.s_hi, a.s_lo, a.dmin);
+    const float f = exp2_accurate(raw_elem<T>(cy, i), md, a.s_hi, a.s_lo, a.dmin);
+    const double et = (double)e, ed = (double)f;
+    const double in = e * rho > f ? 1.0 : 0.0;
+    zt += et;
+    zd += ed;
+    gs = __builtin_fma(et, in, gs);
+    hs = __builtin_fma(ed, in, hs);
+  }
+  zt = wave_sum(zt);
+  zd = wave_sum(zd);
+  gs = wave_sum(gs);
+  hs = wave_sum(hs);
+  if (lane == 0) a.part_b[(size_t)b * a.NTs + t] = SampleTile{(double)mt, (double)md, zt, zd, gs, hs};
+}
+
+// Bonus-row tile sums of tile t (target row K), referenced to the tile's own maximum.
+template <typename T, int NL>
+__device__ __forceinline__ void bonus_tile(const VerifyArgs& a, int b, int t, const u32x4 (&cx)[NL]) {
+  constexpr int P = NL * Elem<T>::kVec;
+  const int lane = threadIdx.x & (kWave - 1);
+  const float mt = wave_max(raw_lane_max<T>(cx));
+  double zt = 0.0;
+  if (mt != kNegInf) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) zt += (double)exp2_accurate(raw_elem<T>(cx, i), mt, a.s_hi, a.s_lo, a.dmin);
+  }
+  zt = wave_sum(zt);
+  if (lane == 0) a.part_b[(size_t)b * a.NTs + t] = SampleTile{(double)mt, (double)kNegInf, zt, 0.0, 0.0, 0.0};
+}
+
+// Block `blk` of the sampling pass.
 template <typename T, bool kAligned>
-__device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk, int b0) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+__device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int K = a.K;
   const int g = blk % a.NGs;
-  const int b = b0 + blk / a.NGs;
+  const int b = blk / a.NGs;
   SampleRowInfo sr;
   const int n = accept_sequence<T>(a, b, g == 0, &sr);
   if (n < 0) return;  // faulty sequence: outputs already written
   const bool resid = n < K;
   const T* trow = row_ptr<T>(a.target, (size_t)b * (K + 1) + n, a.V);
-  const T* drow = resid ? row_ptr<T>(a.draft, (size_t)b * K + n, a.V) : nullptr;
-  constexpr int P = kPerLaneS<T>;
-  // The block covers kTilesPerBlockS consecutive tiles, interleaved over its
-  // waves so that the four waves read neighbouring tiles at the same time.
-  for (int j = 0; j < kTilesPerWaveS; ++j) {
-    const int t = g * kTilesPerBlockS + j * kWavesPerBlock + wave;
-    if (t >= a.NTs) break;
-    float x[P], e[P];
-    load_tile<T, kAligned, kLoadsS>(trow, a.V, t, lane, x);
-    const float mt = wave_max(lane_max(x));
-    double zt = 0.0, zd = 0.0, gs = 0.0, hs = 0.0;
-    float md = kNegInf;
-    if (!resid) {
-      tile_exp(x, mt, a, e);
-#pragma unroll
-      for (int i = 0; i < P; ++i) zt += (double)e[i];
-    } else {
-      float y[P], f[P];
-      load_tile<T, kAligned, kLoadsS>(drow, a.V, t, lane, y);
-      md = wave_max(lane_max(y));
-      tile_exp(x, mt, a, e);
-      tile_exp(y, md, a, f);
-      const float rho = tile_rho(mt, md, sr, a.s64);
-#pragma unroll
-      for (int i = 0; i < P; ++i) {
-        const double et = (double)e[i], ed = (double)f[i];
-        const double in = e[i] * rho > f[i] ? 1.0 : 0.0;
-        zt += et;
-        zd += ed;
-        gs = __builtin_fma(et, in, gs);
-        hs = __builtin_fma(ed, in, hs);
-      }
-    }
-    zt = wave_sum(zt);
-    zd = wave_sum(zd);
-    gs = wave_sum(gs);
-    hs = wave_sum(hs);
-    if (lane == 0) a.part_b[(size_t)b * a.NTs + t] = SampleTile{(double)mt, (double)md, zt, zd, gs, hs};
+  const T* drow = resid ? row_ptr<T>(a.draft, (size_t)b * K + n, a.V) : trow;
+  constexpr int NL = kLoadsS;
+  // The block covers TPWs * 4 consecutive tiles, interleaved over its waves
+  // so that the four waves read neighbouring tiles at the same time.  A tile
+  // stays packed in registers (about 70 VGPRs, seven waves per SIMD); the other waves
+  // on the SIMD cover a tile's load latency.  Loading the next tile ahead
+  // measured slower: the extra registers cost two waves of occupancy.
+  auto tile_of = [&](int j) { return (g * a.TPWs + j) * kWavesPerBlock + wave; };
+  if (tile_of(0) >= a.NTs) return;
+  // Residual: lane l holds the references and the ratio of statistics tile T0 + l.
+  const int T0 = g * a.TPWs * kWavesPerBlock / kSubTiles<T>;
+  float ref_t = kNegInf, ref_d = kNegInf, rho_l = 0.0f;
+  if (resid && lane < a.TPWs * kWavesPerBlock / kSubTiles<T> && T0 + lane < a.NT) {
+    const size_t R = 2 * (size_t)K;
+    ref_t = a.part_a[((size_t)b * R + n) * a.NT + T0 + lane].m;
+    ref_d = a.part_a[((size_t)b * R + K + n) * a.NT + T0 + lane].m;
+    rho_l = tile_rho(ref_t, ref_d, sr, a.s64);
   }
+  for (int j = 0; j < a.TPWs; ++j) {
+    const int t = tile_of(j);
+    if (t >= a.NTs) break;
+    u32x4 cx[NL], cy[NL];
+    load_raw<T, kAligned, kLoadsS>(trow, a.V, t, lane, cx);
+    if (resid) {
+      load_raw<T, kAligned, kLoadsS>(drow, a.V, t, lane, cy);
+      const int lt = t / kSubTiles<T> - T0;
+      residual_tile<T>(a, b, t, lane_value(ref_t, lt), lane_value(ref_d, lt), lane_value(rho_l, lt), cx, cy);
+    } else {
+      bonus_tile<T>(a, b, t, cx);
+    }
+  }
+}
+
+// Two block-wide sums in one round of LDS traffic.
+__device__ __forceinline__ void block_sum2(double& x, double& y, double* sh) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  x = wave_sum(x);
+  y = wave_sum(y);
+  if (lane == 0) {
+    sh[w] = x;
+    sh[kWavesPerBlock + w] = y;
+  }
+  __syncthreads();
+  x = 0.0;
+  y = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWavesPerBlock; ++i) {
+    x += sh[i];
+    y += sh[kWavesPerBlock + i];
+  }
+  __syncthreads();
+}
+
+// Block-wide maximum of two floats, and minimum of two ints, in one round each.
+__device__ __forceinline__ void block_max2(float& x, float& y, float* sh) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  x = wave_max(x);
+  y = wave_max(y);
+  if (lane == 0) {
+    sh[w] = x;
+    sh[kWavesPerBlock + w] = y;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kWavesPerBlock; ++i) {
+    x = fmaxf(x, sh[i]);
+    y = fmaxf(y, sh[kWavesPerBlock + i]);
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void block_min2(int& x, int& y, int* sh) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  x = wave_min(x);
+  y = wave_min(y);
+  if (lane == 0) {
+    sh[w] = x;
+    sh[kWavesPerBlock + w] = y;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kWavesPerBlock; ++i) {
+    x = min(x, sh[i]);
+    y = min(y, sh[kWavesPerBlock + i]);
+  }
+  __syncthreads();
 }
 
 // One block per sequence, after sample_kernel: the inverse-CDF choice of tile
 // from the tile masses, then a four-wave scan of that tile in token-id order.
-// Token pick of sequence b.
+// The tile sums of the sequence (one per thread for up to 256 tiles) and the
+// sample uniforms are loaded together with the row record, so the block waits
+// for one memory round trip before the tile choice and one for the tile.
 template <typename T, bool kAligned>
 __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
-  __shared__ double sh_d[kWavesPerBlock];
-  __shared__ float sh_f[kWavesPerBlock];
-  __shared__ int sh_i[kWavesPerBlock];
+  __shared__ double sh_d[2 * kWavesPerBlock];
+  __shared__ float sh_f[2 * kWavesPerBlock];
+  __shared__ int sh_i[2 * kWavesPerBlock];
   __shared__ double sh_scan[kWavesPerBlock];
   __shared__ double sh_cbefore;
-  const SampleRowInfo sr = a.rows[b];
-  const int K = a.K, NT = a.NTs, n = K == 0 ? 0 : sr.n;
-  if (n < 0) return;
-  const bool resid = n < K;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const T* trow = row_ptr<T>(a.target, (size_t)b * (K + 1) + n, a.V);
-  const T* drow = resid ? row_ptr<T>(a.draft, (size_t)b * K + n, a.V) : nullptr;
-  const SampleTile* P = a.part_b + (size_t)b * NT;
+  __shared__ float sh_u[kMaxK + 1];
   constexpr double kNegInfD = -__builtin_inf();
+  const int K = a.K, NT = a.NTs;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const SampleTile* P = a.part_b + (size_t)b * NT;
+  const bool cached = NT <= kBlock;
+  SampleTile q0{kNegInfD, kNegInfD, 0.0, 0.0, 0.0, 0.0};
+  if (cached && (int)threadIdx.x < NT) q0 = P[threadIdx.x];
+  if ((int)threadIdx.x <= K) sh_u[threadIdx.x] = a.uniforms[((size_t)b * (K + 1) + threadIdx.x) * 2 + 1];
+  const SampleRowInfo sr = a.rows[b];
+  const int n = K == 0 ? 0 : sr.n;
+  if (n < 0) return;  // uniform over the block: every thread read the same record
+  const bool resid = n < K;
+  auto tile_at = [&](int tt) -> SampleTile { return cached ? q0 : P[tt]; };
 
   // Reference maxima: statistics-pass maxima for a residual pair, the maximum
   // over tiles for the bonus row (the statistics pass does not read row K).
   float mref_t = sr.m_t;
   if (!resid) {
-    float mm = kNegInf;
-    for (int tt = threadIdx.x; tt < NT; tt += kBlock) mm = fmaxf(mm, (float)P[tt].mt);
-    mref_t = block_max(mm, sh_f);
+    float mm = kNegInf, unused = kNegInf;
+    for (int tt = threadIdx.x; tt < NT; tt += kBlock) mm = fmaxf(mm, (float)tile_at(tt).mt);
+    block_max2(mm, unused, sh_f);
+    mref_t = mm;
   }
   // Normalisers of the sampled rows from the accurate per-element values.
   double zbt = 0.0, zbd = 0.0;
   if (isfinite(mref_t)) {
     for (int tt = threadIdx.x; tt < NT; tt += kBlock) {
-      const SampleTile q = P[tt];
+      const SampleTile q = tile_at(tt);
       if (q.mt != kNegInfD) zbt += q.zt * exp2((q.mt - (double)mref_t) * a.s64);
       if (resid && q.md != kNegInfD) zbd += q.zd * exp2((q.md - (double)sr.m_d) * a.s64);
     }
   }
-  zbt = block_sum(zbt, sh_d);
-  if (resid) zbd = block_sum(zbd, sh_d);
+  block_sum2(zbt, zbd, sh_d);
   if (!isfinite(mref_t) || !(zbt > 0.0) || !isfinite(zbt) || (resid && (!(zbd > 0.0) || !isfinite(zbd)))) {
     // A sampled row without a finite maximum: the sequence is faulty.
     for (int i = threadIdx.x; i <= K; i += kBlock) a.out_tokens[(size_t)b * (K + 1) + i] = -1;
@@ -337,31 +505,29 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
   // Tile scale factors: P_t(v) = e_t(v) * gt, P_d(v) = e_d(v) * gd.
   auto scale_t = [&](double mt) { return mt == kNegInfD ? 0.0 : exp2((mt - (double)mref_t) * a.s64) / zbt; };
   auto scale_d = [&](double md) { return md == kNegInfD ? 0.0 : exp2((md - (double)sr.m_d) * a.s64) / zbd; };
-  auto tile_mass = [&](int tt, bool fallback) -> double {
-    const SampleTile q = P[tt];
+  auto tile_mass = [&](const SampleTile& q, bool fallback) -> double {
     if (!resid || fallback) return q.zt * scale_t(q.mt);
     return q.g * scale_t(q.mt) - q.h * scale_d(q.md);
   };
 
-  double S = 0.0;
-  for (int tt = threadIdx.x; tt < NT; tt += kBlock) S += tile_mass(tt, false);
-  S = block_sum(S, sh_d);
-  bool fallback = false;
-  if (resid && !(S > 0.0)) {
-    // Rejection with no residual mass left by rounding: sample P_t instead.
-    fallback = true;
-    S = 0.0;
-    for (int tt = threadIdx.x; tt < NT; tt += kBlock) S += tile_mass(tt, true);
-    S = block_sum(S, sh_d);
+  double S = 0.0, S_fb = 0.0;
+  for (int tt = threadIdx.x; tt < NT; tt += kBlock) {
+    const SampleTile q = tile_at(tt);
+    S += tile_mass(q, false);
+    if (resid) S_fb += tile_mass(q, true);
   }
-  const double target = (double)a.uniforms[((size_t)b * (K + 1) + n) * 2 + 1] * S;
+  block_sum2(S, S_fb, sh_d);
+  // Rejection with no residual mass left by rounding: sample P_t instead.
+  const bool fallback = resid && !(S > 0.0);
+  if (fallback) S = S_fb;
+  const double target = (double)sh_u[n] * S;
 
   // Tile holding the inverse-CDF point: block scan over tiles in id order.
-  int jstar = -1;
+  int jstar = -1, last_mass = -1;
   double cbefore = 0.0, offset = 0.0;
   for (int c0 = 0; c0 < NT; c0 += kBlock) {
     const int tt = c0 + threadIdx.x;
-    const double ms = tt < NT ? tile_mass(tt, fallback) : 0.0;
+    const double ms = tt < NT ? tile_mass(tile_at(tt), fallback) : 0.0;
     double incl = wave_inclusive_scan(ms, lane);
     if (lane == kWave - 1) sh_scan[wave] = incl;
     __syncthreads();
@@ -371,10 +537,14 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
       if (w < wave) before_wave += sh_scan[w];
       total += sh_scan[w];
     }
-    __syncthreads();
     incl += before_wave;
     const bool cross = tt < NT && offset + incl > target;
-    const int first = block_min(cross ? tt : 0x7fffffff, sh_i);
+    // First crossing tile of this chunk, and its last tile with mass (for
+    // the case that rounding leaves the point beyond every boundary).
+    int first = cross ? tt : 0x7fffffff;
+    int neg_last = (tt < NT && ms > 0.0) ? -tt : 1;
+    block_min2(first, neg_last, sh_i);  // its barriers also retire sh_scan
+    if (neg_last <= 0) last_mass = -neg_last;
     if (first != 0x7fffffff) {
       if (tt == first) sh_cbefore = offset + incl - ms;
       __syncthreads();
@@ -384,16 +554,10 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
     }
     offset += total;
   }
-  bool no_cross = false;
-  if (jstar < 0) {
-    // Rounding left the point beyond the last boundary: take the last tile
-    // with mass, and in it the last element with positive weight.
-    int last = -1;
-    for (int tt = threadIdx.x; tt < NT; tt += kBlock)
-      if (tile_mass(tt, fallback) > 0.0) last = tt;
-    jstar = -block_min(-last, sh_i);
-    no_cross = true;
-  }
+  // No crossing: take the last tile with mass, and in it the last element
+  // with positive weight.
+  const bool no_cross = jstar < 0;
+  if (no_cross) jstar = last_mass;
   if (jstar < 0) {
     for (int i = threadIdx.x; i <= K; i += kBlock) a.out_tokens[(size_t)b * (K + 1) + i] = -1;
     if (threadIdx.x == 0) a.accepted_len[b] = -1;
@@ -403,16 +567,27 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
   // Scan of tile jstar: wave w owns the tile's load w (kWave*kVec consecutive
   // ids).  The tile maxima and every element value are recomputed exactly as
   // the tile pass computed them.
+  const T* trow = row_ptr<T>(a.target, (size_t)b * (K + 1) + n, a.V);
+  const T* drow = resid ? row_ptr<T>(a.draft, (size_t)b * K + n, a.V) : nullptr;
   constexpr int V8 = Elem<T>::kVec;
   static_assert(kLoadsS == kWavesPerBlock, "one load of the tile per wave");
   const bool use_d = resid && !fallback;
   float x[V8], y[V8], e[V8], f[V8];
   load_tile<T, kAligned, kLoadsS>(trow, a.V, jstar, lane, x, wave);
-  const float mt = block_max(lane_max(x), sh_f);
-  float md = kNegInf;
-  if (use_d) {
-    load_tile<T, kAligned, kLoadsS>(drow, a.V, jstar, lane, y, wave);
-    md = block_max(lane_max(y), sh_f);
+  if (use_d) load_tile<T, kAligned, kLoadsS>(drow, a.V, jstar, lane, y, wave);
+  // Exponent references exactly as the sampling pass took them: the
+  // statistics tile maxima for a rejected position, the tile's own maximum
+  // for the bonus row.
+  float mt, md = kNegInf;
+  if (resid) {
+    const size_t R = 2 * (size_t)K;
+    const int ts = jstar / kSubTiles<T>;
+    mt = a.part_a[((size_t)b * R + n) * a.NT + ts].m;
+    md = a.part_a[((size_t)b * R + K + n) * a.NT + ts].m;
+  } else {
+    mt = lane_max(x);
+    float unused = kNegInf;
+    block_max2(mt, unused, sh_f);
   }
   const double gt = scale_t((double)mt);
   const double gd = use_d ? scale_d((double)md) : 0.0;
@@ -451,8 +626,9 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
     for (int k = V8 - 1; k >= 0; --k)
       if (base + cum[k] > target) mine = id0 + k;
   }
-  int token = block_min(mine, sh_i);
-  if (token == 0x7fffffff) token = -block_min(-last_pos, sh_i);
+  int neg_last_pos = -last_pos;
+  block_min2(mine, neg_last_pos, sh_i);
+  const int token = mine != 0x7fffffff ? mine : -neg_last_pos;
   if (threadIdx.x == 0) {
     a.out_tokens[(size_t)b * (K + 1) + n] = token;
     a.accepted_len[b] = token >= 0 ? n : -1;
@@ -463,12 +639,12 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
 
 template <typename T, bool kAligned>
 __global__ void __launch_bounds__(kBlock) stats_kernel(VerifyArgs a) {
-  stats_block<T, kAligned>(a, blockIdx.x, 0);
+  stats_block<T, kAligned>(a, blockIdx.x);
 }
 
 template <typename T, bool kAligned>
 __global__ void __launch_bounds__(kBlock) sample_kernel(VerifyArgs a) {
-  sample_block<T, kAligned>(a, blockIdx.x, 0);
+  sample_block<T, kAligned>(a, blockIdx.x);
 }
 
 template <typename T, bool kAligned>
@@ -600,7 +776,18 @@ VerifyShape make_shape(int B, int K, int V, int dtype, bool aligned) {
   s.NG = (s.NT + kWavesPerBlock - 1) / kWavesPerBlock;
   const int tile_s = dtype == 1 ? kTileS<uint16_t> : kTileS<float>;
   s.NT_s = (V + tile_s - 1) / tile_s;
-  s.NG_s = (s.NT_s + kTilesPerBlockS - 1) / kTilesPerBlockS;
+  s.TPW_s = 1;
+  for (int tpw = kMaxTilesPerWaveS; tpw > 1; tpw /= 2) {
+    const long long blocks = (long long)B * ((s.NT_s + tpw * kWavesPerBlock - 1) / (tpw * kWavesPerBlock));
+    if (blocks >= kSampleBlocksWanted) {
+      s.TPW_s = tpw;
+      break;
+    }
+  }
+#ifdef SV_SAMPLE_TPW
+  s.TPW_s = SV_SAMPLE_TPW;
+#endif
+  s.NG_s = (s.NT_s + s.TPW_s * kWavesPerBlock - 1) / (s.TPW_s * kWavesPerBlock);
   return s;
 }
 
@@ -650,6 +837,7 @@ static VerifyArgs verify_args(const VerifyShape& s, const VerifyIO& io, const Ve
   a.NG = s.NG;
   a.NTs = s.NT_s;
   a.NGs = s.NG_s;
+  a.TPWs = s.TPW_s;
   a.s64 = log2e_over(io.temperature);
   a.s_hi = (float)a.s64;
   a.s_lo = (float)(a.s64 - (double)a.s_hi);

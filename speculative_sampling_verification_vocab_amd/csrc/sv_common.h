@@ -54,14 +54,21 @@ __device__ __forceinline__ void load_tile(const T* __restrict__ row, int V, int 
   const int base = t * (kWave * L * V8) + first * (kWave * V8) + lane * V8;
   if constexpr (kAligned) {
     u32x4 raw[kL];
+    // A slice wholly inside the row (every slice but the last of a row whose
+    // length is not a tile multiple) loads without per-vector range checks.
+    if (t * (kWave * L * V8) + (first + kL) * (kWave * V8) <= V) {
 #pragma unroll
-    for (int j = 0; j < kL; ++j) {
-      const int off = base + j * (kWave * V8);
-      if (off < V) {
-        raw[j] = *reinterpret_cast<const u32x4*>(row + off);
-      } else {
-        const uint32_t ninf = sizeof(T) == 2 ? 0xff80ff80u : 0xff800000u;
-        raw[j] = u32x4{ninf, ninf, ninf, ninf};
+      for (int j = 0; j < kL; ++j) raw[j] = *reinterpret_cast<const u32x4*>(row + base + j * (kWave * V8));
+    } else {
+#pragma unroll
+      for (int j = 0; j < kL; ++j) {
+        const int off = base + j * (kWave * V8);
+        if (off < V) {
+          raw[j] = *reinterpret_cast<const u32x4*>(row + off);
+        } else {
+          const uint32_t ninf = sizeof(T) == 2 ? 0xff80ff80u : 0xff800000u;
+          raw[j] = u32x4{ninf, ninf, ninf, ninf};
+        }
       }
     }
 #pragma unroll
@@ -101,10 +108,15 @@ __device__ __forceinline__ void load_raw(const T* __restrict__ row, int V, int t
   const int base = t * (kWave * L * V8) + lane * V8;
   constexpr uint32_t kNinf = sizeof(T) == 2 ? 0xff80ff80u : 0xff800000u;
   if constexpr (kAligned) {
+    if (t * (kWave * L * V8) + NL * (kWave * V8) <= V) {
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int off = base + j * (kWave * V8);
-      raw[j] = off < V ? *reinterpret_cast<const u32x4*>(row + off) : u32x4{kNinf, kNinf, kNinf, kNinf};
+      for (int j = 0; j < NL; ++j) raw[j] = *reinterpret_cast<const u32x4*>(row + base + j * (kWave * V8));
+    } else {
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        const int off = base + j * (kWave * V8);
+        raw[j] = off < V ? *reinterpret_cast<const u32x4*>(row + off) : u32x4{kNinf, kNinf, kNinf, kNinf};
+      }
     }
   } else {
 #pragma unroll
@@ -152,34 +164,70 @@ __device__ __forceinline__ float lane_max(const float (&x)[N]) {
   return m;
 }
 
+// Wave-wide reductions with DPP lane moves (gfx9 encodings): two quad
+// permutes, the half-row and row mirrors, then row_bcast15 / row_bcast31
+// carry row results into rows 1 and 3, 2 and 3.  Lane 63 ends with the
+// result, which readlane returns to every lane.  No LDS traffic, one VALU
+// operation per step.
+namespace dpp {
+constexpr int kQuadSwap1 = 0xb1;  // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4e;  // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;
+constexpr int kMirror = 0x140;
+constexpr int kBcast15 = 0x142;
+constexpr int kBcast31 = 0x143;
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int mov(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, kCtrl, kRowMask, 0xf, false);
+}
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float mov(float old, float v) {
+  return __int_as_float(mov<kCtrl, kRowMask>(__float_as_int(old), __float_as_int(v)));
+}
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ double mov(double old, double v) {
+  const int lo = mov<kCtrl, kRowMask>((int)__double2loint(old), (int)__double2loint(v));
+  const int hi = mov<kCtrl, kRowMask>((int)__double2hiint(old), (int)__double2hiint(v));
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(v, 63); }
+__device__ __forceinline__ float lane63(float v) { return __int_as_float(lane63(__float_as_int(v))); }
+__device__ __forceinline__ double lane63(double v) {
+  return __hiloint2double(lane63((int)__double2hiint(v)), lane63((int)__double2loint(v)));
+}
+
+// Reduce with op; `id` is op's identity (what disabled lanes contribute).
+template <typename V, typename Op>
+__device__ __forceinline__ V reduce(V v, V id, Op op) {
+  v = op(v, mov<kQuadSwap1, 0xf>(id, v));
+  v = op(v, mov<kQuadSwap2, 0xf>(id, v));
+  v = op(v, mov<kHalfMirror, 0xf>(id, v));
+  v = op(v, mov<kMirror, 0xf>(id, v));
+  v = op(v, mov<kBcast15, 0xa>(id, v));
+  v = op(v, mov<kBcast31, 0xc>(id, v));
+  return lane63(v);
+}
+}  // namespace dpp
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return dpp::reduce(v, -__builtin_inff(), [](float x, float y) { return fmaxf(x, y); });
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return dpp::reduce(v, 0.0f, [](float x, float y) { return x + y; });
 }
 
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return dpp::reduce(v, 0.0, [](double x, double y) { return x + y; });
 }
 
 __device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-  return v;
+  return dpp::reduce(v, 0x7fffffff, [](int x, int y) { return min(x, y); });
 }
 
 __device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-  return v;
+  return dpp::reduce(v, (int)0x80000000, [](int x, int y) { return max(x, y); });
 }
 
 // Inclusive prefix sum over the 64 lanes in lane order.

@@ -8,15 +8,19 @@ SAMPLE mode.  One step = one spec_verify call over the whole batch with its
 inputs already resident in HBM.
 
 Prints ONE JSON line on stdout:
-  value      verified draft positions per second, B*(K+1) / step time
+  value      verified draft positions per second, B*(K+1) / step time, the
+             step time taken over `--steps` uninstrumented calls
   roofline   the row-statistics kernel (the dominant one): algorithmic bytes
              per launch (every logit of target and draft rows 0..K-1 read
-             once) / its average duration from HIP events on the launch
-             stream, against MI355X's 8 TB/s HBM peak; `traffic` is HBM
-             bytes per launch from the rocprofv3 PMC summary in profiles/
-             when that summary matches the current kernel source, else null.
+             once) / its average duration from HIP events recorded on the
+             launch stream around every launch in a second pass over the same
+             steps, against MI355X's 8 TB/s HBM peak; `traffic` is HBM bytes
+             per launch from the rocprofv3 PMC summary in profiles/ when that
+             summary matches the current kernel source, else null.
   cpu_baseline  the fp64 oracle timed on this host's cores on a sample of the
              same batch (it is a baseline, not a target).
+  early_exit the position-by-position schedule on the same batch (identical
+             outputs; rows after each sequence's first rejection not read).
 """
 from __future__ import annotations
 
@@ -102,7 +106,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="b256_k7_v262144_bf16")
-    ap.add_argument("--mode", default="sample", choices=["sample", "greedy"])
+    ap.add_argument("--mode", default="sample", choices=["sample", "greedy", "sample_early_exit"])
+    ap.add_argument("--no-early-exit", action="store_true",
+                    help="skip the extra timing of the early-exit schedule in sample mode")
     ap.add_argument("--cpu-sample", type=int, default=256, help="sequences timed on the CPU oracle")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="thread-seconds of oracle work to time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -142,42 +148,76 @@ def main():
 
     ws = sv.Workspace(dev)
     stream = torch.cuda.current_stream(dev)
-    L = sv.spec_verify_launch_count(B, K, V, case.target.dtype, args.mode)
-    NE = L + 1
 
-    def mk_events(n):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(NE * n)]
+    def timed(mode, steps, warmup):
+        """Two passes of `steps` verify calls after `warmup` untimed ones.
+        Pass 1 (no instrumentation): mean wall ms per step between two device
+        synchronisations.  Pass 2: the same calls with a HIP event recorded on
+        the launch stream before every kernel launch and after the last, for
+        per-kernel durations (an event record between dependent launches adds
+        ~3 us, so pass 2 is not used for the step time)."""
+        L = sv.spec_verify_launch_count(B, K, V, case.target.dtype, mode)
+        NE = L + 1
+        sampling = mode != "greedy"
+        draft = case.draft if sampling else None
+        uni = case.uniforms if sampling else None
+
+        def step(evs=None):
+            return sv.spec_verify(case.target, draft, case.draft_tokens, uni, case.temperature, mode,
+                                  workspace=ws, events=evs)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        start = time.perf_counter()
+        for _ in range(steps):
+            res = step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - start) * 1e3 / steps
+
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(NE * steps)]
         for e in evs:
             e.record(stream)  # creates the underlying hipEvent
-        return evs
+        torch.cuda.synchronize()
+        for s in range(steps):
+            step(evs[NE * s:NE * s + NE])
+        torch.cuda.synchronize()
 
-    draft = case.draft if args.mode == "sample" else None
-    uni = case.uniforms if args.mode == "sample" else None
+        def span(i, j):
+            return float(np.mean([evs[NE * s + i].elapsed_time(evs[NE * s + j]) for s in range(steps)]))
 
-    def step(evs=None):
-        return sv.spec_verify(case.target, draft, case.draft_tokens, uni, case.temperature, args.mode,
-                              workspace=ws, events=evs)
+        launch_ms = [span(k, k + 1) for k in range(L)]
+        return ms, launch_ms, span(0, L), res
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    evs = mk_events(args.steps)
-    torch.cuda.synchronize()
-    start = time.perf_counter()
-    for s in range(args.steps):
-        res = step(evs[NE * s:NE * s + NE])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - start
-    ms_step = wall * 1e3 / args.steps
-
-    def span(i, j):
-        return float(np.mean([evs[NE * s + i].elapsed_time(evs[NE * s + j]) for s in range(args.steps)]))
-
-    launch_ms = [span(k, k + 1) for k in range(L)]
-    k_ms = {"launches": launch_ms, "events_step": span(0, L)}
+    ms_step, launch_ms, ev_step, res = timed(args.mode, args.steps, args.warmup)
+    k_ms = {"launches": launch_ms, "events_step": ev_step}
     acc = res[0].float()
     mean_tokens = float((acc[acc >= 0] + 1).mean()) if (acc >= 0).any() else float("nan")
+
+    early = None
+    if args.mode == "sample" and not args.no_early_exit:
+        # The early-exit schedule on the same batch: identical outputs, rows after
+        # each sequence's first rejection are not read.
+        ee_ms, ee_launch, ee_ev, ee_res = timed("sample_early_exit", args.steps, args.warmup)
+        same = bool(torch.equal(ee_res[0], res[0]) and torch.equal(ee_res[1], res[1]))
+        n = res[0].cpu().numpy()
+        rows = np.where(n >= 0, np.minimum(n, K - 1) + 1, 0) if K > 0 else np.zeros(B)
+        need = int(2 * rows.sum()) * V * esz            # target and draft rows 0..min(n, K-1)
+        stats_ms = float(sum(ee_launch[0:2 * K:2]))       # the per-position statistics launches
+        decide_ms = float(sum(ee_launch[1:2 * K:2]))
+        early = {
+            "mode": "sample_early_exit",
+            "value": B * (K + 1) / (ee_ms * 1e-3),
+            "unit": "positions/s",
+            "ms_per_step": ee_ms,
+            "outputs_identical_to_full_schedule": same,
+            "rows_read_fraction": float(rows.sum()) / max(1, B * K),
+            "statistics_bytes_needed": need,
+            "statistics_ms": stats_ms,
+            "decision_ms": decide_ms,
+            "statistics_gbs": need / (stats_ms * 1e-3) / 1e9 if stats_ms > 0 else None,
+            "kernels_ms": {"launches": ee_launch, "events_step": ee_ev},
+        }
 
     positions = B * (K + 1)
     value = positions / (ms_step * 1e-3)
@@ -185,6 +225,15 @@ def main():
         step_bytes = B * (2 * K + 1) * V * esz          # every logit read once
         dom_bytes = B * 2 * K * V * esz                 # launch 0: rows 0..K-1 of target and draft
         dom_name, dom_ms = "stats_kernel (per-tile max and exp sums of the proposal rows)", launch_ms[0]
+    elif args.mode == "sample_early_exit":
+        # bytes the rule needs: target and draft rows up to the first rejection,
+        # plus the bonus row where every draft was accepted
+        n = res[0].cpu().numpy()
+        rows = np.where(n >= 0, np.minimum(n, K - 1) + 1, 0) if K > 0 else np.zeros(B, dtype=np.int64)
+        dom_bytes = int(2 * rows.sum()) * V * esz
+        step_bytes = dom_bytes + int((n == K).sum()) * V * esz
+        dom_name = "ee_stats_kernel, all positions (statistics of the rows up to each first rejection)"
+        dom_ms = float(sum(launch_ms[0:2 * K:2])) if K > 0 else launch_ms[0]
     else:
         step_bytes = B * (K + 1) * V * esz
         dom_bytes = step_bytes
@@ -220,6 +269,8 @@ def main():
                      "algorithmic_bytes_per_launch": dom_bytes},
         "cpu_baseline": cpu,
     }
+    if early is not None:
+        out["early_exit"] = early
     print(json.dumps(out), flush=True)
 
 
@@ -260,15 +311,19 @@ def bench_shortlist(args, dev):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        res = step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # second pass with an event around every launch, for per-kernel durations
     evs = [torch.cuda.Event(enable_timing=True) for _ in range((NE + 2) * args.steps)]
     for e in evs:
         e.record(stream)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for s in range(args.steps):
-        res = step(evs[(NE + 2) * s:(NE + 2) * (s + 1)])
+        step(evs[(NE + 2) * s:(NE + 2) * (s + 1)])
     torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
     def span(i, j):
         return float(np.mean([evs[(NE + 2) * s + i].elapsed_time(evs[(NE + 2) * s + j]) for s in range(args.steps)]))

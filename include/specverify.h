@@ -45,7 +45,20 @@ extern "C" {
 #define SPEC_MAX_K 64
 
 typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
-typedef enum { SPEC_MODE_SAMPLE = 0, SPEC_MODE_GREEDY = 1 } spec_mode_t;
+/*
+ * SAMPLE: the Leviathan/Chen rule (accept with probability min(1, P_t/P_d)
+ *   left to right, resample (P_t - P_d)_+ at the first rejection, bonus token
+ *   from P_t,K when every draft is accepted), reading every row once.
+ * GREEDY: argmax verify on the target logits alone.
+ * SAMPLE_EARLY_EXIT: the same rule and bit-identical accepted_len and
+ *   out_tokens, evaluated position by position so that rows after a
+ *   sequence's first rejection are never read (they cannot change its output:
+ *   Speculative Decoding lesson, nextadmin.net, "Core algorithm" step 5).
+ *   Consequences: p_target/p_draft_at_draft are NaN after the first
+ *   rejection, and a non-finite row after it does not mark the sequence
+ *   faulty (draft tokens are still checked at every position).
+ */
+typedef enum { SPEC_MODE_SAMPLE = 0, SPEC_MODE_GREEDY = 1, SPEC_MODE_SAMPLE_EARLY_EXIT = 2 } spec_mode_t;
 typedef enum {
   SPEC_OK = 0,
   SPEC_ERR_INVALID_ARG = 1, /* NULL pointer, negative size, bad temperature, bad enum, overflow */
@@ -81,7 +94,7 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V, spec_dtype_t
  *                  uniform of position i, uniforms[b,i,1] the sampling uniform
  *                  used if the output token at position i is sampled.
  *                  Unused (may be NULL) in GREEDY mode.
- *   temperature    SAMPLE: finite and > 0; both softmaxes use logits / T.
+ *   temperature    SAMPLE modes: finite and > 0; both softmaxes use logits / T.
  *                  GREEDY: ignored.
  *   accepted_len   [B] int32 out: n in [0, K] accepted drafts, or -1 when the
  *                  sequence is faulty (a draft token outside [0, V), or a row
@@ -90,8 +103,9 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V, spec_dtype_t
  *                  argmax) token at position n, then -1.  All -1 when faulty.
  *   p_target_at_draft, p_draft_at_draft
  *                  optional [B, K] float outs (NULL = skip): P_t,i(d_i) and
- *                  P_d,i(d_i) in SAMPLE mode, NaN in GREEDY mode or where a
- *                  sequence is faulty.
+ *                  P_d,i(d_i) in the SAMPLE modes, NaN in GREEDY mode, where a
+ *                  sequence is faulty, and (SAMPLE_EARLY_EXIT) after the
+ *                  first rejection.
  *   workspace      device buffer of at least spec_verify_workspace_bytes(),
  *                  256-byte aligned.
  *
@@ -110,7 +124,10 @@ spec_status_t spec_verify(const void* target_logits, const void* draft_logits,
 /*
  * Number of kernel launches spec_verify makes for this shape (0 for an empty
  * or invalid shape).  SAMPLE mode: 3 (row statistics; accept decisions and
- * the sampled rows' tile sums; token pick).  GREEDY mode: 2 (per-tile argmax,
+ * the sampled rows' tile sums; token pick).  SAMPLE_EARLY_EXIT: K + 2 (row
+ * statistics of position i for i = 0..K-1, each launch also deciding
+ * position i - 1; then the decision of position K - 1 with the sampled rows'
+ * tile sums, and the token pick).  GREEDY mode: 2 (per-tile argmax,
  * then per-sequence finalize).
  */
 int32_t spec_verify_launch_count(int32_t B, int32_t K, int32_t V, spec_dtype_t dtype, spec_mode_t mode);

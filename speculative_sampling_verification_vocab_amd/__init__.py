@@ -22,7 +22,9 @@ __all__ = ["spec_verify", "spec_verify_workspace_bytes", "spec_verify_launch_cou
            "Workspace", "SpecVerifyError", "abi_version"]
 
 _DTYPES = {torch.bfloat16: _native.SPEC_BF16, torch.float32: _native.SPEC_F32}
-_MODES = {"sample": _native.SPEC_MODE_SAMPLE, "greedy": _native.SPEC_MODE_GREEDY}
+_MODES = {"sample": _native.SPEC_MODE_SAMPLE, "greedy": _native.SPEC_MODE_GREEDY,
+          "sample_early_exit": _native.SPEC_MODE_SAMPLE_EARLY_EXIT}
+_SAMPLING = ("sample", "sample_early_exit")
 
 
 def abi_version() -> int:
@@ -90,6 +92,10 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_token
     out_tokens int32 [B, K+1]) and, with return_probs, also (P_t(d), P_d(d))
     float32 [B, K].  `events`: recorded torch.cuda.Event objects, re-recorded
     before each kernel launch and after the last (see spec_verify_timed).
+
+    mode: "sample" (every row read once), "sample_early_exit" (the same
+    accepted_len and out_tokens, reading only the rows up to each sequence's
+    first rejection; probabilities after it are NaN) or "greedy".
     """
     if mode not in _MODES:
         raise ValueError(f"mode must be one of {list(_MODES)}")
@@ -102,7 +108,8 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_token
     if dt is None:
         raise ValueError("logits must be bfloat16 or float32")
     dev = target.device
-    if mode == "sample" and K > 0:
+    sampling = mode in _SAMPLING
+    if sampling and K > 0:
         if draft is None:
             raise ValueError("draft logits are required in sample mode")
         _need_gpu(draft, "draft")
@@ -114,7 +121,7 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_token
         _need_gpu(draft_tokens, "draft_tokens")
         if draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != (B, K):
             raise ValueError("draft_tokens must be int32 [B, K]")
-    if mode == "sample":
+    if sampling:
         if uniforms is None:
             raise ValueError("uniforms are required in sample mode")
         _need_gpu(uniforms, "uniforms")
@@ -127,9 +134,9 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_token
     pd = torch.empty((B, K), dtype=torch.float32, device=dev) if return_probs else None
     need = lib.spec_verify_workspace_bytes(B, K, V, dt, _MODES[mode])
     ws = (workspace or _workspace_for(dev)).get(need)
-    args = [_ptr(target), _ptr(draft) if mode == "sample" else None,
-            _ptr(draft_tokens) if K > 0 else None, _ptr(uniforms) if mode == "sample" else None,
-            B, K, V, dt, ctypes.c_float(temperature if mode == "sample" else 0.0), _MODES[mode],
+    args = [_ptr(target), _ptr(draft) if sampling else None,
+            _ptr(draft_tokens) if K > 0 else None, _ptr(uniforms) if sampling else None,
+            B, K, V, dt, ctypes.c_float(temperature if sampling else 0.0), _MODES[mode],
             _ptr(acc), _ptr(out), _ptr(pt), _ptr(pd), _ptr(ws), ws.numel(), _stream_handle(dev, stream)]
     if events is not None:
         evs = list(events)

@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SPEC_F32, SPEC_BF16 = 0, 1
-SPEC_MODE_SAMPLE, SPEC_MODE_GREEDY = 0, 1
+SPEC_MODE_SAMPLE, SPEC_MODE_GREEDY, SPEC_MODE_SAMPLE_EARLY_EXIT = 0, 1, 2
 SPEC_OK = 0
 
 _lib = None

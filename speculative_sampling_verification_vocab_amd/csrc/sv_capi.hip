@@ -12,7 +12,10 @@ namespace {
 constexpr size_t kMaxGrid = 0x7fffffffu;
 
 bool valid_dtype(spec_dtype_t d) { return d == SPEC_F32 || d == SPEC_BF16; }
-bool valid_mode(spec_mode_t m) { return m == SPEC_MODE_SAMPLE || m == SPEC_MODE_GREEDY; }
+bool valid_mode(spec_mode_t m) {
+  return m == SPEC_MODE_SAMPLE || m == SPEC_MODE_GREEDY || m == SPEC_MODE_SAMPLE_EARLY_EXIT;
+}
+bool sampling(spec_mode_t m) { return m == SPEC_MODE_SAMPLE || m == SPEC_MODE_SAMPLE_EARLY_EXIT; }
 size_t elem_size(spec_dtype_t d) { return d == SPEC_BF16 ? 2 : 4; }
 
 // Shape checks shared by the sizing function and the entry points.
@@ -39,7 +42,8 @@ spec_status_t verify_impl(const void* target_logits, const void* draft_logits, c
                           size_t workspace_bytes, void* stream, void* const* events, int n_events) {
   const spec_status_t sc = check_shape(B, K, V, dtype, mode);
   if (sc != SPEC_OK) return sc;
-  const bool sample = mode == SPEC_MODE_SAMPLE;
+  const bool sample = sampling(mode);
+  const bool early = mode == SPEC_MODE_SAMPLE_EARLY_EXIT;
   if (sample && !(temperature > 0.0f && isfinite(temperature))) return SPEC_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   auto record = [&](int i) {
@@ -60,10 +64,10 @@ spec_status_t verify_impl(const void* target_logits, const void* draft_logits, c
   if (sample && K > 0) aligned = aligned && ((uintptr_t)draft_logits % 16 == 0);
   const sv::VerifyShape s = sv::make_shape(B, K, V, dtype == SPEC_BF16 ? 1 : 0, aligned);
 
-  const size_t need = sv::verify_workspace_layout(s, !sample, nullptr, nullptr);
+  const size_t need = sv::verify_workspace_layout(s, (int)mode, nullptr, nullptr);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 256) != 0) return SPEC_ERR_WORKSPACE;
   sv::VerifyWorkspace ws{};
-  sv::verify_workspace_layout(s, !sample, workspace, &ws);
+  sv::verify_workspace_layout(s, (int)mode, workspace, &ws);
 
   sv::VerifyIO io{};
   io.target = target_logits;
@@ -78,7 +82,9 @@ spec_status_t verify_impl(const void* target_logits, const void* draft_logits, c
 
   (void)hipGetLastError();  // clear a stale error so the checks below see only ours
   hipError_t e = hipSuccess;
-  if (sample) {
+  if (early) {
+    e = sv::launch_early_exit_pipeline(s, io, ws, st, events, n_events);
+  } else if (sample) {
     e = sv::launch_sample_pipeline(s, io, ws, st, events, n_events);
   } else {
     record(0);
@@ -110,7 +116,7 @@ const char* spec_status_string(spec_status_t status) {
 size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V, spec_dtype_t dtype, spec_mode_t mode) {
   if (check_shape(B, K, V, dtype, mode) != SPEC_OK || B == 0) return 0;
   const sv::VerifyShape s = sv::make_shape(B, K, V, dtype == SPEC_BF16 ? 1 : 0, false);
-  return sv::verify_workspace_layout(s, mode == SPEC_MODE_GREEDY, nullptr, nullptr);
+  return sv::verify_workspace_layout(s, (int)mode, nullptr, nullptr);
 }
 
 spec_status_t spec_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
@@ -136,7 +142,8 @@ spec_status_t spec_verify_timed(const void* target_logits, const void* draft_log
 int32_t spec_verify_launch_count(int32_t B, int32_t K, int32_t V, spec_dtype_t dtype, spec_mode_t mode) {
   if (check_shape(B, K, V, dtype, mode) != SPEC_OK || B == 0) return 0;
   if (mode == SPEC_MODE_GREEDY) return 2;
-  return sv::sample_launches(sv::make_shape(B, K, V, dtype == SPEC_BF16 ? 1 : 0, false));
+  const sv::VerifyShape s = sv::make_shape(B, K, V, dtype == SPEC_BF16 ? 1 : 0, false);
+  return mode == SPEC_MODE_SAMPLE_EARLY_EXIT ? sv::early_exit_launches(s) : sv::sample_launches(s);
 }
 
 spec_status_t spec_draft_head_shortlist(const void* h, const void* W, const int32_t* cluster_ids, int32_t B,

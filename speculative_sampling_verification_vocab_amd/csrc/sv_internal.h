@@ -51,6 +51,8 @@ struct VerifyWorkspace {
   SampleRowInfo* rows;  // [B]
   SampleTile* part_b;   // [B][NT_s]
   ArgTile* part_g;      // [B][K+1][NT]
+  float* gx;            // [B][2K] logits at the draft tokens: target rows 0..K-1, then draft rows
+  int32_t* cont;        // [K][B] early exit: 1 if the sequence accepted positions 0..j and goes on
 };
 
 struct VerifyIO {
@@ -67,7 +69,8 @@ struct VerifyIO {
 
 int tile_elems(int dtype);
 VerifyShape make_shape(int B, int K, int V, int dtype, bool aligned);
-size_t verify_workspace_layout(const VerifyShape& s, bool greedy, void* base, VerifyWorkspace* out);
+// mode: 0 SAMPLE, 1 GREEDY, 2 SAMPLE_EARLY_EXIT (spec_mode_t values).
+size_t verify_workspace_layout(const VerifyShape& s, int mode, void* base, VerifyWorkspace* out);
 
 // SAMPLE: three launches (statistics, sampling with accept decisions, pick).
 // events[k] (if present, k < n_events) is recorded before launch k and
@@ -75,6 +78,12 @@ size_t verify_workspace_layout(const VerifyShape& s, bool greedy, void* base, Ve
 int sample_launches(const VerifyShape& s);
 hipError_t launch_sample_pipeline(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws,
                                   hipStream_t st, void* const* events, int n_events);
+// SAMPLE_EARLY_EXIT: K + 2 launches (position i's statistics, each wave
+// first deciding position i - 1 of its sequence; then sampling, which decides
+// position K - 1, and pick); events as above.
+int early_exit_launches(const VerifyShape& s);
+hipError_t launch_early_exit_pipeline(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws,
+                                      hipStream_t st, void* const* events, int n_events);
 // GREEDY: greedy -> greedy_finalize.
 hipError_t launch_greedy(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws, hipStream_t st);
 hipError_t launch_greedy_finalize(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws,

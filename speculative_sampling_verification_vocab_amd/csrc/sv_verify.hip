@@ -37,6 +37,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "sv_common.h"
 #include "sv_internal.h"
 
@@ -66,6 +68,8 @@ struct VerifyArgs {
   TileStat* part_a;      // [B][2K][NT]
   SampleRowInfo* rows;   // [B] what pick_kernel needs about the sampled row pair
   SampleTile* part_b;    // [B][NTs]
+  float* gx;             // [B][2K] logits at the draft tokens (written by the statistics pass)
+  int32_t* cont;         // [K][B] early exit only
   int32_t* accepted_len;
   int32_t* out_tokens;
   float* p_t_out;
@@ -104,25 +108,34 @@ __device__ __forceinline__ void stats_tile(const VerifyArgs& a, const float (&x)
   if (lane == 0) *out = TileStat{M, S};
 }
 
-// Block `blk` of the statistics pass: one tile per wave, all of its loads
-// issued at once.  (Several tiles per wave with the next one loaded during the
+// Block g of the statistics pass over row r of sequence b (r < K: target row
+// r, else draft row r - K): one tile per wave, all of its loads issued at
+// once.  (Several tiles per wave with the next one loaded during the
 // reduction measured 2-6 % slower: the extra registers cost occupancy.)
 template <typename T, bool kAligned>
-__device__ __forceinline__ void stats_block(const VerifyArgs& a, int blk) {
+__device__ __forceinline__ void stats_row_block(const VerifyArgs& a, int b, int r, int g) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int K = a.K, R = 2 * K;
-  const int g = blk % a.NG;
-  const int rb = blk / a.NG;
-  const int r = rb % R;
-  const int b = rb / R;
   const T* row = r < K ? row_ptr<T>(a.target, (size_t)b * (K + 1) + r, a.V)
                        : row_ptr<T>(a.draft, (size_t)b * K + (r - K), a.V);
   const int t = g * kWavesPerBlock + wave;
+  // The drafted token of this row: the wave whose tile holds it also records
+  // its logit (re-read from cache) for the accept test.
+  const int d = a.tokens[(size_t)b * K + (r < K ? r : r - K)];
   if (t < a.NT) {
     float x[kPerLane<T>];
     load_tile<T, kAligned, kLoads>(row, a.V, t, lane, x);
     stats_tile<T>(a, x, a.part_a + ((size_t)b * R + r) * a.NT + t);
+    if (lane == 0 && d >= t * kTile<T> && d < (t + 1) * kTile<T> && d < a.V) a.gx[(size_t)b * R + r] = to_f32(row[d]);
   }
+}
+
+// Block `blk` of the statistics pass over every row 0..K-1 of target and draft.
+template <typename T, bool kAligned>
+__device__ __forceinline__ void stats_block(const VerifyArgs& a, int blk) {
+  const int R = 2 * a.K;
+  const int rb = blk / a.NG;
+  stats_row_block<T, kAligned>(a, rb / R, rb % R, blk % a.NG);
 }
 
 // ---------------------------------------------------------------------------
@@ -135,12 +148,115 @@ __device__ __forceinline__ void stats_block(const VerifyArgs& a, int blk) {
 // ---------------------------------------------------------------------------
 
 // Combines one row's statistics partials into (max, Z): Z = sum over tiles of
-// s * 2^((m_tile - max) * log2e/T), summed in double.
+// s * 2^((m_tile - max) * log2e/T), summed in double.  One wave; q is the
+// lane's tile (tile index = lane) for rows of at most 64 tiles.
 __device__ __forceinline__ void combine_row(const TileStat q, const VerifyArgs& a, float& m, double& z) {
   m = wave_max(q.m);
   z = 0.0;
   if (m != kNegInf && q.m != kNegInf) z = (double)q.s * (double)exp2_fast((q.m - m) * a.s_hi);
   z = wave_sum(z);
+}
+
+// The same for a row of any length p[0 .. NT): lane l takes tiles l, l+64, ...
+// For NT <= 64 the result is bit-identical to combine_row.
+__device__ __forceinline__ void combine_row_any(const TileStat* p, const VerifyArgs& a, float& m, double& z) {
+  const int lane = threadIdx.x & (kWave - 1);
+  m = kNegInf;
+  for (int t = lane; t < a.NT; t += kWave) m = fmaxf(m, p[t].m);
+  m = wave_max(m);
+  z = 0.0;
+  if (m != kNegInf) {
+    for (int t = lane; t < a.NT; t += kWave) {
+      const TileStat q = p[t];
+      if (q.m != kNegInf) z += (double)q.s * (double)exp2_fast((q.m - m) * a.s_hi);
+    }
+  }
+  z = wave_sum(z);
+}
+
+// The accept test of one position (Speculative Decoding lesson, "Step 1"):
+// P_t(d), P_d(d) in double from the row statistics; accept iff
+// u < min(1, P_t/P_d), P_d = 0 counting as an infinite ratio.  `bad` marks a
+// token outside [0, V) or a row without a finite maximum and normaliser.
+__device__ __forceinline__ bool accept_test(const VerifyArgs& a, int d, double xt, double xd, float mt, float md,
+                                            double zt, double zd, float u, double& pt, double& pd, bool& bad) {
+  bad = d < 0 || d >= a.V || !isfinite(mt) || !isfinite(md) || !(zt > 0.0) || !isfinite(zt) || !(zd > 0.0) ||
+        !isfinite(zd);
+  pt = __builtin_nan("");
+  pd = __builtin_nan("");
+  if (bad) return false;
+  pt = exp((xt - (double)mt) / a.T) / zt;
+  pd = exp((xd - (double)md) / a.T) / zd;
+  const double ratio = pd > 0.0 ? pt / pd : __builtin_inf();
+  const double thr = ratio < 1.0 ? ratio : 1.0;
+  return (double)u < thr;
+}
+
+// Decision of position j for sequence b, taken by one wave (every wave that
+// needs it takes it; the results are identical).  Returns 1 if the sequence
+// accepted position j and has positions left, else 0 with *sr filled for the
+// sampling pass (sr->n = j at a rejection, K when every position was
+// accepted, -1 for a fault).  The writer wave also stores the outputs that
+// position j determines: P_t(d_j), P_d(d_j), cont[j][b], and at the
+// sequence's end accepted_len, out_tokens (position n is left for
+// pick_kernel) and rows[b].  The caller has checked that the sequence reached
+// position j.
+__device__ int ee_decide(const VerifyArgs& a, int b, int j, bool writer, SampleRowInfo* sr) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int K = a.K, R = 2 * K;
+  const int32_t* tok = a.tokens + (size_t)b * K;
+  // Every draft token is range-checked at position 0, as in the full schedule.
+  bool bad_tok = false;
+  if (j == 0)
+    for (int q = lane; q < K; q += kWave) bad_tok |= tok[q] < 0 || tok[q] >= a.V;
+  bad_tok = wave_max((int)bad_tok) != 0;
+  const int d = tok[j];
+  const float u = a.uniforms[((size_t)b * (K + 1) + j) * 2];
+  const double xt = (double)a.gx[(size_t)b * R + j];
+  const double xd = (double)a.gx[(size_t)b * R + K + j];
+  const TileStat* pb = a.part_a + (size_t)b * R * a.NT;
+  float mt, md;
+  double zt, zd;
+  if (a.NT <= kWave) {
+    const TileStat none{kNegInf, 0.0f};
+    const TileStat qt = lane < a.NT ? pb[(size_t)j * a.NT + lane] : none;
+    const TileStat qd = lane < a.NT ? pb[(size_t)(K + j) * a.NT + lane] : none;
+    combine_row(qt, a, mt, zt);
+    combine_row(qd, a, md, zd);
+  } else {
+    combine_row_any(pb + (size_t)j * a.NT, a, mt, zt);
+    combine_row_any(pb + (size_t)(K + j) * a.NT, a, md, zd);
+  }
+  double pt, pd;
+  bool bad;
+  const bool acc = accept_test(a, d, xt, xd, mt, md, zt, zd, u, pt, pd, bad);
+  bad = bad || bad_tok;
+  const int n = bad ? -1 : (!acc ? j : (j == K - 1 ? K : -2));  // -2: goes on to position j + 1
+  if (n == -1) *sr = SampleRowInfo{0.0f, 0.0f, 1.0, 1.0, -1};
+  else if (n == K) *sr = SampleRowInfo{0.0f, 0.0f, 1.0, 1.0, K};
+  else *sr = SampleRowInfo{mt, md, zt, zd, n};
+  if (writer) {
+    if (lane == 0) {
+      if (a.p_t_out) a.p_t_out[(size_t)b * K + j] = bad ? __builtin_nanf("") : (float)pt;
+      if (a.p_d_out) a.p_d_out[(size_t)b * K + j] = bad ? __builtin_nanf("") : (float)pd;
+      a.cont[(size_t)j * a.B + b] = n == -2 ? 1 : 0;
+    }
+    if (n != -2) {
+      for (int q = lane; q < K; q += kWave) {
+        if (n < 0 || q > j) {  // not evaluated (or faulty): NaN
+          if (a.p_t_out) a.p_t_out[(size_t)b * K + q] = __builtin_nanf("");
+          if (a.p_d_out) a.p_d_out[(size_t)b * K + q] = __builtin_nanf("");
+        }
+      }
+      for (int q = lane; q <= K; q += kWave)
+        a.out_tokens[(size_t)b * (K + 1) + q] = (n >= 0 && q < n) ? tok[q] : -1;
+      if (lane == 0) {
+        a.accepted_len[b] = n;
+        a.rows[b] = *sr;
+      }
+    }
+  }
+  return n == -2 ? 1 : 0;
 }
 
 template <typename T>
@@ -157,8 +273,8 @@ __device__ int accept_sequence(const VerifyArgs& a, int b, bool write, SampleRow
     return 0;
   }
   if (threadIdx.x == 0) sh_bad = 0;
-  // Loads that do not depend on the statistics go first: the drafted
-  // tokens, their logits and the accept uniforms.
+  // Loads that do not depend on each other go first: the drafted tokens,
+  // their logits (recorded by the statistics pass) and the accept uniforms.
   double xt = 0.0, xd = 0.0;
   float u = 0.0f;
   int d = -1;
@@ -167,8 +283,8 @@ __device__ int accept_sequence(const VerifyArgs& a, int b, bool write, SampleRow
     d = a.tokens[(size_t)b * K + i];
     u = a.uniforms[((size_t)b * (K + 1) + i) * 2];
     if (d >= 0 && d < a.V) {
-      xt = (double)to_f32(row_ptr<T>(a.target, (size_t)b * (K + 1) + i, a.V)[d]);
-      xd = (double)to_f32(row_ptr<T>(a.draft, (size_t)b * K + i, a.V)[d]);
+      xt = (double)a.gx[(size_t)b * R + i];
+      xd = (double)a.gx[(size_t)b * R + K + i];
     }
   }
   // Row (max, Z).  Wave w owns rows w, w+4, ...  When each row has at most 64
@@ -198,18 +314,9 @@ __device__ int accept_sequence(const VerifyArgs& a, int b, bool write, SampleRow
     }
   } else {
     for (int r = wave; r < R; r += kWavesPerBlock) {
-      const TileStat* p = pb + (size_t)r * a.NT;
-      float m = kNegInf;
-      for (int t = lane; t < a.NT; t += kWave) m = fmaxf(m, p[t].m);
-      m = wave_max(m);
-      double z = 0.0;
-      if (m != kNegInf) {
-        for (int t = lane; t < a.NT; t += kWave) {
-          const TileStat q = p[t];
-          if (q.m != kNegInf) z += (double)q.s * (double)exp2_fast((q.m - m) * a.s_hi);
-        }
-      }
-      z = wave_sum(z);
+      float m;
+      double z;
+      combine_row_any(pb + (size_t)r * a.NT, a, m, z);
       if (lane == 0) {
         sh_m[r] = m;
         sh_z[r] = z;
@@ -221,20 +328,9 @@ __device__ int accept_sequence(const VerifyArgs& a, int b, bool write, SampleRow
   double pt = __builtin_nan(""), pd = __builtin_nan("");
   if ((int)threadIdx.x < K) {
     const int i = threadIdx.x;
-    const float mt = sh_m[i], md = sh_m[K + i];
-    const double zt = sh_z[i], zd = sh_z[K + i];
-    const bool bad = d < 0 || d >= a.V || !isfinite(mt) || !isfinite(md) || !(zt > 0.0) || !isfinite(zt) ||
-                     !(zd > 0.0) || !isfinite(zd);
-    int acc = 0;
-    if (!bad) {
-      pt = exp((xt - (double)mt) / a.T) / zt;
-      pd = exp((xd - (double)md) / a.T) / zd;
-      const double ratio = pd > 0.0 ? pt / pd : __builtin_inf();
-      const double thr = ratio < 1.0 ? ratio : 1.0;
-      acc = (double)u < thr;
-    } else {
-      atomicOr(&sh_bad, 1);
-    }
+    bool bad;
+    const bool acc = accept_test(a, d, xt, xd, sh_m[i], sh_m[K + i], sh_z[i], sh_z[K + i], u, pt, pd, bad);
+    if (bad) atomicOr(&sh_bad, 1);
     sh_acc[i] = acc;
   }
   __syncthreads();
@@ -357,14 +453,32 @@ __device__ __forceinline__ void bonus_tile(const VerifyArgs& a, int b, int t, co
 }
 
 // Block `blk` of the sampling pass.
-template <typename T, bool kAligned>
+// kFromRows: n and the row record come from the early-exit decisions
+// (a.rows) instead of this block's own accept prologue.
+template <typename T, bool kAligned, bool kFromRows = false>
 __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int K = a.K;
   const int g = blk % a.NGs;
   const int b = blk / a.NGs;
   SampleRowInfo sr;
-  const int n = accept_sequence<T>(a, b, g == 0, &sr);
+  int n;
+  if constexpr (kFromRows) {
+    // Early exit: a sequence that reached position K - 1 is decided here (by
+    // every wave; wave 0 of the first block writes the outputs); the others
+    // ended earlier and left their record in rows[b].
+    if (K == 0) {
+      n = 0;
+    } else if (K == 1 || a.cont[(size_t)(K - 2) * a.B + b] != 0) {
+      ee_decide(a, b, K - 1, g == 0 && threadIdx.x < kWave, &sr);
+      n = sr.n;
+    } else {
+      sr = a.rows[b];
+      n = sr.n;
+    }
+  } else {
+    n = accept_sequence<T>(a, b, g == 0, &sr);
+  }
   if (n < 0) return;  // faulty sequence: outputs already written
   const bool resid = n < K;
   const T* trow = row_ptr<T>(a.target, (size_t)b * (K + 1) + n, a.V);
@@ -660,6 +774,55 @@ __global__ void __launch_bounds__(kBlock) pick_kernel(VerifyArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Early-exit schedule: position i is processed only for the sequences that
+// accepted every position before it, so rows after a sequence's first
+// rejection are never read (they cannot change its output: Speculative
+// Decoding lesson, "Core algorithm" step 5).  Phase i = statistics of target
+// and draft row i, then one decision wave per sequence.  The statistics and
+// decision code is the SAMPLE schedule's, so both schedules take the same
+// decisions bit for bit.
+// ---------------------------------------------------------------------------
+
+// Statistics tiles per wave in the early-exit phases.  (Two or four, which
+// amortise the decision prologue over more tiles, measured within 2 % at
+// B=256 and slower for small batches.)
+constexpr int kEETPW = 1;
+
+// Phase i of the early-exit schedule: statistics of target and draft row i
+// for the sequences that accepted positions 0..i-1.  For i > 0 every wave
+// first decides position i - 1 of its sequence (its statistics are complete:
+// the previous launch produced them); block 0 of the target row writes the
+// outputs of that decision.
+template <typename T, bool kAligned>
+__global__ void __launch_bounds__(kBlock) ee_phase_kernel(VerifyArgs a, int i) {
+  const int wave = threadIdx.x / kWave;
+  const int NGe = (a.NT + kEETPW * kWavesPerBlock - 1) / (kEETPW * kWavesPerBlock);
+  const int b = blockIdx.x / (2 * NGe), rem = blockIdx.x % (2 * NGe);
+  const int which = rem / NGe, g = rem % NGe;
+  if (i > 0) {
+    const bool writer = g == 0 && which == 0 && wave == 0;
+    if (i > 1 && a.cont[(size_t)(i - 2) * a.B + b] == 0) {
+      // ended earlier: carry the flag forward (the workspace holds stale
+      // flags from earlier calls, so every entry a later launch reads is written)
+      if (writer && threadIdx.x == 0) a.cont[(size_t)(i - 1) * a.B + b] = 0;
+      return;
+    }
+    SampleRowInfo sr;
+    if (!ee_decide(a, b, i - 1, writer, &sr)) return;
+  }
+  for (int j = 0; j < kEETPW; ++j) {
+    const int t = (g * kEETPW + j) * kWavesPerBlock + wave;
+    if (t >= a.NT) break;
+    stats_row_block<T, kAligned>(a, b, which == 0 ? i : a.K + i, t / kWavesPerBlock);
+  }
+}
+
+template <typename T, bool kAligned>
+__global__ void __launch_bounds__(kBlock) ee_sample_kernel(VerifyArgs a) {
+  sample_block<T, kAligned, true>(a, blockIdx.x);
+}
+
+// ---------------------------------------------------------------------------
 // Greedy verify.
 // ---------------------------------------------------------------------------
 
@@ -791,30 +954,30 @@ VerifyShape make_shape(int B, int K, int V, int dtype, bool aligned) {
       break;
     }
   }
-#ifdef SV_SAMPLE_TPW
-  s.TPW_s = SV_SAMPLE_TPW;
-#endif
   s.NG_s = (s.NT_s + s.TPW_s * kWavesPerBlock - 1) / (s.TPW_s * kWavesPerBlock);
   return s;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t verify_workspace_layout(const VerifyShape& s, bool greedy, void* base, VerifyWorkspace* out) {
+size_t verify_workspace_layout(const VerifyShape& s, int mode, void* base, VerifyWorkspace* out) {
   const size_t B = (size_t)s.B, K = (size_t)s.K;
+  const bool greedy = mode == 1, early = mode == 2;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
     off = align256(off + bytes);
     return at;
   };
-  size_t o_pa = 0, o_rows = 0, o_pb = 0, o_pg = 0;
+  size_t o_pa = 0, o_rows = 0, o_pb = 0, o_pg = 0, o_gx = 0, o_cont = 0;
   if (greedy) {
     o_pg = take(B * (K + 1) * (size_t)s.NT * sizeof(ArgTile));
   } else {
     o_pa = take(B * 2 * K * (size_t)s.NT * sizeof(TileStat));
     o_rows = take(B * sizeof(SampleRowInfo));
     o_pb = take(B * (size_t)s.NT_s * sizeof(SampleTile));
+    o_gx = take(B * 2 * (K > 0 ? K : 1) * sizeof(float));
+    if (early) o_cont = take(B * (K > 0 ? K : 1) * sizeof(int32_t));
   }
   if (out && base) {
     VerifyWorkspace w{};
@@ -825,6 +988,8 @@ size_t verify_workspace_layout(const VerifyShape& s, bool greedy, void* base, Ve
       w.part_a = reinterpret_cast<TileStat*>(p + o_pa);
       w.rows = reinterpret_cast<SampleRowInfo*>(p + o_rows);
       w.part_b = reinterpret_cast<SampleTile*>(p + o_pb);
+      w.gx = reinterpret_cast<float*>(p + o_gx);
+      if (early) w.cont = reinterpret_cast<int32_t*>(p + o_cont);
     }
     *out = w;
   }
@@ -853,6 +1018,8 @@ static VerifyArgs verify_args(const VerifyShape& s, const VerifyIO& io, const Ve
   a.part_a = ws.part_a;
   a.rows = ws.rows;
   a.part_b = ws.part_b;
+  a.gx = ws.gx;
+  a.cont = ws.cont;
   a.accepted_len = io.accepted_len;
   a.out_tokens = io.out_tokens;
   a.p_t_out = io.p_target;
@@ -885,6 +1052,39 @@ hipError_t launch_sample_pipeline(const VerifyShape& s, const VerifyIO& io, cons
   if (e == hipSuccess)
     e = dispatch4(s.dtype, s.aligned, dim3((unsigned)((size_t)s.B * s.NG_s)), st, sample_kernel<uint16_t, true>,
                   sample_kernel<uint16_t, false>, sample_kernel<float, true>, sample_kernel<float, false>, a);
+  record();
+  if (e == hipSuccess)
+    e = dispatch4(s.dtype, s.aligned, dim3((unsigned)s.B), st, pick_kernel<uint16_t, true>,
+                  pick_kernel<uint16_t, false>, pick_kernel<float, true>, pick_kernel<float, false>, a);
+  record();
+  return e;
+}
+
+int early_exit_launches(const VerifyShape& s) { return s.B == 0 ? 0 : s.K + 2; }
+
+hipError_t launch_early_exit_pipeline(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws,
+                                      hipStream_t st, void* const* events, int n_events) {
+  if (s.B == 0) return hipSuccess;
+  const VerifyArgs a = verify_args(s, io, ws);
+  int k = 0;
+  auto record = [&]() {
+    if (events && k < n_events && events[k]) (void)hipEventRecord(static_cast<hipEvent_t>(events[k]), st);
+    ++k;
+  };
+  hipError_t e = hipSuccess;
+  const int NGe = (s.NT + kEETPW * kWavesPerBlock - 1) / (kEETPW * kWavesPerBlock);
+  const dim3 phase_grid((unsigned)((size_t)s.B * 2 * NGe));
+  for (int i = 0; i < s.K && e == hipSuccess; ++i) {
+    record();
+    e = dispatch4(s.dtype, s.aligned, phase_grid, st, ee_phase_kernel<uint16_t, true>,
+                  ee_phase_kernel<uint16_t, false>, ee_phase_kernel<float, true>, ee_phase_kernel<float, false>, a,
+                  i);
+  }
+  record();
+  if (e == hipSuccess)
+    e = dispatch4(s.dtype, s.aligned, dim3((unsigned)((size_t)s.B * s.NG_s)), st, ee_sample_kernel<uint16_t, true>,
+                  ee_sample_kernel<uint16_t, false>, ee_sample_kernel<float, true>, ee_sample_kernel<float, false>,
+                  a);
   record();
   if (e == hipSuccess)
     e = dispatch4(s.dtype, s.aligned, dim3((unsigned)s.B), st, pick_kernel<uint16_t, true>,

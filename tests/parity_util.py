@@ -89,7 +89,7 @@ def run_gpu(case, mode="sample", return_probs=True, **kw):
     dr = case.draft.to(dev) if case.draft is not None else None
     tok = case.draft_tokens.to(dev)
     uni = case.uniforms.to(dev)
-    res = sv.spec_verify(tgt, dr, tok, uni, case.temperature if mode == "sample" else 0.0, mode,
+    res = sv.spec_verify(tgt, dr, tok, uni, case.temperature if mode != "greedy" else 0.0, mode,
                          return_probs=return_probs, **kw)
     torch.cuda.synchronize()
     return [r.cpu().numpy() for r in res]

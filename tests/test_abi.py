@@ -51,6 +51,19 @@ def test_workspace_sizes(lib):
     assert lib.spec_verify_workspace_bytes(4, 3, 1000, 7, 0) == 0       # bad dtype
     g = lib.spec_verify_workspace_bytes(256, 7, 262144, 1, 1)
     assert 0 < g < big
+    # the early-exit schedule adds one int32 flag per (position, sequence)
+    ee = lib.spec_verify_workspace_bytes(256, 7, 262144, 1, 2)
+    assert big < ee <= big + 256 * 7 * 4 + 256
+
+
+def test_launch_counts(lib):
+    f = lib.spec_verify_launch_count
+    assert f(256, 7, 262144, 1, 0) == 3            # statistics, sampling, pick
+    assert f(256, 7, 262144, 1, 1) == 2            # greedy argmax, finalize
+    assert f(256, 7, 262144, 1, 2) == 7 + 2        # one launch per position; sampling; pick
+    assert f(4, 0, 1000, 0, 2) == 2
+    assert f(0, 7, 262144, 1, 0) == 0
+    assert f(4, 3, 1000, 1, 3) == 0                # unknown mode
 
 
 def _call(lib, **over):
@@ -79,6 +92,11 @@ def test_host_validation(lib):
     assert _call(lib, V=0) == INVALID
     assert _call(lib, dt=5) == INVALID
     assert _call(lib, mode=3) == INVALID
+    # the early-exit schedule validates like SAMPLE
+    assert _call(lib, mode=2, T=0.0) == INVALID
+    assert _call(lib, mode=2, uni=None) == INVALID
+    assert _call(lib, mode=2, draft=None) == INVALID
+    assert _call(lib, mode=2) == WS
     assert _call(lib, K=65) == UNSUP
     # the workspace is checked after the arguments: missing, too small, misaligned
     assert _call(lib) == WS

@@ -52,6 +52,8 @@ def _load():
             lib.oracle_row_stats.restype = ctypes.c_int
             lib.oracle_head.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, P, P, P]
             lib.oracle_head.restype = ctypes.c_int
+            lib.oracle_kv_commit.argtypes = [P, P, P, P, P, i32, i32, i32, i32, ctypes.c_int64]
+            lib.oracle_kv_commit.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -188,3 +190,26 @@ def head(h, W, cluster_ids, cluster_size, dense=False, threads=1):
 
 def default_threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
+
+
+def kv_commit(cache, staging, accepted_len, cache_len):
+    """KV-cache commit (see oracle_kv_commit in oracle.c).
+
+    cache [P, B, Lmax, E] and staging [P, B, K, E] numpy arrays of any
+    fixed-size dtype (copied byte for byte); accepted_len, cache_len int32 [B].
+    Returns (new cache, new cache_len, status) without modifying the inputs."""
+    cache = np.array(cache, copy=True, order="C")
+    staging = np.ascontiguousarray(staging)
+    if staging.dtype != cache.dtype:
+        raise ValueError("cache and staging must share a dtype")
+    P, B, Lmax = cache.shape[:3]
+    K = staging.shape[2]
+    if staging.shape[:2] != (P, B) or staging.shape[3:] != cache.shape[3:]:
+        raise ValueError("staging must be [P, B, K, ...] matching the cache")
+    row_bytes = int(np.prod(cache.shape[3:], dtype=np.int64)) * cache.dtype.itemsize
+    acc = np.ascontiguousarray(accepted_len, dtype=np.int32)
+    ln = np.array(cache_len, dtype=np.int32, copy=True)
+    status = np.zeros(B, dtype=np.int32)
+    _load().oracle_kv_commit(_ptr(cache), _ptr(staging), _ptr(acc), _ptr(ln), _ptr(status),
+                             P, B, K, Lmax, row_bytes)
+    return cache, ln, status

@@ -295,3 +295,39 @@ int oracle_head(const uint16_t* h, const uint16_t* W, const int32_t* cluster_ids
     }
   return 0;
 }
+
+/*
+ * KV-cache commit after a verify step (Speculative Decoding lesson,
+ * nextadmin.net, section on KV-cache management and exercise 4): the
+ * verifier's forward over K drafts produced one KV entry per draft position;
+ * after verification the cache must hold only the accepted prefix.  The new
+ * entries sit in a staging buffer and the accepted ones are committed.
+ *   cache      [P][B][Lmax][row_bytes]  P planes (for instance layers x {K, V})
+ *   staging    [P][B][K][row_bytes]     entries of draft positions 0..K-1
+ *   accepted_len [B]  n: staging entries 0..n-1 go to cache positions
+ *                     cache_len[b] .. cache_len[b]+n-1
+ *   cache_len  [B] in/out: advanced by n where the commit happens
+ *   status     [B] out: 0 committed, 1 no room (cache_len + n > Lmax),
+ *                       2 n outside [0, K] (e.g. -1 from a faulty verify);
+ *                       nothing is committed unless the status is 0
+ * Plain byte copies, one entry at a time.  Returns 0.
+ */
+int oracle_kv_commit(uint8_t* cache, const uint8_t* staging, const int32_t* accepted_len,
+                     int32_t* cache_len, int32_t* status, int32_t P, int32_t B, int32_t K,
+                     int32_t Lmax, int64_t row_bytes) {
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t n = accepted_len[b];
+    const int32_t len = cache_len[b];
+    if (n < 0 || n > K) { status[b] = 2; continue; }
+    if (len < 0 || len > Lmax - n) { status[b] = 1; continue; }
+    for (int32_t p = 0; p < P; ++p)
+      for (int32_t j = 0; j < n; ++j) {
+        const uint8_t* src = staging + (((size_t)p * B + b) * (size_t)K + (size_t)j) * (size_t)row_bytes;
+        uint8_t* dst = cache + (((size_t)p * B + b) * (size_t)Lmax + (size_t)(len + j)) * (size_t)row_bytes;
+        for (int64_t q = 0; q < row_bytes; ++q) dst[q] = src[q];
+      }
+    cache_len[b] = len + n;
+    status[b] = 0;
+  }
+  return 0;
+}

@@ -13,6 +13,7 @@ import tempfile
 import pytest
 
 import oracle
+from tests import test_oracle_kv as kv_pins
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
@@ -34,6 +35,11 @@ MUTANTS = {
     "emit_draft_at_rejection": ("out[n] = pick;", "out[n] = n < K ? d[n] : pick;"),
     "zero_ratio_accepts": ("double ratio = pd > 0.0 ? pt / pd : INFINITY;",
                            "double ratio = pd > 0.0 ? pt / pd : 0.0;"),
+    "kv_commit_off_by_one": ("(size_t)Lmax + (size_t)(len + j)) * (size_t)row_bytes;",
+                             "(size_t)Lmax + (size_t)(len + j + 1)) * (size_t)row_bytes;"),
+    "kv_commit_includes_rejected": ("for (int32_t j = 0; j < n; ++j) {", "for (int32_t j = 0; j <= n && j < K; ++j) {"),
+    "kv_commit_no_room_check": ("if (len < 0 || len > Lmax - n) { status[b] = 1; continue; }",
+                                "if (len < 0) { status[b] = 1; continue; }"),
 }
 
 PINS = [
@@ -49,6 +55,9 @@ PINS = [
     pins.test_inverse_cdf_skips_zero_weight_tokens,
     pins.test_expected_tokens_closed_form,
     lambda: pins.test_chi_square_output_follows_target(2.0),
+    kv_pins.test_exercise_prefix_plus_accepted_drafts,
+    kv_pins.test_multi_step_cache_holds_the_committed_stream,
+    kv_pins.test_status_cases_commit_nothing,
 ]
 
 
@@ -70,7 +79,7 @@ def test_mutant_is_caught(name, monkeypatch):
     with tempfile.TemporaryDirectory() as tmp:
         so = _build_mutant(name, old, new, tmp)
         lib = ctypes.CDLL(so)
-        for fn in ("oracle_verify", "oracle_row_stats", "oracle_head"):
+        for fn in ("oracle_verify", "oracle_row_stats", "oracle_head", "oracle_kv_commit"):
             getattr(lib, fn).argtypes = getattr(real, fn).argtypes
             getattr(lib, fn).restype = getattr(real, fn).restype
         monkeypatch.setattr(oracle, "_lib", lib)

@@ -21,6 +21,8 @@ Prints ONE JSON line on stdout:
              same batch (it is a baseline, not a target).
   early_exit the position-by-position schedule on the same batch (identical
              outputs; rows after each sequence's first rejection not read).
+  kv_commit  the KV-cache commit of that batch's accepted drafts on a
+             Llama-3-8B-like cache layout (bytes moved, HBM rate).
 """
 from __future__ import annotations
 
@@ -100,6 +102,59 @@ def cpu_baseline(case, res, args, K):
                       f"{threads} threads, {wall:.2f} s wall; accepted_len agrees on {agree}/{nb}"}
 
 
+def bench_kv_commit(accepted_len, K, steps, dev):
+    """KV-cache commit of one verify step's accepted drafts (spec_kv_commit)
+    on a Llama-3-8B-like layout: 32 layers x {K, V} planes, 8 KV heads x 128
+    dims, bf16, 128 cache positions, B sequences.  Bytes moved = 2 (read and
+    write) x sum over committed sequences of n x planes x row bytes.  Each
+    timed call restores the lengths first (outside the events), so every call
+    moves the same rows.  Sampled rows are checked against the staging buffer."""
+    import numpy as np
+    import torch
+
+    import speculative_sampling_verification_vocab_amd as sv
+    from workloads import KV_WORKLOAD, kv_case
+
+    w = KV_WORKLOAD
+    B = int(accepted_len.numel())
+    kc = kv_case(w["P"], B, K, w["Lmax"], w["E"], device=dev)
+    ln0 = kc.cache_len.clone()
+    stream = torch.cuda.current_stream(dev)
+    acc = accepted_len.to(torch.int32)
+    st = sv.spec_kv_commit(kc.cache, kc.staging, acc, kc.cache_len)
+    torch.cuda.synchronize()
+    n = acc.cpu().numpy()
+    l0 = ln0.cpu().numpy()
+    ok = st.cpu().numpy() == 0
+    rng = np.random.default_rng(11)
+    checked = 0
+    for _ in range(16):
+        b = int(rng.integers(B))
+        p = int(rng.integers(w["P"]))
+        if not ok[b] or n[b] == 0:
+            continue
+        got = kc.cache[p, b, l0[b]:l0[b] + n[b]]
+        assert torch.equal(got, kc.staging[p, b, :n[b]]), "kv commit: committed rows differ from staging"
+        checked += 1
+    row_bytes = w["E"] * 2
+    moved = int(2 * n[ok].clip(min=0).sum()) * w["P"] * row_bytes
+    times = []
+    for _ in range(steps):
+        kc.cache_len.copy_(ln0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        sv.spec_kv_commit(kc.cache, kc.staging, acc, kc.cache_len, status=st)
+        e1.record(stream)
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in times]))
+    del kc
+    return {"workload": w["name"].replace("b256", f"b{B}"), "P": w["P"], "E": w["E"], "L_max": w["Lmax"],
+            "ms_per_call": ms, "bytes_moved": moved, "achieved_gbs": moved / (ms * 1e-3) / 1e9,
+            "hbm_frac": moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "committed_sequences": int(ok.sum()),
+            "mean_committed_entries": float(n[ok].mean()) if ok.any() else 0.0, "sampled_rows_checked": checked}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,6 +162,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="b256_k7_v262144_bf16")
     ap.add_argument("--mode", default="sample", choices=["sample", "greedy", "sample_early_exit"])
+    ap.add_argument("--no-kv-commit", action="store_true",
+                    help="skip the KV-cache commit of the verify step's accepted drafts in sample mode")
     ap.add_argument("--no-early-exit", action="store_true",
                     help="skip the extra timing of the early-exit schedule in sample mode")
     ap.add_argument("--cpu-sample", type=int, default=256, help="sequences timed on the CPU oracle")
@@ -244,6 +301,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, res, args, K)
+    kv = None
+    if args.mode == "sample" and not args.no_kv_commit:
+        kv = bench_kv_commit(res[0], K, args.steps, dev)
 
     out = {
         "metric": "verified draft positions/sec (B*(K+1)) and achieved HBM GB/s vs peak",
@@ -271,6 +331,8 @@ def main():
     }
     if early is not None:
         out["early_exit"] = early
+    if kv is not None:
+        out["kv_commit"] = kv
     print(json.dumps(out), flush=True)
 
 

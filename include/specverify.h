@@ -177,6 +177,38 @@ spec_status_t spec_draft_head_shortlist(const void* h, const void* W, const int3
                                         spec_dtype_t dense_dtype,
                                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * KV-cache commit after a verify step (Speculative Decoding lesson,
+ * nextadmin.net, section on KV-cache management and exercise 4).  The
+ * target's forward over the K drafts wrote one KV entry per draft position
+ * into `staging`; this call moves the entries of the accepted drafts into the
+ * cache at each sequence's current length and advances the length, so the
+ * cache holds exactly the accepted prefix.  (The token sampled at position n
+ * has no entry yet: the next forward computes it.)
+ *
+ *   cache         [P, B, L_max, E] of dtype, device: P planes (for instance
+ *                 layers x {key, value}), E elements per token per plane
+ *                 (for instance kv_heads x head_dim).  Updated in place.
+ *   staging       [P, B, K, E] of dtype: entries for draft positions 0..K-1.
+ *   accepted_len  [B] int32, spec_verify's output: staging entries 0..n-1 are
+ *                 committed to cache positions cache_len[b] .. cache_len[b]+n-1.
+ *   cache_len     [B] int32 in/out: advanced by n where the commit happens.
+ *   status        [B] int32 out, or NULL: 0 committed; 1 no room
+ *                 (cache_len + n > L_max); 2 n outside [0, K] (for instance
+ *                 -1 from a faulty verify).  Nothing is committed unless 0.
+ * Two launches on `stream` (copy; lengths and status).  All buffers are
+ * caller-owned device memory; nothing is allocated.  16-byte vector copies
+ * when E * size is a multiple of 16 and both buffers are 16-byte aligned,
+ * element copies otherwise.
+ * Errors: SPEC_ERR_INVALID_ARG for NULL buffers, buffers not aligned to the
+ * element size, negative sizes, an unknown dtype or sizes that overflow;
+ * SPEC_ERR_UNSUPPORTED for a grid too large for
+ * one launch; SPEC_ERR_HIP for a launch failure.
+ */
+spec_status_t spec_kv_commit(void* cache, const void* staging, const int32_t* accepted_len,
+                             int32_t* cache_len, int32_t* status, int32_t P, int32_t B, int32_t K,
+                             int32_t L_max, int32_t E, spec_dtype_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

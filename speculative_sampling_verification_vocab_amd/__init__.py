@@ -19,6 +19,7 @@ from . import _native
 from ._native import SpecVerifyError  # noqa: F401
 
 __all__ = ["spec_verify", "spec_verify_workspace_bytes", "spec_verify_launch_count", "spec_draft_head_shortlist",
+           "spec_kv_commit",
            "Workspace", "SpecVerifyError", "abi_version"]
 
 _DTYPES = {torch.bfloat16: _native.SPEC_BF16, torch.float32: _native.SPEC_F32}
@@ -176,3 +177,37 @@ def spec_draft_head_shortlist(h: torch.Tensor, W: torch.Tensor, cluster_ids: tor
                                        _stream_handle(dev, stream))
     _native.check(st, "spec_draft_head_shortlist")
     return comp, dn
+
+
+def spec_kv_commit(cache: torch.Tensor, staging: torch.Tensor, accepted_len: torch.Tensor,
+                   cache_len: torch.Tensor, status: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Commit the accepted drafts' KV entries (see spec_kv_commit in specverify.h).
+
+    cache [P, B, L_max, ...] and staging [P, B, K, ...] (same trailing shape,
+    bf16 or float32, contiguous, on the GPU); accepted_len int32 [B] from
+    spec_verify; cache_len int32 [B], advanced in place.  Returns the status
+    tensor (int32 [B]: 0 committed, 1 no room, 2 accepted_len outside [0, K])."""
+    for t, name in ((cache, "cache"), (staging, "staging"), (accepted_len, "accepted_len"), (cache_len, "cache_len")):
+        _need_gpu(t, name)
+    dt = _DTYPES.get(cache.dtype)
+    if dt is None or staging.dtype != cache.dtype:
+        raise ValueError("cache and staging must both be bfloat16 or both float32")
+    if cache.dim() < 3 or staging.dim() != cache.dim() or staging.shape[:2] != cache.shape[:2] \
+            or staging.shape[3:] != cache.shape[3:]:
+        raise ValueError("cache must be [P, B, L_max, ...] and staging [P, B, K, ...] with the same trailing shape")
+    if not (cache.is_contiguous() and staging.is_contiguous()):
+        raise ValueError("cache and staging must be contiguous")
+    P, B, Lmax = cache.shape[:3]
+    K = staging.shape[2]
+    E = 1
+    for x in cache.shape[3:]:
+        E *= int(x)
+    for t, name in ((accepted_len, "accepted_len"), (cache_len, "cache_len")):
+        if t.dtype != torch.int32 or tuple(t.shape) != (B,) or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous int32 [B]")
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=cache.device)
+    st = _native.load().spec_kv_commit(_ptr(cache), _ptr(staging), _ptr(accepted_len), _ptr(cache_len),
+                                       _ptr(status), P, B, K, Lmax, E, dt, _stream_handle(cache.device, stream))
+    _native.check(st, "spec_kv_commit")
+    return status

@@ -166,4 +166,31 @@ spec_status_t spec_draft_head_shortlist(const void* h, const void* W, const int3
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
+spec_status_t spec_kv_commit(void* cache, const void* staging, const int32_t* accepted_len, int32_t* cache_len,
+                             int32_t* status, int32_t P, int32_t B, int32_t K, int32_t L_max, int32_t E,
+                             spec_dtype_t dtype, void* stream) {
+  if (!valid_dtype(dtype)) return SPEC_ERR_INVALID_ARG;
+  if (P < 0 || B < 0 || K < 0 || L_max < 0 || E < 0) return SPEC_ERR_INVALID_ARG;
+  if (B == 0) return SPEC_OK;
+  if (!accepted_len || !cache_len) return SPEC_ERR_INVALID_ARG;
+  const size_t esz = elem_size(dtype);
+  const size_t row = (size_t)E * esz;
+  // the larger buffer must fit size_t byte offsets
+  const size_t planes = (size_t)P * (size_t)B;
+  const size_t rows = planes * (size_t)(L_max > K ? L_max : K);
+  if (planes / (size_t)B != (size_t)P || (row != 0 && rows > SIZE_MAX / 2 / row)) return SPEC_ERR_INVALID_ARG;
+  const bool copies = P > 0 && K > 0 && E > 0;
+  if (copies && (!cache || !staging)) return SPEC_ERR_INVALID_ARG;
+  if (copies && ((uintptr_t)cache % esz != 0 || (uintptr_t)staging % esz != 0)) return SPEC_ERR_INVALID_ARG;
+  const bool vec = row % 16 == 0 && ((uintptr_t)cache % 16 == 0) && ((uintptr_t)staging % 16 == 0);
+  const size_t units = copies ? (vec ? row / 16 : (size_t)E) : 0;
+  if (copies && units > 0x7fffffffu / (size_t)K) return SPEC_ERR_UNSUPPORTED;  // K > 0 when copies
+  if (copies && planes > kMaxGrid) return SPEC_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  const hipError_t e = sv::launch_kv_commit(copies ? cache : nullptr, copies ? staging : nullptr, accepted_len,
+                                            cache_len, status, copies ? P : 0, B, K, L_max, (int64_t)row,
+                                            (int)esz, vec, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
 }  // extern "C"

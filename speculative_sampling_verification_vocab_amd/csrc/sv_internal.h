@@ -94,4 +94,9 @@ hipError_t launch_head(const void* h, const void* W, const int32_t* cluster_ids,
                        hipStream_t st);
 int head_max_contexts();
 
+// KV-cache commit: copy, then lengths and status (two launches).
+hipError_t launch_kv_commit(void* cache, const void* staging, const int32_t* accepted_len, int32_t* cache_len,
+                            int32_t* status, int P, int B, int K, int Lmax, int64_t row_bytes, int elem_bytes,
+                            bool vec_ok, hipStream_t st);
+
 }  // namespace sv

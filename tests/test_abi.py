@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("spec_verify", "spec_verify_timed", "spec_verify_workspace_bytes",
-              "spec_draft_head_shortlist", "spec_status_string", "spec_abi_version"):
+              "spec_draft_head_shortlist", "spec_status_string", "spec_abi_version", "spec_kv_commit"):
         assert n in names
 
 
@@ -117,3 +117,39 @@ def test_head_validation(lib):
     assert f(fake, fake, fake, 2, 4, 64, 1000, 10, 2, None, None, 0, None, 0, None) == 1
     assert f(fake, fake, fake, 2, 4, 64, 1000, 10, 101, fake, None, 0, None, 0, None) == 1
     assert f(fake, fake, fake, 0, 4, 64, 1000, 10, 2, fake, None, 0, None, 0, None) == 0
+
+
+def test_kv_commit_validation(lib):
+    fake = ctypes.c_void_p(0x10000)
+    f = lib.spec_kv_commit
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int32] * 5 + [ctypes.c_int, ctypes.c_void_p]
+    ok = dict(cache=fake, staging=fake, acc=fake, ln=fake, st=None, P=4, B=2, K=3, L=16, E=64, dt=1)
+
+    def call(**o):
+        a = dict(ok)
+        a.update(o)
+        return f(a["cache"], a["staging"], a["acc"], a["ln"], a["st"], a["P"], a["B"], a["K"], a["L"],
+                 a["E"], a["dt"], None)
+    INVALID = 1
+    assert call(B=0) == 0                       # empty call, nothing launched
+    assert call(cache=None) == INVALID
+    assert call(staging=None) == INVALID
+    assert call(acc=None) == INVALID
+    assert call(ln=None) == INVALID
+    assert call(P=-1) == INVALID
+    assert call(E=-2) == INVALID
+    assert call(dt=9) == INVALID
+    assert call(cache=ctypes.c_void_p(0x10001)) == INVALID   # not aligned to the element size
+
+
+def test_kv_commit_zero_drafts_validates_without_dividing_by_k(lib):
+    """K == 0 (nothing to copy) must pass host validation (regression: a size
+    check divided by K).  On a machine without a GPU the lengths launch then
+    reports SPEC_ERR_HIP; on a GPU it succeeds."""
+    fake = ctypes.c_void_p(0x10000)
+    f = lib.spec_kv_commit
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int32] * 5 + [ctypes.c_int, ctypes.c_void_p]
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("the launch would dereference the fake pointers on a GPU")
+    assert f(fake, fake, fake, fake, None, 2, 3, 0, 10, 8, 1, None) in (0, 4)

@@ -28,10 +28,12 @@ __all__ = [
     "normal_logits", "round_to", "noisy_copy", "gumbel_max_tokens",
     "argmax_tokens", "verify_uniforms", "verify_case", "workload_case",
     "head_case", "top_clusters", "bf16_bits", "f32_from_bf16_bits",
+    "TAG_KV", "KvCase", "kv_case", "KV_WORKLOAD",
 ]
 
 TAG_TARGET, TAG_DRAFT_NOISE, TAG_DRAFT_TOKENS, TAG_UNIFORMS = 0, 1, 2, 3
 TAG_SCORES, TAG_HIDDEN, TAG_HEAD_W = 4, 5, 6
+TAG_KV = 7
 
 # Numeric namespaces for the seed keys of the named workloads.
 WORKLOAD_IDS = {
@@ -40,6 +42,7 @@ WORKLOAD_IDS = {
     "b64_k4_v151936_bf16": 3,
     "b256_k7_v262144_bf16": 4,
     "shortlist_head_b32_k4_d4096_v128256": 5,
+    "kv_commit_b256_k7_p64_e1024_bf16": 6,
 }
 
 
@@ -235,3 +238,29 @@ def f32_from_bf16_bits(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
+
+
+# KV layout of a Llama-3-8B-like target: 32 layers x {key, value} planes,
+# 8 KV heads x 128 dims per token and plane, bf16; 128 cache positions.
+KV_WORKLOAD = dict(name="kv_commit_b256_k7_p64_e1024_bf16", P=64, B=256, K=7, Lmax=128, E=1024)
+
+
+@dataclasses.dataclass
+class KvCase:
+    cache: torch.Tensor      # [P, B, Lmax, E]
+    staging: torch.Tensor    # [P, B, K, E]
+    cache_len: torch.Tensor  # int32 [B]
+
+
+def kv_case(P, B, K, Lmax, E, dtype=torch.bfloat16, *, trial=0, device="cpu") -> KvCase:
+    """Synthetic KV cache and staging buffer: entries ~ N(0,1) in dtype; each
+    sequence's current length uniform on [0, Lmax - K] (room for any commit)."""
+    key = (0, 6, 0, TAG_KV, trial)
+    g = _gen(device, key)
+    cache = torch.empty((P, B, Lmax, E), dtype=dtype, device=device)
+    staging = torch.empty((P, B, K, E), dtype=dtype, device=device)
+    for p in range(P):
+        cache[p] = torch.randn((B, Lmax, E), generator=g, device=device, dtype=torch.float32).to(dtype)
+        staging[p] = torch.randn((B, K, E), generator=g, device=device, dtype=torch.float32).to(dtype)
+    ln = torch.randint(0, max(1, Lmax - K + 1), (B,), generator=g, device=device, dtype=torch.int64)
+    return KvCase(cache, staging, ln.to(torch.int32))

@@ -421,7 +421,77 @@ def bench_shortlist(args, dev):
                                f"{MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):.0f}: HBM-bound"},
         "cpu_baseline": None,
     }
+    out["sparse_draft"] = bench_sparse_draft(hc, target, uni, args.steps, args.warmup, dev)
     print(json.dumps(out), flush=True)
+
+
+def bench_sparse_draft(hc, target, uni, steps, warmup, dev):
+    """The same contexts with DynaSpec's position-aware budget (k_max = 16:
+    16, 16, 2, 2 clusters at positions 0..3): per-position head straight into
+    the compact layout (bf16), then spec_verify_sparse_draft, which reads the
+    compact draft instead of -inf-filled dense rows.  Draft tokens are sampled
+    from the compact draft (Gumbel-max on its dense form, outside the timed
+    region)."""
+    import numpy as np
+    import torch
+
+    import speculative_sampling_verification_vocab_amd as sv
+    from workloads import gumbel_max_tokens, normal_logits, top_clusters
+
+    B, K, d = hc.h.shape
+    V = hc.W.shape[0]
+    cs = hc.cluster_size
+    nc = V // cs
+    n_sel = [sv.position_budget(t, 16) for t in range(K)]
+    S = max(n_sel)
+    cids = torch.full((B, K, S), -1, dtype=torch.int32, device=dev)
+    for k in range(K):
+        cids[:, k, :n_sel[k]] = top_clusters(normal_logits((B, nc), 1.0, 0.0, (0, 5, 1, 4, k), dev), n_sel[k])
+    comp = sv.spec_draft_head_positions(hc.h, hc.W, cids, n_sel, cs)
+    dense = torch.full((B, K, V), float("-inf"), dtype=torch.bfloat16, device=dev)
+    for k in range(K):
+        ids = (cids[:, k, :n_sel[k]].long()[:, :, None] * cs + torch.arange(cs, device=dev)).reshape(B, -1)
+        dense[:, k].scatter_(1, ids, comp[:, k, :ids.shape[1]])
+    tok = gumbel_max_tokens(dense, 1.0, (0, 5, 1, 2, 0))
+    del dense
+    ws = sv.Workspace(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        cp = sv.spec_draft_head_positions(hc.h, hc.W, cids, n_sel, cs, out=comp)
+        if evs:
+            evs[1].record(stream)
+        r = sv.spec_verify_sparse_draft(target, cp, cids, n_sel, cs, tok, uni, 1.0, workspace=ws)
+        if evs:
+            evs[2].record(stream)
+        return r
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        res = step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e3 in evs:
+        step(e3)
+    torch.cuda.synchronize()
+    head_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    ver_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    short = int(sum(n_sel)) * cs
+    verify_bytes = B * (K + 1) * V * 2 + B * short * 2       # target rows + compact draft
+    dense_verify_bytes = B * (2 * K + 1) * V * 2
+    acc = res[0].float()
+    return {"n_sel_per_position": n_sel, "ms_per_step": ms, "value": B * (K + 1) / (ms * 1e-3),
+            "unit": "positions/s", "head_ms": head_ms, "verify_ms": ver_ms,
+            "verify_bytes": verify_bytes, "dense_verify_bytes_same_shape": dense_verify_bytes,
+            "verify_gbs": verify_bytes / (ver_ms * 1e-3) / 1e9,
+            "mean_shortlist_tokens": short / K,
+            "mean_tokens_per_verify": float((acc[acc >= 0] + 1).mean())}
 
 
 if __name__ == "__main__":

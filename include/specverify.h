@@ -149,6 +149,39 @@ spec_status_t spec_verify_timed(const void* target_logits, const void* draft_log
                                 void* const* events, int32_t n_events);
 
 /*
+ * Verify with a sparse draft (DynaSpec summary: the drafter's logits exist
+ * only on a shortlist, the union of the clusters selected for the context
+ * and position; verification keeps the full vocabulary and the exact rule).
+ * The rule, outputs, workspace (spec_verify_workspace_bytes with
+ * SPEC_MODE_SAMPLE) and errors are those of spec_verify in SAMPLE mode, with
+ * P_d at position i = softmax over position i's shortlist and 0 elsewhere.
+ * Reads B*K*L draft elements instead of B*K*V.
+ *
+ *   draft_compact  [B, K, L] of dtype: position i's logits on its shortlist in
+ *                  ascending token id (cluster_ids order, then id within the
+ *                  cluster); entries past n_sel[i] * cluster_size are ignored.
+ *   cluster_ids    [B, K, S] int32 (device): position i's cluster ids,
+ *                  strictly ascending in [0, V / cluster_size); the first
+ *                  n_sel[i] are used.  Not validated on the host: ids out of
+ *                  order give wrong draft values but no access outside the
+ *                  compact row.
+ *   n_sel          [K] int32 (HOST memory): clusters per position, the same
+ *                  for every sequence (for instance DynaSpec's position-aware
+ *                  budget), 1 <= n_sel[i] <= S and
+ *                  n_sel[i] * cluster_size <= min(L, V).
+ *   cluster_size   ids per cluster; V % cluster_size == 0.
+ * A draft token off its position's shortlist has P_d = 0 and is accepted.
+ */
+spec_status_t spec_verify_sparse_draft(const void* target_logits, const void* draft_compact,
+                                       const int32_t* cluster_ids, const int32_t* n_sel,
+                                       int32_t L, int32_t S, int32_t cluster_size,
+                                       const int32_t* draft_tokens, const float* uniforms,
+                                       int32_t B, int32_t K, int32_t V, spec_dtype_t dtype,
+                                       float temperature, int32_t* accepted_len, int32_t* out_tokens,
+                                       float* p_target_at_draft, float* p_draft_at_draft,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Shortlisted drafter head (DynaSpec summary, "Model architecture", items 1,
  * 3 and 4).  The vocabulary is split into V / cluster_size contiguous
  * clusters; cluster c holds ids [c*cluster_size, (c+1)*cluster_size).  Context
@@ -176,6 +209,29 @@ spec_status_t spec_draft_head_shortlist(const void* h, const void* W, const int3
                                         float* logits_compact, void* dense_out,
                                         spec_dtype_t dense_dtype,
                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Shortlisted drafter head with a shortlist per draft position (DynaSpec
+ * summary, "Model architecture" item 3: a position-aware budget selects
+ * k_c(t) clusters at draft position t).  Position k of context b uses the
+ * first n_sel[k] of cluster_ids[b, k, :]; its logits land in the compact
+ * layout spec_verify_sparse_draft reads.
+ *
+ *   h             bf16 [B, K, d]; W bf16 [V, d] row-major.
+ *   cluster_ids   int32 [B, K, S] (device): position k's first n_sel[k] ids
+ *                 strictly ascending in [0, V / cluster_size).
+ *   n_sel         [K] int32 (HOST memory), 0 <= n_sel[k] <= S and
+ *                 n_sel[k] * cluster_size <= L.
+ *   logits_compact [B, K, L] of compact_dtype out: position k's logits in
+ *                 ascending token id, fp32 accumulation (bf16 output rounds
+ *                 to nearest even); entries past n_sel[k] * cluster_size are
+ *                 not written.
+ * Errors: as spec_draft_head_shortlist; SPEC_ERR_UNSUPPORTED if B * K > 1024.
+ */
+spec_status_t spec_draft_head_positions(const void* h, const void* W, const int32_t* cluster_ids,
+                                        const int32_t* n_sel, int32_t B, int32_t K, int32_t d, int32_t V,
+                                        int32_t cluster_size, int32_t S, int32_t L, void* logits_compact,
+                                        spec_dtype_t compact_dtype, void* stream);
 
 /*
  * KV-cache commit after a verify step (Speculative Decoding lesson,

@@ -19,7 +19,7 @@ from . import _native
 from ._native import SpecVerifyError  # noqa: F401
 
 __all__ = ["spec_verify", "spec_verify_workspace_bytes", "spec_verify_launch_count", "spec_draft_head_shortlist",
-           "spec_kv_commit",
+           "spec_kv_commit", "spec_verify_sparse_draft", "position_budget", "spec_draft_head_positions",
            "Workspace", "SpecVerifyError", "abi_version"]
 
 _DTYPES = {torch.bfloat16: _native.SPEC_BF16, torch.float32: _native.SPEC_F32}
@@ -211,3 +211,104 @@ def spec_kv_commit(cache: torch.Tensor, staging: torch.Tensor, accepted_len: tor
                                        _ptr(status), P, B, K, Lmax, E, dt, _stream_handle(cache.device, stream))
     _native.check(st, "spec_kv_commit")
     return status
+
+
+def position_budget(t: int, k_max: int) -> int:
+    """Clusters selected for draft position t (0-based) under DynaSpec's
+    position-aware budget (DynaSpec summary, "Model architecture" item 3):
+    k_max for t in {0, 1}, floor(k_max / ((t + 1) * 2)) after that, and at
+    least one cluster so that every position keeps a shortlist."""
+    if t < 0 or k_max < 1:
+        raise ValueError("t >= 0 and k_max >= 1")
+    return k_max if t < 2 else max(1, k_max // ((t + 1) * 2))
+
+
+def spec_verify_sparse_draft(target: torch.Tensor, draft_compact: torch.Tensor, cluster_ids: torch.Tensor,
+                             n_sel, cluster_size: int, draft_tokens: torch.Tensor, uniforms: torch.Tensor,
+                             temperature: float = 1.0, *, return_probs: bool = False,
+                             workspace: Optional[Workspace] = None, stream=None):
+    """Speculative-sampling verify with a sparse draft (see spec_verify_sparse_draft in specverify.h).
+
+    target [B, K+1, V]; draft_compact [B, K, L] (same dtype) holding position
+    i's logits on its shortlist in ascending token id; cluster_ids int32
+    [B, K, S] (ascending, first n_sel[i] used); n_sel: K ints.  Returns what
+    spec_verify returns in sample mode."""
+    _need_gpu(target, "target")
+    if target.dim() != 3:
+        raise ValueError("target must be [B, K+1, V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dt = _DTYPES.get(target.dtype)
+    if dt is None:
+        raise ValueError("logits must be bfloat16 or float32")
+    if len(n_sel) != K:
+        raise ValueError("n_sel must have K entries")
+    ns = (ctypes.c_int32 * max(1, K))(*[int(x) for x in n_sel])
+    L = S = 1
+    if K > 0:
+        for t, name in ((draft_compact, "draft_compact"), (cluster_ids, "cluster_ids"),
+                        (draft_tokens, "draft_tokens")):
+            _need_gpu(t, name)
+        if draft_compact.dtype != target.dtype or draft_compact.dim() != 3 or draft_compact.shape[:2] != (B, K):
+            raise ValueError("draft_compact must be [B, K, L] with the target's dtype")
+        if cluster_ids.dtype != torch.int32 or cluster_ids.dim() != 3 or cluster_ids.shape[:2] != (B, K):
+            raise ValueError("cluster_ids must be int32 [B, K, S]")
+        if draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != (B, K):
+            raise ValueError("draft_tokens must be int32 [B, K]")
+        L, S = draft_compact.shape[2], cluster_ids.shape[2]
+        draft_compact, cluster_ids = draft_compact.contiguous(), cluster_ids.contiguous()
+    _need_gpu(uniforms, "uniforms")
+    if uniforms.dtype != torch.float32 or tuple(uniforms.shape) != (B, K + 1, 2):
+        raise ValueError("uniforms must be float32 [B, K+1, 2]")
+    lib = _native.load()
+    dev = target.device
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    pt = torch.empty((B, K), dtype=torch.float32, device=dev) if return_probs else None
+    pd = torch.empty((B, K), dtype=torch.float32, device=dev) if return_probs else None
+    need = lib.spec_verify_workspace_bytes(B, K, V, dt, _MODES["sample"])
+    ws = (workspace or _workspace_for(dev)).get(need)
+    st = lib.spec_verify_sparse_draft(_ptr(target), _ptr(draft_compact) if K > 0 else None,
+                                      _ptr(cluster_ids) if K > 0 else None, ns, L, S, int(cluster_size),
+                                      _ptr(draft_tokens) if K > 0 else None, _ptr(uniforms), B, K, V, dt,
+                                      ctypes.c_float(temperature), _ptr(acc), _ptr(out), _ptr(pt), _ptr(pd),
+                                      _ptr(ws), ws.numel(), _stream_handle(dev, stream))
+    _native.check(st, "spec_verify_sparse_draft")
+    return (acc, out, pt, pd) if return_probs else (acc, out)
+
+
+def spec_draft_head_positions(h: torch.Tensor, W: torch.Tensor, cluster_ids: torch.Tensor, n_sel,
+                              cluster_size: int, L: Optional[int] = None, dtype: torch.dtype = torch.bfloat16,
+                              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Drafter head with a shortlist per draft position (see spec_draft_head_positions in specverify.h).
+
+    h bf16 [B, K, d]; W bf16 [V, d]; cluster_ids int32 [B, K, S] (first n_sel[k]
+    ascending for position k); n_sel: K ints.  Returns compact logits
+    [B, K, L] of `dtype` (L defaults to S * cluster_size), the input that
+    spec_verify_sparse_draft takes."""
+    for t, name in ((h, "h"), (W, "W"), (cluster_ids, "cluster_ids")):
+        _need_gpu(t, name)
+    if h.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+        raise ValueError("h and W must be bfloat16")
+    B, K, d = h.shape
+    V = W.shape[0]
+    if cluster_ids.dtype != torch.int32 or cluster_ids.dim() != 3 or cluster_ids.shape[:2] != (B, K):
+        raise ValueError("cluster_ids must be int32 [B, K, S]")
+    if len(n_sel) != K:
+        raise ValueError("n_sel must have K entries")
+    S = cluster_ids.shape[2]
+    L = S * cluster_size if L is None else int(L)
+    dt = _DTYPES.get(dtype)
+    if dt is None:
+        raise ValueError("dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((B, K, L), dtype=dtype, device=h.device)
+    elif out.dtype != dtype or tuple(out.shape) != (B, K, L) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, K, L] tensor of dtype")
+    ns = (ctypes.c_int32 * max(1, K))(*[int(x) for x in n_sel])
+    st = _native.load().spec_draft_head_positions(_ptr(h.contiguous()), _ptr(W.contiguous()),
+                                                  _ptr(cluster_ids.contiguous()), ns, B, K, d, V,
+                                                  int(cluster_size), S, L, _ptr(out), dt,
+                                                  _stream_handle(h.device, stream))
+    _native.check(st, "spec_draft_head_positions")
+    return out

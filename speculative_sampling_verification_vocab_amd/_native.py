@@ -58,6 +58,11 @@ def load() -> ctypes.CDLL:
         lib.spec_draft_head_shortlist.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, P, P,
                                                   ctypes.c_int, P, sz, P]
         lib.spec_draft_head_shortlist.restype = ctypes.c_int
+        lib.spec_verify_sparse_draft.argtypes = [P, P, P, P, i32, i32, i32, P, P, i32, i32, i32, ctypes.c_int,
+                                                 ctypes.c_float, P, P, P, P, P, sz, P]
+        lib.spec_verify_sparse_draft.restype = ctypes.c_int
+        lib.spec_draft_head_positions.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, i32, P, ctypes.c_int, P]
+        lib.spec_draft_head_positions.restype = ctypes.c_int
         lib.spec_kv_commit.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_int, P]
         lib.spec_kv_commit.restype = ctypes.c_int
         _lib = lib

@@ -35,11 +35,18 @@ spec_status_t check_shape(int32_t B, int32_t K, int32_t V, spec_dtype_t dtype, s
   return SPEC_OK;
 }
 
+struct SparseDraft {
+  const int32_t* cids;
+  const int32_t* nsel;  // host
+  int L, S, cs;
+};
+
 spec_status_t verify_impl(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
                           const float* uniforms, int32_t B, int32_t K, int32_t V, spec_dtype_t dtype,
                           float temperature, spec_mode_t mode, int32_t* accepted_len, int32_t* out_tokens,
                           float* p_target_at_draft, float* p_draft_at_draft, void* workspace,
-                          size_t workspace_bytes, void* stream, void* const* events, int n_events) {
+                          size_t workspace_bytes, void* stream, void* const* events, int n_events,
+                          const SparseDraft* sparse = nullptr) {
   const spec_status_t sc = check_shape(B, K, V, dtype, mode);
   if (sc != SPEC_OK) return sc;
   const bool sample = sampling(mode);
@@ -61,7 +68,7 @@ spec_status_t verify_impl(const void* target_logits, const void* draft_logits, c
   const size_t esz = elem_size(dtype);
   const size_t vec = 16 / esz;
   bool aligned = ((size_t)V % vec == 0) && ((uintptr_t)target_logits % 16 == 0);
-  if (sample && K > 0) aligned = aligned && ((uintptr_t)draft_logits % 16 == 0);
+  if (sample && K > 0 && !sparse) aligned = aligned && ((uintptr_t)draft_logits % 16 == 0);
   const sv::VerifyShape s = sv::make_shape(B, K, V, dtype == SPEC_BF16 ? 1 : 0, aligned);
 
   const size_t need = sv::verify_workspace_layout(s, (int)mode, nullptr, nullptr);
@@ -79,6 +86,13 @@ spec_status_t verify_impl(const void* target_logits, const void* draft_logits, c
   io.out_tokens = out_tokens;
   io.p_target = p_target_at_draft;
   io.p_draft = p_draft_at_draft;
+  if (sparse && K > 0) {
+    io.cids = sparse->cids;
+    io.nsel = sparse->nsel;
+    io.L = sparse->L;
+    io.S = sparse->S;
+    io.cs = sparse->cs;
+  }
 
   (void)hipGetLastError();  // clear a stale error so the checks below see only ours
   hipError_t e = hipSuccess;
@@ -139,6 +153,33 @@ spec_status_t spec_verify_timed(const void* target_logits, const void* draft_log
                      stream, events, n_events);
 }
 
+spec_status_t spec_verify_sparse_draft(const void* target_logits, const void* draft_compact,
+                                       const int32_t* cluster_ids, const int32_t* n_sel, int32_t L, int32_t S,
+                                       int32_t cluster_size, const int32_t* draft_tokens, const float* uniforms,
+                                       int32_t B, int32_t K, int32_t V, spec_dtype_t dtype, float temperature,
+                                       int32_t* accepted_len, int32_t* out_tokens, float* p_target_at_draft,
+                                       float* p_draft_at_draft, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  const spec_status_t sc = check_shape(B, K, V, dtype, SPEC_MODE_SAMPLE);
+  if (sc != SPEC_OK) return sc;
+  if (B > 0 && K > 0) {
+    if (!cluster_ids || !n_sel || cluster_size < 1 || L < 1 || S < 1) return SPEC_ERR_INVALID_ARG;
+    if (V % cluster_size != 0) return SPEC_ERR_UNSUPPORTED;
+    if (S > V / cluster_size) return SPEC_ERR_INVALID_ARG;
+    if ((size_t)B * (size_t)K * (size_t)L > SIZE_MAX / 8 || (size_t)B * (size_t)K * (size_t)S > SIZE_MAX / 8)
+      return SPEC_ERR_INVALID_ARG;
+    for (int i = 0; i < K; ++i) {
+      if (n_sel[i] < 1 || n_sel[i] > S) return SPEC_ERR_INVALID_ARG;
+      const long long len = (long long)n_sel[i] * cluster_size;
+      if (len > L || len > V) return SPEC_ERR_INVALID_ARG;
+    }
+  }
+  const SparseDraft sp{cluster_ids, n_sel, L, S, cluster_size};
+  return verify_impl(target_logits, draft_compact, draft_tokens, uniforms, B, K, V, dtype, temperature,
+                     SPEC_MODE_SAMPLE, accepted_len, out_tokens, p_target_at_draft, p_draft_at_draft, workspace,
+                     workspace_bytes, stream, nullptr, 0, &sp);
+}
+
 int32_t spec_verify_launch_count(int32_t B, int32_t K, int32_t V, spec_dtype_t dtype, spec_mode_t mode) {
   if (check_shape(B, K, V, dtype, mode) != SPEC_OK || B == 0) return 0;
   if (mode == SPEC_MODE_GREEDY) return 2;
@@ -163,6 +204,28 @@ spec_status_t spec_draft_head_shortlist(const void* h, const void* W, const int3
   (void)hipGetLastError();
   const hipError_t e = sv::launch_head(h, W, cluster_ids, B, K, d, V, cluster_size, n_sel, logits_compact,
                                        dense_out, dense_dtype == SPEC_BF16 ? 1 : 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+spec_status_t spec_draft_head_positions(const void* h, const void* W, const int32_t* cluster_ids,
+                                        const int32_t* n_sel, int32_t B, int32_t K, int32_t d, int32_t V,
+                                        int32_t cluster_size, int32_t S, int32_t L, void* logits_compact,
+                                        spec_dtype_t compact_dtype, void* stream) {
+  if (B < 0 || K < 0 || d < 1 || V < 1 || cluster_size < 1 || S < 1 || L < 1) return SPEC_ERR_INVALID_ARG;
+  if (!valid_dtype(compact_dtype)) return SPEC_ERR_INVALID_ARG;
+  if (V % cluster_size != 0) return SPEC_ERR_UNSUPPORTED;
+  if (B == 0 || K == 0) return SPEC_OK;
+  if (K > SPEC_MAX_K || (size_t)B * K > (size_t)sv::head_max_contexts() || S > 0xffff) return SPEC_ERR_UNSUPPORTED;
+  if (S > V / cluster_size || (size_t)B * K * (size_t)S > 0x7fffffffu || (size_t)B * K * (size_t)L > SIZE_MAX / 8)
+    return SPEC_ERR_INVALID_ARG;
+  if (!h || !W || !cluster_ids || !n_sel || !logits_compact) return SPEC_ERR_INVALID_ARG;
+  for (int i = 0; i < K; ++i)
+    if (n_sel[i] < 0 || n_sel[i] > S || (long long)n_sel[i] * cluster_size > L) return SPEC_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  // every (context, position) is a context of its own with one row
+  const hipError_t e = sv::launch_head(h, W, cluster_ids, B * K, 1, d, V, cluster_size, 0, logits_compact, nullptr,
+                                       0, static_cast<hipStream_t>(stream), n_sel, K, S, L,
+                                       compact_dtype == SPEC_BF16 ? 1 : 0);
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 

@@ -37,10 +37,15 @@ struct HeadArgs {
   const uint16_t* W;    // bf16 [V, d]
   const int32_t* cids;  // [B, n_sel]
   int B, K, d, V, cs, n_sel;
-  float* compact;       // [B, K, n_sel*cs] or null
+  void* compact;        // [B, K, L] fp32 (or bf16 with compact_bf16) or null
+  int compact_bf16;
   void* dense;          // [B, K, V] or null
   int dense_bf16;
   int vec_ok;           // d % 8 == 0 and h, W 16-byte aligned: 16-byte row loads
+  int S;                // entries per row of cids (n_sel for one shortlist per context)
+  int L;                // compact row stride
+  int nsel_period;      // 0: every context uses n_sel; else context x uses nsel_pos[x % period]
+  int nsel_pos[kMaxK];
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -82,10 +87,11 @@ __global__ void __launch_bounds__(kBlock) head_mfma_kernel(HeadArgs a) {
   if (threadIdx.x == 0) sh_count = 0;
   for (int i = threadIdx.x; i < kMaxCtx / 32; i += kBlock) sh_sel[i] = 0u;
   __syncthreads();
-  const int entries = a.B * a.n_sel;
+  const int entries = a.B * a.S;
   for (int e0 = 0; e0 < entries; e0 += kBlock) {
     const int e = e0 + threadIdx.x;
-    const bool hit = e < entries && a.cids[e] == c;
+    const int used = a.nsel_period ? a.nsel_pos[(e / a.S) % a.nsel_period] : a.n_sel;
+    const bool hit = e < entries && e % a.S < used && a.cids[e] == c;
     const uint64_t mask = __ballot(hit);
     if (lane == 0) sh_wcount[wave] = __popcll(mask);
     __syncthreads();
@@ -96,7 +102,7 @@ __global__ void __launch_bounds__(kBlock) head_mfma_kernel(HeadArgs a) {
     }
     if (hit) {
       const int pos = before + __popcll(mask & ((1ull << lane) - 1ull));
-      const int b = e / a.n_sel, s = e % a.n_sel;
+      const int b = e / a.S, s = e % a.S;
       if (pos < kMaxCtx) sh_ctx[pos] = (b << 16) | s;
       atomicOr(&sh_sel[b >> 5], 1u << (b & 31));
     }
@@ -105,7 +111,7 @@ __global__ void __launch_bounds__(kBlock) head_mfma_kernel(HeadArgs a) {
     __syncthreads();
   }
   const int nctx = min(sh_count, kMaxCtx);
-  const int K = a.K, L = a.n_sel * a.cs;
+  const int K = a.K, L = a.L;
 
   // 2. -inf for every (context, position) that did not select c.
   if (a.dense) {
@@ -207,7 +213,11 @@ __global__ void __launch_bounds__(kBlock) head_mfma_kernel(HeadArgs a) {
               const int b = ctx >> 16, s = ctx & 0xffff, k = rr % K;
               const float v = acc[mc][i];
               const size_t bk = (size_t)b * K + k;
-              if (a.compact) a.compact[bk * L + (size_t)s * a.cs + tok_in0 + my_tok] = v;
+              if (a.compact) {
+                const size_t o = bk * L + (size_t)s * a.cs + tok_in0 + my_tok;
+                if (a.compact_bf16) static_cast<uint16_t*>(a.compact)[o] = f32_to_bf16_rne(v);
+                else static_cast<float*>(a.compact)[o] = v;
+              }
               if (a.dense) store_dense(a, bk * a.V + tok0 + my_tok, v);
             }
           }
@@ -220,7 +230,8 @@ __global__ void __launch_bounds__(kBlock) head_mfma_kernel(HeadArgs a) {
 }  // namespace
 
 hipError_t launch_head(const void* h, const void* W, const int32_t* cluster_ids, int B, int K, int d, int V,
-                       int cluster_size, int n_sel, float* compact, void* dense, int dense_dtype, hipStream_t st) {
+                       int cluster_size, int n_sel, void* compact, void* dense, int dense_dtype, hipStream_t st,
+                       const int32_t* nsel_pos, int nsel_period, int S, int L, int compact_dtype) {
   HeadArgs a{};
   a.h = static_cast<const uint16_t*>(h);
   a.W = static_cast<const uint16_t*>(W);
@@ -232,9 +243,14 @@ hipError_t launch_head(const void* h, const void* W, const int32_t* cluster_ids,
   a.cs = cluster_size;
   a.n_sel = n_sel;
   a.compact = compact;
+  a.compact_bf16 = compact_dtype == 1;
   a.dense = dense;
   a.dense_bf16 = dense_dtype == 1;
   a.vec_ok = (d % 8 == 0) && ((uintptr_t)h % 16 == 0) && ((uintptr_t)W % 16 == 0);
+  a.S = nsel_pos ? S : n_sel;
+  a.L = nsel_pos ? L : n_sel * cluster_size;
+  a.nsel_period = nsel_pos ? nsel_period : 0;
+  for (int i = 0; nsel_pos && i < nsel_period; ++i) a.nsel_pos[i] = nsel_pos[i];
   const int n_clusters = V / cluster_size;
   const dim3 grid((unsigned)n_clusters, (unsigned)((cluster_size + kSlabTok - 1) / kSlabTok));
   hipLaunchKernelGGL(head_mfma_kernel, grid, dim3(kBlock), 0, st, a);

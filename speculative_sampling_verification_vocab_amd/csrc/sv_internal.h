@@ -65,6 +65,10 @@ struct VerifyIO {
   int32_t* out_tokens;
   float* p_target;
   float* p_draft;
+  // sparse draft (null cids: dense draft rows)
+  const int32_t* cids;  // [B][K][S]
+  int L, S, cs;
+  const int32_t* nsel;  // host [K]
 };
 
 int tile_elems(int dtype);
@@ -89,9 +93,13 @@ hipError_t launch_greedy(const VerifyShape& s, const VerifyIO& io, const VerifyW
 hipError_t launch_greedy_finalize(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws,
                                   hipStream_t st);
 
+// nsel_pos (host, nsel_period entries) set: context x uses the first
+// nsel_pos[x % nsel_period] of its S cluster ids and writes compact rows of
+// stride L; otherwise every context uses n_sel ids and rows of n_sel * cs.
 hipError_t launch_head(const void* h, const void* W, const int32_t* cluster_ids, int B, int K, int d, int V,
-                       int cluster_size, int n_sel, float* compact, void* dense, int dense_dtype,
-                       hipStream_t st);
+                       int cluster_size, int n_sel, void* compact, void* dense, int dense_dtype,
+                       hipStream_t st, const int32_t* nsel_pos = nullptr, int nsel_period = 0, int S = 0,
+                       int L = 0, int compact_dtype = 0);
 int head_max_contexts();
 
 // KV-cache commit: copy, then lengths and status (two launches).

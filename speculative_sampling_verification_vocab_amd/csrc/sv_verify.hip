@@ -70,6 +70,13 @@ struct VerifyArgs {
   SampleTile* part_b;    // [B][NTs]
   float* gx;             // [B][2K] logits at the draft tokens (written by the statistics pass)
   int32_t* cont;         // [K][B] early exit only
+  // Sparse draft rows (null cids: dense [B][K][V] draft rows).  Position i's
+  // draft logits exist on the union of its nsel[i] clusters of cs ids and are
+  // stored compactly, [B][K][L], in ascending token id.
+  const int32_t* cids;   // [B][K][S] cluster ids per position, ascending
+  int L, S, cs;
+  int compact_vec;       // compact rows 16-byte aligned with L a whole number of vectors
+  int nsel[kMaxK];
   int32_t* accepted_len;
   int32_t* out_tokens;
   float* p_t_out;
@@ -79,6 +86,114 @@ struct VerifyArgs {
 template <typename T>
 __device__ __forceinline__ const T* row_ptr(const void* base, size_t rows_before, int V) {
   return static_cast<const T*>(base) + rows_before * (size_t)V;
+}
+
+// ---------------------------------------------------------------------------
+// Sparse draft rows.
+// ---------------------------------------------------------------------------
+
+// Rank of cluster c among position i's clusters of sequence b, or -1.  Binary
+// search over the ascending ids; ids that are not ascending give wrong ranks
+// but never an index outside the row.
+__device__ __forceinline__ int sparse_rank(const VerifyArgs& a, int b, int i, int c) {
+  const int32_t* ids = a.cids + ((size_t)b * a.K + i) * a.S;
+  int lo = 0, hi = a.nsel[i] - 1;
+  while (lo <= hi) {
+    const int mid = (lo + hi) >> 1;
+    const int v = ids[mid];
+    if (v == c) return mid;
+    if (v < c) lo = mid + 1;
+    else hi = mid - 1;
+  }
+  return -1;
+}
+
+// Index of token v in the compact draft row (b, i), or -1 off the shortlist.
+__device__ __forceinline__ int sparse_index(const VerifyArgs& a, int b, int i, int v) {
+  if (v < 0 || v >= a.V) return -1;
+  const int c = v / a.cs;
+  const int r = sparse_rank(a, b, i, c);
+  return r < 0 ? -1 : r * a.cs + (v - c * a.cs);
+}
+
+// Storage bits of the draft logits at ids v0 .. v0 + kVec - 1 of row (b, i):
+// the compact entry where the id is on the shortlist, -inf elsewhere.
+// Rank lookups go through `tab` (rank of every cluster of the row, in LDS)
+// when the caller built one, else through sparse_rank.
+constexpr int kRankTab = 4096;  // clusters an LDS rank table covers (8 KiB)
+
+__device__ __forceinline__ int rank_of(const VerifyArgs& a, int b, int i, int c, const int16_t* tab) {
+  return tab ? (int)tab[c] : sparse_rank(a, b, i, c);
+}
+
+// Fill tab (kRankTab entries of LDS) with the rank of every cluster in
+// position i's shortlist of sequence b, -1 elsewhere.  Whole block; returns
+// tab, or nullptr when the vocabulary has more clusters than the table holds.
+__device__ __forceinline__ const int16_t* build_rank_tab(const VerifyArgs& a, int b, int i, int16_t* tab) {
+  const int nc = a.V / a.cs;
+  if (nc > kRankTab) return nullptr;
+  for (int c = threadIdx.x; c < nc; c += kBlock) tab[c] = -1;
+  __syncthreads();
+  const int32_t* ids = a.cids + ((size_t)b * a.K + i) * a.S;
+  for (int r = threadIdx.x; r < a.nsel[i]; r += kBlock) {
+    const int c = ids[r];
+    if (c >= 0 && c < nc) tab[c] = (int16_t)r;
+  }
+  __syncthreads();
+  return tab;
+}
+
+template <typename T>
+__device__ __forceinline__ void sparse_group_bits(const VerifyArgs& a, int b, int i, int v0,
+                                                  uint32_t (&bits)[Elem<T>::kVec], const int16_t* tab = nullptr) {
+  constexpr int V8 = Elem<T>::kVec;
+  constexpr uint32_t kNinf = sizeof(T) == 2 ? 0xff80u : 0xff800000u;
+  const T* crow = static_cast<const T*>(a.draft) + ((size_t)b * a.K + i) * (size_t)a.L;
+  int c = v0 < a.V ? v0 / a.cs : 0, r = v0 < a.V ? rank_of(a, b, i, c, tab) : -1;
+#pragma unroll
+  for (int q = 0; q < V8; ++q) {
+    const int v = v0 + q;
+    bits[q] = kNinf;
+    if (v < a.V) {
+      if (v - c * a.cs >= a.cs) {  // the group crossed into the next cluster
+        c = v / a.cs;
+        r = rank_of(a, b, i, c, tab);
+      }
+      if (r >= 0) {
+        const T x = crow[r * a.cs + (v - c * a.cs)];
+        if constexpr (sizeof(T) == 2) bits[q] = (uint32_t)x;
+        else bits[q] = __float_as_uint(x);
+      }
+    }
+  }
+}
+
+// The lane's slice of sampling tile t of draft row (b, i) in load_raw's packed form.
+template <typename T, int NL>
+__device__ __forceinline__ void sparse_tile_raw(const VerifyArgs& a, int b, int i, int t, int lane, u32x4 (&raw)[NL],
+                                                const int16_t* tab) {
+  constexpr int V8 = Elem<T>::kVec;
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    uint32_t bits[V8];
+    sparse_group_bits<T>(a, b, i, t * kTileS<T> + j * (kWave * V8) + lane * V8, bits, tab);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (sizeof(T) == 2) raw[j][q] = bits[2 * q] | (bits[2 * q + 1] << 16);
+      else raw[j][q] = bits[q];
+    }
+  }
+}
+
+// Load `first` of sampling tile t of draft row (b, i) as floats (load_tile's element order).
+template <typename T>
+__device__ __forceinline__ void sparse_tile_load(const VerifyArgs& a, int b, int i, int t, int lane, int first,
+                                                 float (&x)[Elem<T>::kVec], const int16_t* tab) {
+  constexpr int V8 = Elem<T>::kVec;
+  uint32_t bits[V8];
+  sparse_group_bits<T>(a, b, i, t * kTileS<T> + first * (kWave * V8) + lane * V8, bits, tab);
+#pragma unroll
+  for (int q = 0; q < V8; ++q) x[q] = sizeof(T) == 2 ? __uint_as_float(bits[q] << 16) : __uint_as_float(bits[q]);
 }
 
 // ---------------------------------------------------------------------------
@@ -112,16 +227,57 @@ __device__ __forceinline__ void stats_tile(const VerifyArgs& a, const float (&x)
 // r, else draft row r - K): one tile per wave, all of its loads issued at
 // once.  (Several tiles per wave with the next one loaded during the
 // reduction measured 2-6 % slower: the extra registers cost occupancy.)
-template <typename T, bool kAligned>
+template <typename T, bool kAligned, bool kSparse = false>
 __device__ __forceinline__ void stats_row_block(const VerifyArgs& a, int b, int r, int g) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int K = a.K, R = 2 * K;
-  const T* row = r < K ? row_ptr<T>(a.target, (size_t)b * (K + 1) + r, a.V)
-                       : row_ptr<T>(a.draft, (size_t)b * K + (r - K), a.V);
   const int t = g * kWavesPerBlock + wave;
   // The drafted token of this row: the wave whose tile holds it also records
   // its logit (re-read from cache) for the accept test.
   const int d = a.tokens[(size_t)b * K + (r < K ? r : r - K)];
+  if (kSparse && r >= K) {
+    // Sparse draft row: the compact row of position r - K.
+    const int i = r - K;
+    const T* row = static_cast<const T*>(a.draft) + ((size_t)b * K + i) * (size_t)a.L;
+    const int len = a.nsel[i] * a.cs;
+    if (t >= a.NT) return;
+    TileStat* out = a.part_a + ((size_t)b * R + r) * a.NT + t;
+    if (t * kTile<T> >= len) {
+      if (lane == 0) *out = TileStat{kNegInf, 0.0f};  // past the compact row
+    } else {
+      float x[kPerLane<T>];
+      if (a.compact_vec) {
+        // 16-byte loads up to len rounded up to a vector (inside the L-long
+        // row), then ids past len masked
+        constexpr int V8 = Elem<T>::kVec;
+        load_tile<T, true, kLoads>(row, (len + V8 - 1) / V8 * V8, t, lane, x);
+        if ((t + 1) * kTile<T> > len) {
+#pragma unroll
+          for (int e = 0; e < kPerLane<T>; ++e)
+            if (t * kTile<T> + tile_offset<T>(e, lane) >= len) x[e] = kNegInf;
+        }
+      } else {
+        load_tile<T, false, kLoads>(row, len, t, lane, x);
+      }
+      stats_tile<T>(a, x, out);
+    }
+    if (t == 0) {
+      // The logit at the draft token: its cluster's rank by a wave-wide
+      // comparison with the position's cluster ids (one memory round trip).
+      const int c = d >= 0 && d < a.V ? d / a.cs : -1;
+      const int32_t* ids = a.cids + ((size_t)b * K + i) * a.S;
+      int rank = -1;
+      for (int base = 0; base < a.nsel[i] && rank < 0; base += kWave) {
+        const bool hit = base + lane < a.nsel[i] && c >= 0 && ids[base + lane] == c;
+        const uint64_t m = __ballot(hit);
+        if (m) rank = base + (int)__builtin_ctzll(m);
+      }
+      if (lane == 0) a.gx[(size_t)b * R + r] = rank >= 0 ? to_f32(row[rank * a.cs + (d - c * a.cs)]) : kNegInf;
+    }
+    return;
+  }
+  const T* row = r < K ? row_ptr<T>(a.target, (size_t)b * (K + 1) + r, a.V)
+                       : row_ptr<T>(a.draft, (size_t)b * K + (r - K), a.V);
   if (t < a.NT) {
     float x[kPerLane<T>];
     load_tile<T, kAligned, kLoads>(row, a.V, t, lane, x);
@@ -131,11 +287,11 @@ __device__ __forceinline__ void stats_row_block(const VerifyArgs& a, int b, int 
 }
 
 // Block `blk` of the statistics pass over every row 0..K-1 of target and draft.
-template <typename T, bool kAligned>
+template <typename T, bool kAligned, bool kSparse = false>
 __device__ __forceinline__ void stats_block(const VerifyArgs& a, int blk) {
   const int R = 2 * a.K;
   const int rb = blk / a.NG;
-  stats_row_block<T, kAligned>(a, rb / R, rb % R, blk % a.NG);
+  stats_row_block<T, kAligned, kSparse>(a, rb / R, rb % R, blk % a.NG);
 }
 
 // ---------------------------------------------------------------------------
@@ -455,7 +611,7 @@ __device__ __forceinline__ void bonus_tile(const VerifyArgs& a, int b, int t, co
 // Block `blk` of the sampling pass.
 // kFromRows: n and the row record come from the early-exit decisions
 // (a.rows) instead of this block's own accept prologue.
-template <typename T, bool kAligned, bool kFromRows = false>
+template <typename T, bool kAligned, bool kFromRows = false, bool kSparse = false>
 __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int K = a.K;
@@ -482,7 +638,7 @@ __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
   if (n < 0) return;  // faulty sequence: outputs already written
   const bool resid = n < K;
   const T* trow = row_ptr<T>(a.target, (size_t)b * (K + 1) + n, a.V);
-  const T* drow = resid ? row_ptr<T>(a.draft, (size_t)b * K + n, a.V) : trow;
+  const T* drow = resid && !kSparse ? row_ptr<T>(a.draft, (size_t)b * K + n, a.V) : trow;
   constexpr int NL = kLoadsS;
   // The block covers TPWs * 4 consecutive tiles, interleaved over its waves
   // so that the four waves read neighbouring tiles at the same time.  A tile
@@ -490,6 +646,11 @@ __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
   // on the SIMD cover a tile's load latency.  Loading the next tile ahead
   // measured slower: the extra registers cost two waves of occupancy.
   auto tile_of = [&](int j) { return (g * a.TPWs + j) * kWavesPerBlock + wave; };
+  const int16_t* tab = nullptr;
+  if constexpr (kSparse) {
+    __shared__ int16_t sh_tab[kRankTab];
+    if (resid) tab = build_rank_tab(a, b, n, sh_tab);  // resid is uniform over the block
+  }
   if (tile_of(0) >= a.NTs) return;
   // Residual: lane l holds the references and the ratio of statistics tile T0 + l.
   const int T0 = g * a.TPWs * kWavesPerBlock / kSubTiles<T>;
@@ -497,7 +658,8 @@ __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
   if (resid && lane < a.TPWs * kWavesPerBlock / kSubTiles<T> && T0 + lane < a.NT) {
     const size_t R = 2 * (size_t)K;
     ref_t = a.part_a[((size_t)b * R + n) * a.NT + T0 + lane].m;
-    ref_d = a.part_a[((size_t)b * R + K + n) * a.NT + T0 + lane].m;
+    // a sparse draft row has no dense tiles: its row maximum is the reference
+    ref_d = kSparse ? sr.m_d : a.part_a[((size_t)b * R + K + n) * a.NT + T0 + lane].m;
     rho_l = tile_rho(ref_t, ref_d, sr, a.s64);
   }
   for (int j = 0; j < a.TPWs; ++j) {
@@ -506,7 +668,8 @@ __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
     u32x4 cx[NL], cy[NL];
     load_raw<T, kAligned, kLoadsS>(trow, a.V, t, lane, cx);
     if (resid) {
-      load_raw<T, kAligned, kLoadsS>(drow, a.V, t, lane, cy);
+      if constexpr (kSparse) sparse_tile_raw<T>(a, b, n, t, lane, cy, tab);
+      else load_raw<T, kAligned, kLoadsS>(drow, a.V, t, lane, cy);
       const int lt = t / kSubTiles<T> - T0;
       residual_tile<T>(a, b, t, lane_value(ref_t, lt), lane_value(ref_d, lt), lane_value(rho_l, lt), cx, cy);
     } else {
@@ -575,7 +738,7 @@ __device__ __forceinline__ void block_min2(int& x, int& y, int* sh) {
 // The tile sums of the sequence (one per thread for up to 256 tiles) and the
 // sample uniforms are loaded together with the row record, so the block waits
 // for one memory round trip before the tile choice and one for the tile.
-template <typename T, bool kAligned>
+template <typename T, bool kAligned, bool kSparse = false>
 __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
   __shared__ double sh_d[2 * kWavesPerBlock];
   __shared__ float sh_f[2 * kWavesPerBlock];
@@ -689,13 +852,21 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
   // ids).  The tile maxima and every element value are recomputed exactly as
   // the tile pass computed them.
   const T* trow = row_ptr<T>(a.target, (size_t)b * (K + 1) + n, a.V);
-  const T* drow = resid ? row_ptr<T>(a.draft, (size_t)b * K + n, a.V) : nullptr;
+  const T* drow = resid && !kSparse ? row_ptr<T>(a.draft, (size_t)b * K + n, a.V) : nullptr;
   constexpr int V8 = Elem<T>::kVec;
   static_assert(kLoadsS == kWavesPerBlock, "one load of the tile per wave");
   const bool use_d = resid && !fallback;
+  const int16_t* sh_tab = nullptr;
+  if constexpr (kSparse) {
+    __shared__ int16_t sh_rank[kRankTab];
+    if (use_d) sh_tab = build_rank_tab(a, b, n, sh_rank);  // use_d is uniform over the block
+  }
   float x[V8], y[V8], e[V8], f[V8];
   load_tile<T, kAligned, kLoadsS>(trow, a.V, jstar, lane, x, wave);
-  if (use_d) load_tile<T, kAligned, kLoadsS>(drow, a.V, jstar, lane, y, wave);
+  if (use_d) {
+    if constexpr (kSparse) sparse_tile_load<T>(a, b, n, jstar, lane, wave, y, sh_tab);
+    else load_tile<T, kAligned, kLoadsS>(drow, a.V, jstar, lane, y, wave);
+  }
   // Exponent references exactly as the sampling pass took them: the
   // statistics tile maxima for a rejected position, the tile's own maximum
   // for the bonus row.
@@ -704,7 +875,7 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
     const size_t R = 2 * (size_t)K;
     const int ts = jstar / kSubTiles<T>;
     mt = a.part_a[((size_t)b * R + n) * a.NT + ts].m;
-    md = a.part_a[((size_t)b * R + K + n) * a.NT + ts].m;
+    md = kSparse ? sr.m_d : a.part_a[((size_t)b * R + K + n) * a.NT + ts].m;
   } else {
     mt = lane_max(x);
     float unused = kNegInf;
@@ -758,19 +929,21 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
   }
 }
 
-template <typename T, bool kAligned>
+// (Forcing six waves per SIMD here, at most 80 VGPRs, spills one register to
+// scratch and measured 16 % slower than the compiler's five.)
+template <typename T, bool kAligned, bool kSparse = false>
 __global__ void __launch_bounds__(kBlock) stats_kernel(VerifyArgs a) {
-  stats_block<T, kAligned>(a, blockIdx.x);
+  stats_block<T, kAligned, kSparse>(a, blockIdx.x);
 }
 
-template <typename T, bool kAligned>
+template <typename T, bool kAligned, bool kSparse = false>
 __global__ void __launch_bounds__(kBlock) sample_kernel(VerifyArgs a) {
-  sample_block<T, kAligned>(a, blockIdx.x);
+  sample_block<T, kAligned, false, kSparse>(a, blockIdx.x);
 }
 
-template <typename T, bool kAligned>
+template <typename T, bool kAligned, bool kSparse = false>
 __global__ void __launch_bounds__(kBlock) pick_kernel(VerifyArgs a) {
-  pick_block<T, kAligned>(a, blockIdx.x);
+  pick_block<T, kAligned, kSparse>(a, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1020,6 +1193,14 @@ static VerifyArgs verify_args(const VerifyShape& s, const VerifyIO& io, const Ve
   a.part_b = ws.part_b;
   a.gx = ws.gx;
   a.cont = ws.cont;
+  a.cids = io.cids;
+  if (io.cids) {
+    a.L = io.L;
+    a.S = io.S;
+    a.cs = io.cs;
+    a.compact_vec = (io.L % (s.dtype == 1 ? 8 : 4) == 0) && ((uintptr_t)io.draft % 16 == 0);
+    for (int i = 0; i < s.K; ++i) a.nsel[i] = io.nsel[i];
+  }
   a.accepted_len = io.accepted_len;
   a.out_tokens = io.out_tokens;
   a.p_t_out = io.p_target;
@@ -1029,14 +1210,9 @@ static VerifyArgs verify_args(const VerifyShape& s, const VerifyIO& io, const Ve
 
 int sample_launches(const VerifyShape& s) { return s.B == 0 ? 0 : 3; }
 
-// Three dedicated kernels.  (Splitting the batch into groups and running the
-// statistics of one group in the same launch as the sampling of the previous
-// one measured 0-2 % faster at best: both passes are VALU-heavy, so running
-// them side by side gains little over running them back to back.)
-hipError_t launch_sample_pipeline(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws,
-                                  hipStream_t st, void* const* events, int n_events) {
-  if (s.B == 0) return hipSuccess;
-  const VerifyArgs a = verify_args(s, io, ws);
+template <bool kSparse>
+static hipError_t sample_pipeline(const VerifyShape& s, const VerifyArgs& a, hipStream_t st, void* const* events,
+                                  int n_events) {
   int k = 0;
   auto record = [&]() {
     if (events && k < n_events && events[k]) (void)hipEventRecord(static_cast<hipEvent_t>(events[k]), st);
@@ -1046,18 +1222,34 @@ hipError_t launch_sample_pipeline(const VerifyShape& s, const VerifyIO& io, cons
   record();
   if (s.K > 0)
     e = dispatch4(s.dtype, s.aligned, dim3((unsigned)((size_t)s.B * 2 * s.K * s.NG)), st,
-                  stats_kernel<uint16_t, true>, stats_kernel<uint16_t, false>, stats_kernel<float, true>,
-                  stats_kernel<float, false>, a);
+                  stats_kernel<uint16_t, true, kSparse>, stats_kernel<uint16_t, false, kSparse>,
+                  stats_kernel<float, true, kSparse>, stats_kernel<float, false, kSparse>, a);
   record();
   if (e == hipSuccess)
-    e = dispatch4(s.dtype, s.aligned, dim3((unsigned)((size_t)s.B * s.NG_s)), st, sample_kernel<uint16_t, true>,
-                  sample_kernel<uint16_t, false>, sample_kernel<float, true>, sample_kernel<float, false>, a);
+    e = dispatch4(s.dtype, s.aligned, dim3((unsigned)((size_t)s.B * s.NG_s)), st,
+                  sample_kernel<uint16_t, true, kSparse>, sample_kernel<uint16_t, false, kSparse>,
+                  sample_kernel<float, true, kSparse>, sample_kernel<float, false, kSparse>, a);
   record();
   if (e == hipSuccess)
-    e = dispatch4(s.dtype, s.aligned, dim3((unsigned)s.B), st, pick_kernel<uint16_t, true>,
-                  pick_kernel<uint16_t, false>, pick_kernel<float, true>, pick_kernel<float, false>, a);
+    e = dispatch4(s.dtype, s.aligned, dim3((unsigned)s.B), st, pick_kernel<uint16_t, true, kSparse>,
+                  pick_kernel<uint16_t, false, kSparse>, pick_kernel<float, true, kSparse>,
+                  pick_kernel<float, false, kSparse>, a);
   record();
   return e;
+}
+
+// Three dedicated kernels.  (Splitting the batch into groups and running the
+// statistics of one group in the same launch as the sampling of the previous
+// one measured 0-2 % faster at best: both passes are VALU-heavy, so running
+// them side by side gains little over running them back to back.)  A sparse
+// draft (io.cids set) uses the same three kernels compiled for compact draft
+// rows.
+hipError_t launch_sample_pipeline(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws,
+                                  hipStream_t st, void* const* events, int n_events) {
+  if (s.B == 0) return hipSuccess;
+  const VerifyArgs a = verify_args(s, io, ws);
+  return io.cids ? sample_pipeline<true>(s, a, st, events, n_events)
+                 : sample_pipeline<false>(s, a, st, events, n_events);
 }
 
 int early_exit_launches(const VerifyShape& s) { return s.B == 0 ? 0 : s.K + 2; }

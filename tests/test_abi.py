@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("spec_verify", "spec_verify_timed", "spec_verify_workspace_bytes",
-              "spec_draft_head_shortlist", "spec_status_string", "spec_abi_version", "spec_kv_commit"):
+              "spec_draft_head_shortlist", "spec_status_string", "spec_abi_version", "spec_kv_commit",
+              "spec_verify_sparse_draft"):
         assert n in names
 
 
@@ -153,3 +154,23 @@ def test_kv_commit_zero_drafts_validates_without_dividing_by_k(lib):
     if torch.cuda.is_available():
         pytest.skip("the launch would dereference the fake pointers on a GPU")
     assert f(fake, fake, fake, fake, None, 2, 3, 0, 10, 8, 1, None) in (0, 4)
+
+
+def test_sparse_draft_validation(lib):
+    fake = ctypes.c_void_p(0x10000)
+    f = lib.spec_verify_sparse_draft
+    ns = (ctypes.c_int32 * 3)(4, 2, 1)
+
+    def call(n_sel=ns, L=2004, S=4, cs=501, V=4008, B=2, K=3, cids=fake, T=1.0):
+        return f(fake, fake, cids, n_sel, L, S, cs, fake, fake, B, K, V, 1, ctypes.c_float(T), fake, fake,
+                 None, None, None, 0, None)
+    INVALID, UNSUP, WS = 1, 2, 3
+    assert call() == WS                                  # valid arguments, no workspace
+    assert call(cs=500) == UNSUP                         # V % cluster_size != 0
+    assert call(cids=None) == INVALID
+    assert call(n_sel=None) == INVALID
+    assert call(n_sel=(ctypes.c_int32 * 3)(4, 0, 1)) == INVALID     # empty shortlist
+    assert call(n_sel=(ctypes.c_int32 * 3)(5, 2, 1)) == INVALID     # more than S clusters
+    assert call(L=2003) == INVALID                       # 4 clusters of 501 do not fit L
+    assert call(S=9) == INVALID                          # more slots than clusters
+    assert call(T=0.0) == INVALID

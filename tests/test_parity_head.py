@@ -129,3 +129,31 @@ def test_verify_on_shortlisted_draft():
     rep, out, orc = check_case(case)
     # drafts lie in the shortlist, so P_d(d) > 0 everywhere
     assert np.all(orc["p_draft"] > 0)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_head_per_position_budget(dtype):
+    """A shortlist per draft position (DynaSpec's position-aware budget, k_max = 8):
+    each position's compact logits against the oracle head run on that position alone."""
+    import speculative_sampling_verification_vocab_amd as sv
+    from workloads import top_clusters
+    g = torch.Generator().manual_seed(61)
+    B, K, d, nc, cs = 6, 4, 320, 20, 48
+    n_sel = [sv.position_budget(t, 8) for t in range(K)]          # [8, 8, 1, 1]
+    S = max(n_sel)
+    h = torch.randn(B, K, d, generator=g).to(torch.bfloat16)
+    W = (torch.randn(nc * cs, d, generator=g) * 0.05).to(torch.bfloat16)
+    cids = torch.full((B, K, S), -1, dtype=torch.int32)
+    for k in range(K):
+        cids[:, k, :n_sel[k]] = top_clusters(torch.randn(B, nc, generator=g), n_sel[k])
+    L = S * cs + 5
+    out = sv.spec_draft_head_positions(h.to(DEV), W.to(DEV), cids.to(DEV), n_sel, cs, L=L, dtype=dtype)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    for k in range(K):
+        ref = oracle.head(h[:, k:k + 1].contiguous(), W, cids[:, k, :n_sel[k]].contiguous(), cs,
+                          threads=oracle.default_threads())
+        n = n_sel[k] * cs
+        g_k = got[:, k:k + 1, :n]
+        tol = HEAD_TOL * ref["absdot"] + (np.abs(ref["compact"]) * 2.0 ** -8 if dtype == torch.bfloat16 else 0)
+        assert np.all(np.abs(g_k - ref["compact"]) <= tol + 1e-30), k

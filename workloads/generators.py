@@ -28,7 +28,7 @@ __all__ = [
     "normal_logits", "round_to", "noisy_copy", "gumbel_max_tokens",
     "argmax_tokens", "verify_uniforms", "verify_case", "workload_case",
     "head_case", "top_clusters", "bf16_bits", "f32_from_bf16_bits",
-    "TAG_KV", "KvCase", "kv_case", "KV_WORKLOAD",
+    "TAG_KV", "KvCase", "kv_case", "KV_WORKLOAD", "SparseDraftCase", "sparse_draft_case",
 ]
 
 TAG_TARGET, TAG_DRAFT_NOISE, TAG_DRAFT_TOKENS, TAG_UNIFORMS = 0, 1, 2, 3
@@ -264,3 +264,66 @@ def kv_case(P, B, K, Lmax, E, dtype=torch.bfloat16, *, trial=0, device="cpu") ->
         staging[p] = torch.randn((B, K, E), generator=g, device=device, dtype=torch.float32).to(dtype)
     ln = torch.randint(0, max(1, Lmax - K + 1), (B,), generator=g, device=device, dtype=torch.int64)
     return KvCase(cache, staging, ln.to(torch.int32))
+
+
+@dataclasses.dataclass
+class SparseDraftCase:
+    target: torch.Tensor        # [B, K+1, V]
+    compact: torch.Tensor       # [B, K, L] draft logits on each position's shortlist, ascending id
+    cluster_ids: torch.Tensor   # int32 [B, K, S], first n_sel[i] ascending, the rest -1
+    n_sel: list                 # K ints
+    cluster_size: int
+    dense_draft: torch.Tensor   # [B, K, V]: the same logits at their ids, -inf elsewhere
+    draft_tokens: torch.Tensor  # int32 [B, K]
+    uniforms: torch.Tensor      # float32 [B, K+1, 2]
+    temperature: float
+    dtype: str
+
+    @property
+    def B(self):
+        return self.target.shape[0]
+
+    @property
+    def K(self):
+        return self.target.shape[1] - 1
+
+    @property
+    def V(self):
+        return self.target.shape[2]
+
+
+def sparse_draft_case(B: int, K: int, V: int, cluster_size: int, n_sel, dtype: str = "bf16", *,
+                      sigma: float = 0.7, temperature: float = 1.0, key=(8,), device="cpu",
+                      target_std: float = 3.0, zipf_s: float = 1.1) -> SparseDraftCase:
+    """Per-position shortlists of a context: position i keeps its top n_sel[i]
+    clusters (contiguous id ranges of cluster_size) by a N(0,1) score; its draft
+    logits there are the target's plus N(0, sigma^2) noise.  Draft tokens are
+    sampled from the draft softmax (Gumbel-max on the dense -inf-filled form)."""
+    assert V % cluster_size == 0 and len(n_sel) == K
+    nc = V // cluster_size
+    S = max(n_sel) if K > 0 else 1
+    L = S * cluster_size
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    target = normal_logits((B, K + 1, V), target_std, zipf_s, key + (TAG_TARGET,), device)
+    noise = normal_logits((B, K, V), sigma, 0.0, key + (TAG_DRAFT_NOISE,), device)
+    scores = normal_logits((B, K, nc), 1.0, 0.0, key + (TAG_SCORES,), device)
+    cids = torch.full((B, K, S), -1, dtype=torch.int32, device=device)
+    compact = torch.zeros((B, K, L), dtype=torch.float32, device=device)
+    dense = torch.full((B, K, V), float("-inf"), dtype=torch.float32, device=device)
+    full_draft = round_to(target[:, :K] + noise, dtype).float()
+    for i in range(K):
+        top = torch.topk(scores[:, i], n_sel[i], dim=-1).indices
+        top = torch.sort(top, dim=-1).values.to(torch.int32)
+        cids[:, i, :n_sel[i]] = top
+        ids = (top.long()[:, :, None] * cluster_size + torch.arange(cluster_size, device=device)).reshape(B, -1)
+        vals = torch.gather(full_draft[:, i], 1, ids)
+        compact[:, i, :ids.shape[1]] = vals
+        dense[:, i].scatter_(1, ids, vals)
+    target = round_to(target, dtype)
+    compact = compact.to(tdt)
+    dense = dense.to(tdt)
+    tok = gumbel_max_tokens(dense, temperature, key + (TAG_DRAFT_TOKENS,)) if K > 0 else \
+        torch.zeros((B, 0), dtype=torch.int32, device=device)
+    uni = verify_uniforms(B, K, key + (TAG_UNIFORMS,), device)
+    return SparseDraftCase(target, compact, cids, list(n_sel), cluster_size, dense, tok, uni,
+                           float(temperature), dtype)

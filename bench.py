@@ -46,6 +46,8 @@ HEAD_PROFILE_PMC = os.path.join(ROOT, "profiles", "head_mfma_kernel_shortlist_b3
 CSRC = os.path.join(ROOT, "speculative_sampling_verification_vocab_amd", "csrc")
 KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("sv_verify.hip", "sv_common.h")]
 HEAD_SOURCES = [os.path.join(CSRC, f) for f in ("sv_head.hip", "sv_common.h")]
+STATIC_PROFILE_PMC = os.path.join(ROOT, "profiles", "head_static_kernel_frspec_m128_n32768_d4096_pmc.md")
+STATIC_SOURCES = [os.path.join(CSRC, f) for f in ("sv_static.hip", "sv_common.h")]
 
 
 def log(*a):
@@ -422,7 +424,72 @@ def bench_shortlist(args, dev):
         "cpu_baseline": None,
     }
     out["sparse_draft"] = bench_sparse_draft(hc, target, uni, args.steps, args.warmup, dev)
+    out["static_head"] = bench_static_head(hc, args.steps, args.warmup, dev)
     print(json.dumps(out), flush=True)
+
+
+def bench_static_head(hc, steps, warmup, dev):
+    """Drafter head over one static shortlist shared by all 128 contexts
+    (FR-Spec / VocabTrim): the same h and W, a fixed set of 32768 token ids at
+    cluster size 1 (FR-Spec's shortlist size) and of 16 clusters of 501
+    (N = 8016).  Times spec_draft_head_static (W rows gathered inside the
+    kernel) with fp32 and bf16 logits, and, for context, torch's bf16 GEMM
+    (F.linear, i.e. hipBLASLt) on a pre-gathered contiguous W_S."""
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+
+    import speculative_sampling_verification_vocab_amd as sv
+
+    B, K, d = hc.h.shape
+    V = hc.W.shape[0]
+    M = B * K
+    h2 = hc.h.reshape(M, d)
+
+    def med(fn, n):
+        for _ in range(warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+    shapes = []
+    for name, cs, n_sel, seed in (("frspec_32768_tokens", 1, 32768, 11), ("clusters_16x501", 501, 16, 12)):
+        g = torch.Generator().manual_seed(seed)
+        ids = torch.sort(torch.randperm(V // cs, generator=g)[:n_sel]).values.to(torch.int32).to(dev)
+        N = n_sel * cs
+        o32 = torch.empty((M, N), dtype=torch.float32, device=dev)
+        o16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        n = max(steps, 20)
+        ms32 = med(lambda: sv.spec_draft_head_static(h2, hc.W, ids, cs, out=o32), n)
+        ms16 = med(lambda: sv.spec_draft_head_static(h2, hc.W, ids, cs, dtype=torch.bfloat16, out=o16), n)
+        rows = (ids.long()[:, None] * cs + torch.arange(cs, device=dev)[None, :]).reshape(-1)
+        Ws = hc.W[rows].contiguous()
+        ms_blas = med(lambda: F.linear(h2, Ws), n)
+        del Ws
+        flops = 2.0 * M * N * d
+        b32 = N * d * 2 + M * d * 2 + M * N * 4
+        b16 = N * d * 2 + M * d * 2 + M * N * 2
+        ach = b32 / (ms32 * 1e-3) / 1e9
+        shapes.append({
+            "shortlist": name, "M": M, "N": N, "d": d, "cluster_size": cs,
+            "us_fp32_out": ms32 * 1e3, "us_bf16_out": ms16 * 1e3,
+            "roofline": {"bound": "hbm", "kernel": "head_static_kernel", "achieved": ach, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                         "traffic": traffic_from_profile(STATIC_PROFILE_PMC, STATIC_SOURCES)
+                         if name.startswith("frspec") else None,
+                         "algorithmic_bytes_per_launch": b32},
+            "bf16_out_gbs": b16 / (ms16 * 1e-3) / 1e9,
+            "mfma": {"achieved_tflops": flops / (ms32 * 1e-3) / 1e12, "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                     "frac": flops / (ms32 * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+            "blas_reference": {"op": "torch F.linear bf16 on a pre-gathered contiguous W_S (hipBLASLt)",
+                               "us": ms_blas * 1e3},
+        })
+    return shapes
 
 
 def bench_sparse_draft(hc, target, uni, steps, warmup, dev):

@@ -234,6 +234,26 @@ spec_status_t spec_draft_head_positions(const void* h, const void* W, const int3
                                         spec_dtype_t compact_dtype, void* stream);
 
 /*
+ * Drafter head over a static shortlist shared by every context: the fixed,
+ * frequency-ranked subsets (FR-Spec, VocabTrim) that the DynaSpec summary
+ * compares against.  A dense bf16 MFMA GEMM with fp32 accumulation:
+ *   logits[m, s] = sum_j h[m, j] * W[tok(s), j],  tok(s) = cluster_ids[s / cs] * cs + s % cs,
+ * for M = B*K hidden-state rows and N = n_sel * cluster_size shortlist tokens.
+ *
+ *   h            bf16 [M, d];  W  bf16 [V, d] row-major.
+ *   cluster_ids  int32 [n_sel] (device), ascending ids in [0, V / cluster_size);
+ *                an id outside that range contributes zero rows (not checked
+ *                on the host).
+ *   logits       [M, N] of out_dtype out (bf16 rounds to nearest even).
+ * Errors: SPEC_ERR_INVALID_ARG for NULL buffers or bad sizes;
+ * SPEC_ERR_UNSUPPORTED if V % cluster_size != 0 or the output needs more than
+ * 2^31 - 1 tiles of 128 x 32.
+ */
+spec_status_t spec_draft_head_static(const void* h, const void* W, const int32_t* cluster_ids, int32_t M,
+                                     int32_t d, int32_t V, int32_t cluster_size, int32_t n_sel, void* logits,
+                                     spec_dtype_t out_dtype, void* stream);
+
+/*
  * KV-cache commit after a verify step (Speculative Decoding lesson,
  * nextadmin.net, section on KV-cache management and exercise 4).  The
  * target's forward over the K drafts wrote one KV entry per draft position

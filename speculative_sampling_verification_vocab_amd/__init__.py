@@ -20,6 +20,7 @@ from ._native import SpecVerifyError  # noqa: F401
 
 __all__ = ["spec_verify", "spec_verify_workspace_bytes", "spec_verify_launch_count", "spec_draft_head_shortlist",
            "spec_kv_commit", "spec_verify_sparse_draft", "position_budget", "spec_draft_head_positions",
+           "spec_draft_head_static",
            "Workspace", "SpecVerifyError", "abi_version"]
 
 _DTYPES = {torch.bfloat16: _native.SPEC_BF16, torch.float32: _native.SPEC_F32}
@@ -311,4 +312,37 @@ def spec_draft_head_positions(h: torch.Tensor, W: torch.Tensor, cluster_ids: tor
                                                   int(cluster_size), S, L, _ptr(out), dt,
                                                   _stream_handle(h.device, stream))
     _native.check(st, "spec_draft_head_positions")
+    return out
+
+
+def spec_draft_head_static(h: torch.Tensor, W: torch.Tensor, cluster_ids: torch.Tensor, cluster_size: int,
+                           dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """Drafter head over one shortlist shared by every context (see
+    spec_draft_head_static in specverify.h).  h bf16 [..., d] (all leading
+    dims are rows), W bf16 [V, d], cluster_ids int32 [n_sel].  Returns logits
+    [..., n_sel * cluster_size] of dtype."""
+    for t, name in ((h, "h"), (W, "W"), (cluster_ids, "cluster_ids")):
+        _need_gpu(t, name)
+    if h.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+        raise ValueError("h and W must be bfloat16")
+    if cluster_ids.dtype != torch.int32 or cluster_ids.dim() != 1:
+        raise ValueError("cluster_ids must be int32 [n_sel]")
+    d = h.shape[-1]
+    M = h.numel() // d
+    V = W.shape[0]
+    N = cluster_ids.numel() * cluster_size
+    dt = _DTYPES.get(dtype)
+    if dt is None:
+        raise ValueError("dtype must be bfloat16 or float32")
+    shape = tuple(h.shape[:-1]) + (N,)
+    if out is None:
+        out = torch.empty(shape, dtype=dtype, device=h.device)
+    elif out.dtype != dtype or tuple(out.shape) != shape or not out.is_contiguous():
+        raise ValueError("out must be contiguous with shape h.shape[:-1] + (N,) and dtype")
+    st = _native.load().spec_draft_head_static(_ptr(h.contiguous()), _ptr(W.contiguous()),
+                                               _ptr(cluster_ids.contiguous()), M, d, V, int(cluster_size),
+                                               cluster_ids.numel(), _ptr(out), dt,
+                                               _stream_handle(h.device, stream))
+    _native.check(st, "spec_draft_head_static")
     return out

@@ -229,6 +229,24 @@ spec_status_t spec_draft_head_positions(const void* h, const void* W, const int3
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
+spec_status_t spec_draft_head_static(const void* h, const void* W, const int32_t* cluster_ids, int32_t M,
+                                     int32_t d, int32_t V, int32_t cluster_size, int32_t n_sel, void* logits,
+                                     spec_dtype_t out_dtype, void* stream) {
+  if (M < 0 || d < 1 || V < 1 || cluster_size < 1 || n_sel < 0) return SPEC_ERR_INVALID_ARG;
+  if (!valid_dtype(out_dtype)) return SPEC_ERR_INVALID_ARG;
+  if (V % cluster_size != 0) return SPEC_ERR_UNSUPPORTED;
+  if (n_sel > V / cluster_size) return SPEC_ERR_INVALID_ARG;
+  if (M == 0 || n_sel == 0) return SPEC_OK;
+  if (!h || !W || !cluster_ids || !logits) return SPEC_ERR_INVALID_ARG;
+  const size_t N = (size_t)n_sel * (size_t)cluster_size;
+  if ((size_t)M * N > SIZE_MAX / 8 || (size_t)M * (size_t)d > SIZE_MAX / 8) return SPEC_ERR_INVALID_ARG;
+  if (((N + 31) / 32) * (((size_t)M + 127) / 128) > 0x7fffffffu) return SPEC_ERR_UNSUPPORTED;  // 1-D grid of tiles
+  (void)hipGetLastError();
+  const hipError_t e = sv::launch_head_static(h, W, cluster_ids, M, d, V, cluster_size, n_sel, logits,
+                                              out_dtype == SPEC_BF16 ? 1 : 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
 spec_status_t spec_kv_commit(void* cache, const void* staging, const int32_t* accepted_len, int32_t* cache_len,
                              int32_t* status, int32_t P, int32_t B, int32_t K, int32_t L_max, int32_t E,
                              spec_dtype_t dtype, void* stream) {

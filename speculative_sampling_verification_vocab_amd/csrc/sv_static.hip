@@ -1,0 +1,330 @@
+// Drafter head over a static shortlist shared by every context (the
+// fixed-subset methods the DynaSpec summary contrasts with, FR-Spec and
+// VocabTrim: one frequency-ranked subset of the vocabulary for all contexts).
+// With one shortlist the head is a dense GEMM, C[M, N] = h[M, d] * W_S[N, d]^T,
+// M = B*K rows of hidden states and N = n_sel * cluster_size shortlist tokens
+// whose W rows are gathered cluster by cluster.
+//
+// For the drafting shapes (M = B*K up to a few hundred, d = 4096, N of 8k to
+// 32k) the GEMM is bound by the stream of W_S from HBM: 2 flops per byte per
+// row of M, far below the MFMA/HBM balance of about 300.  The kernel:
+//   * one block per (kMt x kNt) output tile; h (1 MiB at M = 128) is re-read
+//     from L2 by every column tile, so kNt is as wide as the grid allows;
+//   * both operands go global -> registers -> LDS in stages of 64 hidden dims
+//     (two LDS buffers) with fully coalesced 16-byte loads, P stages in flight
+//     in registers; the loads are issued without branches and masked on the
+//     way to LDS, which keeps the compiler's wait counts partial;
+//   * each wave computes TM x TN chunks of 16 x 16 with
+//     v_mfma_f32_16x16x32_bf16 from LDS fragments (lane l: row l % 16,
+//     k offset 8 * (l / 16)), fp32 accumulation; WK > 1 splits the MFMA
+//     k-steps of a stage between waves and adds the partial tiles at the end.
+// With W already coalesced, what remains is the LDS traffic of the fragment
+// reads (each h fragment is read by every column wave): the kernel runs at
+// about two thirds of the HBM rate.  Loading W straight into B-fragment
+// registers (no LDS for W) measured slower: a B fragment spans 16 rows, so
+// each such load touches twice the cache lines per byte.
+// Cluster ids are not checked on the host; an id outside [0, V / cluster_size)
+// contributes zero rows.
+
+#include "sv_common.h"
+#include "sv_internal.h"
+
+namespace sv {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+
+struct StaticArgs {
+  const uint16_t* h;     // bf16 [M, d]
+  const uint16_t* W;     // bf16 [V, d]
+  const int32_t* cids;   // [n_sel]
+  int M, d, cs, N;
+  int nclusters;         // V / cs: ids outside [0, nclusters) read as zero rows
+  int m_tiles;           // row tiles; column tile = v / m_tiles
+  int remap;             // XCD-aware tile order (grid a multiple of 8, m_tiles > 1)
+  void* out;             // [M, N] fp32 or bf16
+  int out_bf16;
+  int pair16;            // bf16 out, N even, out 4-byte aligned: dword stores of column pairs
+};
+
+__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// 8 consecutive bf16 of a row from k, zeros past d (any d, any alignment).
+__device__ __forceinline__ u32x4 load8_slow(const uint16_t* row, int k, int d) {
+  uint32_t t4[4] = {0u, 0u, 0u, 0u};
+  for (int e = 0; e < 8; ++e)
+    if (k + e < d) t4[e >> 1] |= (uint32_t)row[k + e] << (16 * (e & 1));
+  return u32x4{t4[0], t4[1], t4[2], t4[3]};
+}
+
+// WM x WN x WK waves; each wave TM x TN chunks of 16 x 16 over every WK-th
+// MFMA k-step of a stage (WK > 1: the WK partial sums are added through LDS
+// at the end); P (even) stages in flight; rows of kStage + kPad bf16 in LDS.
+// kVec: d % 8 == 0 and 16-byte aligned rows (eight dims are all inside d or
+// all past it).
+template <int WM, int WN, int WK, int TM, int TN, int P, int kStage, int kPad, bool kVec>
+__global__ void __launch_bounds__(kWave * WM * WN * WK) head_static_kernel(StaticArgs a) {
+  constexpr int kStride = kStage + kPad;
+  constexpr int kCols = kStage / 8;     // sixteen-byte columns per row and stage
+  constexpr int kThreads = kWave * WM * WN * WK;
+  constexpr int kMt = 16 * WM * TM, kNt = 16 * WN * TN, kRows = kMt + kNt;
+  constexpr int kR = kThreads / kCols;          // rows one load slot covers across the block
+  constexpr int kL = kRows / kR;                // load slots per thread and stage
+  constexpr int kLA = kMt / kR;                 // the first kLA slots are h rows
+  static_assert(kThreads % kCols == 0 && kMt % kR == 0 && kNt % kR == 0, "tile / block mismatch");
+  static_assert(P % 2 == 0, "stage parity must be static");
+  static_assert(kStage % (32 * WK) == 0 && kPad % 8 == 0, "stage / split mismatch");
+  static_assert((WK - 1) * WM * WN * kWave * TN * 4 * 4 <= 2 * kRows * kStride * 2, "reduction space");
+  __shared__ __attribute__((aligned(16))) uint16_t sh[2][kRows * kStride];
+
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int wk = wave / (WM * WN), wmn = wave % (WM * WN);
+  const int wm = wmn / WN, wn = wmn % WN;
+  int v = blockIdx.x;
+  if (a.remap) v = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int n0 = (v / a.m_tiles) * kNt, m0 = (v % a.m_tiles) * kMt;
+
+  const int lrow = threadIdx.x / kCols, c8 = (threadIdx.x % kCols) * 8;
+  // Every slot loads from a valid row (h row 0 stands in for rows past M,
+  // past N or of an out-of-range cluster) and masks the value: loads under a
+  // branch would make the compiler wait for all of them before each stage.
+  const uint16_t* src[kL];
+  uint32_t live[kL];
+#pragma unroll
+  for (int j = 0; j < kL; ++j) {
+    const int r = lrow + kR * j;
+    src[j] = a.h;
+    live[j] = 0u;
+    if (j < kLA) {
+      const int m = m0 + r;
+      if (m < a.M) src[j] = a.h + (size_t)m * a.d, live[j] = ~0u;
+    } else {
+      const int n = n0 + r - kMt;
+      if (n < a.N) {
+        const int s = n / a.cs;
+        const int c = a.cids[s];
+        if (c >= 0 && c < a.nclusters) src[j] = a.W + ((size_t)c * a.cs + (n - s * a.cs)) * a.d, live[j] = ~0u;
+      }
+    }
+  }
+  const int nst = (a.d + kStage - 1) / kStage;
+  u32x4 R[P][kL];
+  // Loads of stage s.  Dims past d (the ragged last stage, and the stages up
+  // to the next multiple of P, which the loop runs as zeros) load from the
+  // row start and are zeroed when the slot is written to LDS, with rows that
+  // are not live; masking at load time would make the wave wait for the
+  // loads at once, and a branch around them makes the compiler wait for all
+  // loads in flight.
+  auto issue = [&](u32x4 (&slot)[kL], int s) {
+    const int k = s * kStage + c8;
+    if (kVec) {
+      const int kk = k < a.d ? k : 0;
+#pragma unroll
+      for (int j = 0; j < kL; ++j) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(src[j] + kk);
+#ifdef SV_STATIC_W_CACHED
+        slot[j] = *p;
+#else
+        slot[j] = j < kLA ? *p : __builtin_nontemporal_load(p);
+#endif
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kL; ++j) slot[j] = live[j] ? load8_slow(src[j], k, a.d) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto put = [&](const u32x4 (&slot)[kL], int buf, int s) {
+    const uint32_t kin = s * kStage + c8 < a.d ? ~0u : 0u;
+#pragma unroll
+    for (int j = 0; j < kL; ++j) {
+      const uint32_t m = live[j] & kin;
+      *reinterpret_cast<u32x4*>(&sh[buf][(lrow + kR * j) * kStride + c8]) =
+          u32x4{slot[j][0] & m, slot[j][1] & m, slot[j][2] & m, slot[j][3] & m};
+    }
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Slot by slot, in the order the loop issues them (no interleaving by the
+  // scheduler), so the loads in flight at the loop head are the same on entry
+  // and on the back edge and the compiler's wait counts stay partial.
+#pragma unroll
+  for (int q = 0; q < P; ++q) {
+    issue(R[q], q);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  put(R[0], 0, 0);
+  issue(R[0], P);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+
+  const int frow = lane & 15, fk = 8 * (lane >> 4);
+  const int arow0 = wm * 16 * TM + frow, brow0 = kMt + wn * 16 * TN + frow;
+  // Stage s lives in LDS buffer s & 1 (P is even, so q & 1) and in register
+  // slot s % P before that.  No exit inside the unrolled body: every path
+  // through the loop issues the same loads.
+  for (int s0 = 0; s0 < nst; s0 += P) {
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      const int s = s0 + q;
+      const int buf = q & 1;
+#pragma unroll
+      for (int kk = 0; kk < kStage / (32 * WK); ++kk) {
+        const int ks = 32 * (kk * WK + wk);
+        bf16x8 bf[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          bf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                 &sh[buf][(brow0 + 16 * j) * kStride + ks + fk]));
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const bf16x8 af = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                           &sh[buf][(arow0 + 16 * i) * kStride + ks + fk]));
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
+        }
+      }
+      // The other LDS buffer was last read in stage s - 1, before the
+      // previous barrier.
+      put(R[(q + 1) % P], buf ^ 1, s + 1);
+      issue(R[(q + 1) % P], s + 1 + P);
+      __syncthreads();
+    }
+  }
+
+  if (WK > 1) {
+    // The loop ended on a barrier: LDS is free.  One row chunk i at a time,
+    // split k-groups 1.. park their sums and group 0 adds them in a fixed
+    // order.
+    float* red = reinterpret_cast<float*>(&sh[0][0]);
+    constexpr int kE = TN * 4;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (wk > 0) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            red[(((wk - 1) * WM * WN + wmn) * kE + j * 4 + r) * kWave + lane] = acc[i][j][r];
+      }
+      __syncthreads();
+      if (wk == 0) {
+#pragma unroll
+        for (int k2 = 1; k2 < WK; ++k2)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[i][j][r] += red[(((k2 - 1) * WM * WN + wmn) * kE + j * 4 + r) * kWave + lane];
+      }
+      __syncthreads();
+    }
+    if (wk > 0) return;
+  }
+  // Lane holds D[4 * (lane / 16) + r][lane % 16] of each 16 x 16 chunk.
+  if (a.pair16) {
+    // bf16 pairs: lanes c and c ^ 1 (columns n, n + 1) swap two of their
+    // four rows, so each lane stores two rows as one dword per row (the even
+    // lane rows 0 and 1, the odd lane rows 2 and 3) instead of four shorts.
+    const int odd = lane & 1;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int nc = n0 + wn * 16 * TN + 16 * j + (lane & 14);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const f32x4 v = acc[i][j];
+        const float r0 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(odd ? v[0] : v[2]), 0xb1, 0xf, 0xf, false));
+        const float r1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(odd ? v[1] : v[3]), 0xb1, 0xf, 0xf, false));
+        if (nc >= a.N) continue;
+        const int mb = m0 + wm * 16 * TM + 16 * i + 4 * (lane >> 4) + 2 * odd;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int m = mb + q;
+          if (m >= a.M) continue;
+          const float lo = odd ? (q ? r1 : r0) : v[q];
+          const float hi = odd ? v[2 + q] : (q ? r1 : r0);
+          *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + (size_t)m * a.N + nc) =
+              (uint32_t)to_bf16_rne(lo) | ((uint32_t)to_bf16_rne(hi) << 16);
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int n = n0 + wn * 16 * TN + 16 * j + (lane & 15);
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * 16 * TM + 16 * i + 4 * (lane >> 4) + r;
+        if (m < a.M) {
+          const size_t o = (size_t)m * a.N + n;
+          if (a.out_bf16) static_cast<uint16_t*>(a.out)[o] = to_bf16_rne(acc[i][j][r]);
+          else static_cast<float*>(a.out)[o] = acc[i][j][r];
+        }
+      }
+    }
+  }
+}
+
+template <int WM, int WN, int WK, int TM, int TN, int P, int KS = 64, int KP = 8>
+hipError_t launch_cfg(StaticArgs a, bool vec, hipStream_t st) {
+  constexpr int kMt = 16 * WM * TM, kNt = 16 * WN * TN;
+  a.m_tiles = (a.M + kMt - 1) / kMt;
+  const long long total = (long long)((a.N + kNt - 1) / kNt) * a.m_tiles;
+  if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+  a.remap = a.m_tiles > 1 && total % 8 == 0;
+  const dim3 grid((unsigned)total), block(kWave * WM * WN * WK);
+  if (vec) hipLaunchKernelGGL((head_static_kernel<WM, WN, WK, TM, TN, P, KS, KP, true>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((head_static_kernel<WM, WN, WK, TM, TN, P, KS, KP, false>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_head_static(const void* h, const void* W, const int32_t* cluster_ids, int M, int d, int V,
+                              int cluster_size, int n_sel, void* out, int out_dtype, hipStream_t st) {
+  StaticArgs a{};
+  a.h = static_cast<const uint16_t*>(h);
+  a.W = static_cast<const uint16_t*>(W);
+  a.cids = cluster_ids;
+  a.M = M;
+  a.d = d;
+  a.cs = cluster_size;
+  a.N = n_sel * cluster_size;
+  a.nclusters = V / cluster_size;
+  a.out = out;
+  a.out_bf16 = out_dtype == 1;
+  a.pair16 = a.out_bf16 && a.N % 2 == 0 && (uintptr_t)out % 4 == 0;
+  const bool vec = (d % 8 == 0) && ((uintptr_t)h % 16 == 0) && ((uintptr_t)W % 16 == 0);
+  // Widest column tile whose grid still gives most CUs a block: 128 x 128
+  // tiles on 8 waves (2 x 4, each 64 x 32) for wide shortlists, else 128 x 32
+  // tiles on 4 waves (2 x 1 x 2: two row halves, each MFMA k-step split
+  // between two waves).  Rows of 64 + 16 bf16 in LDS.
+  const long long t128 = (long long)((M + 127) / 128) * ((a.N + 127) / 128);
+#ifdef SV_STATIC_CFG
+  const int cfg = SV_STATIC_CFG;
+#else
+  const int cfg = t128 >= 192 ? 0 : 1;
+#endif
+  (void)t128;
+  if (cfg == 0) return launch_cfg<2, 4, 1, 4, 2, 4, 64, 16>(a, vec, st);
+  return launch_cfg<2, 1, 2, 4, 2, 4, 64, 16>(a, vec, st);
+}
+
+}  // namespace sv

@@ -26,7 +26,7 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("spec_verify", "spec_verify_timed", "spec_verify_workspace_bytes",
               "spec_draft_head_shortlist", "spec_status_string", "spec_abi_version", "spec_kv_commit",
-              "spec_verify_sparse_draft"):
+              "spec_verify_sparse_draft", "spec_draft_head_positions", "spec_draft_head_static"):
         assert n in names
 
 
@@ -118,6 +118,22 @@ def test_head_validation(lib):
     assert f(fake, fake, fake, 2, 4, 64, 1000, 10, 2, None, None, 0, None, 0, None) == 1
     assert f(fake, fake, fake, 2, 4, 64, 1000, 10, 101, fake, None, 0, None, 0, None) == 1
     assert f(fake, fake, fake, 0, 4, 64, 1000, 10, 2, fake, None, 0, None, 0, None) == 0
+
+
+def test_static_head_validation(lib):
+    fake = ctypes.c_void_p(0x10000)
+    f = lib.spec_draft_head_static
+    assert f(fake, fake, fake, 4, 64, 1000, 7, 2, fake, 0, None) == 2      # V % cs
+    assert f(None, fake, fake, 4, 64, 1000, 10, 2, fake, 0, None) == 1     # NULL h
+    assert f(fake, fake, fake, 4, 64, 1000, 10, 2, None, 0, None) == 1     # NULL out
+    assert f(fake, fake, fake, 4, 64, 1000, 10, 101, fake, 0, None) == 1   # n_sel > V / cs
+    assert f(fake, fake, fake, 4, 0, 1000, 10, 2, fake, 0, None) == 1      # d < 1
+    assert f(fake, fake, fake, -1, 64, 1000, 10, 2, fake, 0, None) == 1    # M < 0
+    assert f(fake, fake, fake, 4, 64, 1000, 10, 2, fake, 7, None) == 1     # bad dtype
+    assert f(None, None, None, 0, 64, 1000, 10, 2, None, 0, None) == 0     # M = 0: nothing to do
+    assert f(None, None, None, 4, 64, 1000, 10, 0, None, 0, None) == 0     # empty shortlist
+    # more than 2^31 - 1 output tiles of 128 x 32
+    assert f(fake, fake, fake, 0x7fffffff, 8, 1 << 20, 1, 1 << 20, fake, 0, None) == 2
 
 
 def test_kv_commit_validation(lib):

@@ -48,6 +48,8 @@ KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("sv_verify.hip", "sv_common.h"
 HEAD_SOURCES = [os.path.join(CSRC, f) for f in ("sv_head.hip", "sv_common.h")]
 STATIC_PROFILE_PMC = os.path.join(ROOT, "profiles", "head_static_kernel_frspec_m128_n32768_d4096_pmc.md")
 STATIC_SOURCES = [os.path.join(CSRC, f) for f in ("sv_static.hip", "sv_common.h")]
+MFMA_PROFILE_PMC = os.path.join(ROOT, "profiles", "head_kernels_mfma_busy_pmc.md")
+MFMA_SOURCES = [os.path.join(CSRC, f) for f in ("sv_head.hip", "sv_static.hip", "sv_common.h")]
 
 
 def log(*a):
@@ -62,17 +64,23 @@ def source_hash(sources=KERNEL_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(path=PROFILE_PMC, sources=KERNEL_SOURCES):
-    """HBM bytes per launch of the dominant kernel from a committed PMC
-    summary, if it was taken on the current kernel source."""
+def profile_value(path, key, sources):
+    """A figure recorded as `key: value` in a committed rocprofv3 summary, if
+    the summary was taken on the current kernel source (its source_sha256)."""
     if not os.path.exists(path):
         return None
     txt = open(path).read()
     m_hash = re.search(r"source_sha256:\s*([0-9a-f]+)", txt)
-    m_tr = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m_hash or not m_tr or m_hash.group(1) != source_hash(sources):
+    m_v = re.search(re.escape(key) + r":\s*([0-9.eE+-]+)", txt)
+    if not m_hash or not m_v or m_hash.group(1) != source_hash(sources):
         return None
-    return float(m_tr.group(1))
+    return float(m_v.group(1))
+
+
+def traffic_from_profile(path=PROFILE_PMC, sources=KERNEL_SOURCES):
+    """HBM bytes per launch of the dominant kernel from a committed PMC
+    summary, if it was taken on the current kernel source."""
+    return profile_value(path, "hbm_bytes_per_launch", sources)
 
 
 def cpu_baseline(case, res, args, K):
@@ -99,9 +107,63 @@ def cpu_baseline(case, res, args, K):
         wall += time.perf_counter() - t1
         reps += 1
     agree = int(np.sum(orc["accepted_len"] == res[0][sl].cpu().numpy()))
+    # one thread on a smaller slice of the same sample, for the per-core rate
+    n1 = max(1, min(nb, 16))
+    t1 = time.perf_counter()
+    oracle.verify(tgt_h[:n1], None if dr_h is None else dr_h[:n1], tok_h[:n1], None if uni_h is None else uni_h[:n1],
+                  case.temperature, mode=mode, threads=1)
+    w1 = time.perf_counter() - t1
     return {"value": reps * nb * (K + 1) / wall, "unit": "positions/s", "cores": threads, "kind": "oracle",
+            "single_thread_value": n1 * (K + 1) / w1,
             "sample": f"first {nb} of {B} sequences of the same batch x {reps} repetitions, fp64 C oracle, "
-                      f"{threads} threads, {wall:.2f} s wall; accepted_len agrees on {agree}/{nb}"}
+                      f"{threads} threads, {wall:.2f} s wall; accepted_len agrees on {agree}/{nb}; "
+                      f"single thread: first {n1} sequences once, {w1:.2f} s"}
+
+
+def copy_reference(dev, gib=1.0, reps=5):
+    """Measured bandwidth of a plain device copy (torch's copy kernel), bytes
+    read + written per second: the practical ceiling beside the 8 TB/s peak."""
+    import numpy as np
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        b.copy_(a)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([x.elapsed_time(y) for x, y in ev]))
+    del a, b
+    return 2.0 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def cold_warm(call, input_bytes, dev, reps=20):
+    """Median HIP-event time of one call with its inputs cache-resident (warm)
+    and after a 512 MiB write that evicts them from the 256 MB last-level
+    cache (cold).  Only meaningful for inputs well under 256 MB."""
+    import numpy as np
+    import torch
+    flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
+    out = {}
+    for kind in ("warm", "cold"):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        call()
+        for e0, e1 in ev:
+            if kind == "cold":
+                flush.fill_(float(len(out)))
+            e0.record()
+            call()
+            e1.record()
+        torch.cuda.synchronize()
+        out[kind + "_us"] = float(np.median([x.elapsed_time(y) for x, y in ev])) * 1e3
+    del flush
+    out["input_bytes"] = input_bytes
+    out["cold_gbs"] = input_bytes / (out["cold_us"] * 1e-6) / 1e9
+    out["note"] = "median of %d calls, events around the call only; cold = after a 512 MiB fill kernel" % reps
+    return out
 
 
 def bench_kv_commit(accepted_len, K, steps, dev):
@@ -303,6 +365,15 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, res, args, K)
+    copy_gbs = copy_reference(dev)
+    cache = None
+    in_bytes = step_bytes + B * K * 4 + B * (K + 1) * 8
+    if in_bytes < 256_000_000:
+        # inputs that fit the 256 MB last-level cache: report cold and warm calls
+        sampling = args.mode != "greedy"
+        cache = cold_warm(lambda: sv.spec_verify(case.target, case.draft if sampling else None, case.draft_tokens,
+                                                 case.uniforms if sampling else None, case.temperature,
+                                                 args.mode, workspace=ws), in_bytes, dev)
     kv = None
     if args.mode == "sample" and not args.no_kv_commit:
         kv = bench_kv_commit(res[0], K, args.steps, dev)
@@ -328,9 +399,12 @@ def main():
         "mean_tokens_per_verify": mean_tokens,
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": dom_bytes},
+                     "algorithmic_bytes_per_launch": dom_bytes,
+                     "measured_copy_gbs": copy_gbs, "frac_of_copy": achieved / copy_gbs},
         "cpu_baseline": cpu,
     }
+    if cache is not None:
+        out["cache_residency"] = cache
     if early is not None:
         out["early_exit"] = early
     if kv is not None:
@@ -419,10 +493,16 @@ def bench_shortlist(args, dev):
                      "algorithmic_bytes_per_launch": head_bytes},
         "mfma": {"achieved_tflops": tflops, "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                  "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "flops_per_launch": flops,
+                 "busy_frac_pmc": profile_value(MFMA_PROFILE_PMC, "mfma_busy_frac head_mfma_kernel", MFMA_SOURCES),
                  "ridge_note": f"{flops / head_bytes:.1f} flop/byte against a ridge of "
                                f"{MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):.0f}: HBM-bound"},
         "cpu_baseline": None,
     }
+    vb = B * (2 * K + 1) * V * 2 + B * K * 4 + B * (K + 1) * 8
+    out["cache_residency_verify"] = cold_warm(
+        lambda: sv.spec_verify(target, dense, tok, uni, 1.0, "sample", workspace=ws), vb, dev)
+    out["roofline"]["measured_copy_gbs"] = copy_reference(dev)
+    out["roofline"]["frac_of_copy"] = achieved / out["roofline"]["measured_copy_gbs"]
     out["sparse_draft"] = bench_sparse_draft(hc, target, uni, args.steps, args.warmup, dev)
     out["static_head"] = bench_static_head(hc, args.steps, args.warmup, dev)
     print(json.dumps(out), flush=True)
@@ -485,7 +565,10 @@ def bench_static_head(hc, steps, warmup, dev):
                          "algorithmic_bytes_per_launch": b32},
             "bf16_out_gbs": b16 / (ms16 * 1e-3) / 1e9,
             "mfma": {"achieved_tflops": flops / (ms32 * 1e-3) / 1e12, "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-                     "frac": flops / (ms32 * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+                     "frac": flops / (ms32 * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                     "busy_frac_pmc": profile_value(MFMA_PROFILE_PMC, "mfma_busy_frac head_static_kernel "
+                                                    + ("n32768_fp32" if name.startswith("frspec") else "n8016"),
+                                                    MFMA_SOURCES)},
             "blas_reference": {"op": "torch F.linear bf16 on a pre-gathered contiguous W_S (hipBLASLt)",
                                "us": ms_blas * 1e3},
         })

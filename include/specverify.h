@@ -241,11 +241,13 @@ spec_status_t spec_draft_head_positions(const void* h, const void* W, const int3
  * for M = B*K hidden-state rows and N = n_sel * cluster_size shortlist tokens.
  *
  *   h            bf16 [M, d];  W  bf16 [V, d] row-major.
- *   cluster_ids  int32 [n_sel] (device), ascending ids in [0, V / cluster_size);
- *                an id outside that range contributes zero rows (not checked
- *                on the host).
+ *   cluster_ids  int32 [n_sel] (device), ids in [0, V / cluster_size) in any
+ *                order (the output columns follow it); an id outside that
+ *                range contributes zero columns (not checked on the host).
  *   logits       [M, N] of out_dtype out (bf16 rounds to nearest even).
- * Errors: SPEC_ERR_INVALID_ARG for NULL buffers or bad sizes;
+ * Any alignment of whole elements works; 16-byte aligned h and W with d % 8 == 0
+ * take the vector-load path.
+ * Errors: SPEC_ERR_INVALID_ARG for NULL or misaligned buffers or bad sizes;
  * SPEC_ERR_UNSUPPORTED if V % cluster_size != 0 or the output needs more than
  * 2^31 - 1 tiles of 128 x 32.
  */

@@ -238,6 +238,9 @@ spec_status_t spec_draft_head_static(const void* h, const void* W, const int32_t
   if (n_sel > V / cluster_size) return SPEC_ERR_INVALID_ARG;
   if (M == 0 || n_sel == 0) return SPEC_OK;
   if (!h || !W || !cluster_ids || !logits) return SPEC_ERR_INVALID_ARG;
+  if ((uintptr_t)h % 2 || (uintptr_t)W % 2 || (uintptr_t)cluster_ids % 4 ||
+      (uintptr_t)logits % elem_size(out_dtype))
+    return SPEC_ERR_INVALID_ARG;
   const size_t N = (size_t)n_sel * (size_t)cluster_size;
   if ((size_t)M * N > SIZE_MAX / 8 || (size_t)M * (size_t)d > SIZE_MAX / 8) return SPEC_ERR_INVALID_ARG;
   if (((N + 31) / 32) * (((size_t)M + 127) / 128) > 0x7fffffffu) return SPEC_ERR_UNSUPPORTED;  // 1-D grid of tiles

@@ -24,7 +24,7 @@
 // registers (no LDS for W) measured slower: a B fragment spans 16 rows, so
 // each such load touches twice the cache lines per byte.
 // Cluster ids are not checked on the host; an id outside [0, V / cluster_size)
-// contributes zero rows.
+// contributes zero columns.
 
 #include "sv_common.h"
 #include "sv_internal.h"
@@ -40,7 +40,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 struct StaticArgs {
   const uint16_t* h;     // bf16 [M, d]
   const uint16_t* W;     // bf16 [V, d]
-  const int32_t* cids;   // [n_sel]
+  const int32_t* cids;   // [n_sel], any order
   int M, d, cs, N;
   int nclusters;         // V / cs: ids outside [0, nclusters) read as zero rows
   int m_tiles;           // row tiles; column tile = v / m_tiles

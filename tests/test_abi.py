@@ -130,6 +130,9 @@ def test_static_head_validation(lib):
     assert f(fake, fake, fake, 4, 0, 1000, 10, 2, fake, 0, None) == 1      # d < 1
     assert f(fake, fake, fake, -1, 64, 1000, 10, 2, fake, 0, None) == 1    # M < 0
     assert f(fake, fake, fake, 4, 64, 1000, 10, 2, fake, 7, None) == 1     # bad dtype
+    odd = ctypes.c_void_p(0x10001)
+    assert f(odd, fake, fake, 4, 64, 1000, 10, 2, fake, 0, None) == 1      # h not on a bf16 boundary
+    assert f(fake, fake, fake, 4, 64, 1000, 10, 2, ctypes.c_void_p(0x10002), 0, None) == 1  # fp32 out misaligned
     assert f(None, None, None, 0, 64, 1000, 10, 2, None, 0, None) == 0     # M = 0: nothing to do
     assert f(None, None, None, 4, 64, 1000, 10, 0, None, 0, None) == 0     # empty shortlist
     # more than 2^31 - 1 output tiles of 128 x 32

@@ -275,8 +275,9 @@ def main():
         Pass 1 (no instrumentation): mean wall ms per step between two device
         synchronisations.  Pass 2: the same calls with a HIP event recorded on
         the launch stream before every kernel launch and after the last, for
-        per-kernel durations (an event record between dependent launches adds
-        ~3 us, so pass 2 is not used for the step time)."""
+        per-kernel durations, mean and median over the steps (an event record
+        between dependent launches adds ~3 us, so pass 2 is not used for the
+        step time)."""
         L = sv.spec_verify_launch_count(B, K, V, case.target.dtype, mode)
         NE = L + 1
         sampling = mode != "greedy"
@@ -304,14 +305,16 @@ def main():
             step(evs[NE * s:NE * s + NE])
         torch.cuda.synchronize()
 
-        def span(i, j):
-            return float(np.mean([evs[NE * s + i].elapsed_time(evs[NE * s + j]) for s in range(steps)]))
+        def span(i, j, f=np.mean):
+            return float(f([evs[NE * s + i].elapsed_time(evs[NE * s + j]) for s in range(steps)]))
 
         launch_ms = [span(k, k + 1) for k in range(L)]
+        timed.medians = {"launches": [span(k, k + 1, np.median) for k in range(L)],
+                         "events_step": span(0, L, np.median)}
         return ms, launch_ms, span(0, L), res
 
     ms_step, launch_ms, ev_step, res = timed(args.mode, args.steps, args.warmup)
-    k_ms = {"launches": launch_ms, "events_step": ev_step}
+    k_ms = {"launches": launch_ms, "events_step": ev_step, "median": timed.medians}
     acc = res[0].float()
     mean_tokens = float((acc[acc >= 0] + 1).mean()) if (acc >= 0).any() else float("nan")
 

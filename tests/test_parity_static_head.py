@@ -58,6 +58,19 @@ def test_static_head_shapes(B, K, d, V, n_clusters, n_sel):
     _check(hc.h, hc.W, ids, V // n_clusters)
 
 
+@pytest.mark.parametrize("B,K,d,V", [
+    (2, 4, 200, 32000),       # d % 64 != 0: register-staged kernel, 128 x 128 tiles
+    (2, 4, 203, 32000),       # element loads, 128 x 128 tiles
+    (13, 10, 256, 32000),     # LDS-DMA kernel, 128 x 128 tiles, two row tiles (M = 130)
+])
+def test_static_head_wide_tiles(B, K, d, V):
+    """Shortlists wide enough for the 128 x 128-tile instances (N = 25000 token
+    ids, at least 192 tiles), ragged in both directions."""
+    hc = head_case(B, K, d, V, V, 1, trial=11)
+    ids = _static_ids(V, 1, 25000, seed=d)
+    _check(hc.h, hc.W, ids, 1)
+
+
 @pytest.mark.parametrize("B,K,V,cs,n_sel", [
     (4, 6, 8192, 128, 9),      # N even: column pairs stored as dwords
     (3, 5, 4096, 1, 301),      # N odd: one bf16 per store; M = 15 ragged

@@ -9,9 +9,9 @@
 // d = 4096).  It finds the contexts that selected the cluster and streams its
 // W slab through MFMA once per pass of up to 32 (context, position) rows,
 // staging W and the hidden rows through LDS so that global loads stay fully
-// coalesced while MFMA reads its lane-major fragments.  The same block writes -inf
-// into the dense output for every context that did not select the cluster, so
-// each dense element is written exactly once.
+// coalesced while MFMA reads its lane-major fragments.  A dense output is
+// first filled with -inf by a separate pass of whole-line stores; the head
+// then writes the shortlist's logits into it.
 
 #include "sv_common.h"
 #include "sv_internal.h"
@@ -46,6 +46,7 @@ struct HeadArgs {
   int L;                // compact row stride
   int nsel_period;      // 0: every context uses n_sel; else context x uses nsel_pos[x % period]
   int nsel_pos[kMaxK];
+  int dense_filled;     // the dense output already holds -inf everywhere (dense_fill_kernel)
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -69,21 +70,15 @@ __device__ __forceinline__ u32x4 load8(const uint16_t* row, int k, int d, int ve
   return u32x4{t4[0], t4[1], t4[2], t4[3]};
 }
 
-__global__ void __launch_bounds__(kBlock) head_mfma_kernel(HeadArgs a) {
-  __shared__ int sh_ctx[kMaxCtx];     // (b << 16) | s of every context that selected this cluster
-  __shared__ uint32_t sh_sel[kMaxCtx / 32];
+// Steps 1 and 2 of both kernels: list the contexts that selected cluster c in
+// (b, s) order (sh_ctx, count returned), and write -inf into the dense output
+// for every (context, position) that did not select it.  Every thread of the
+// block must call this.
+__device__ __forceinline__ int list_contexts(const HeadArgs& a, int c, int tok0, int ntok, int* sh_ctx,
+                                             uint32_t* sh_sel) {
   __shared__ int sh_count;
-  __shared__ __attribute__((aligned(16))) uint16_t sh_w[kSlabTok * kLdsStride];   // 33 KiB
-  __shared__ __attribute__((aligned(16))) uint16_t sh_a[kPassRows * kLdsStride];  // 16.5 KiB
-
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int c = blockIdx.x;
-  const int tok_in0 = blockIdx.y * kSlabTok;
-  const int ntok = min(kSlabTok, a.cs - tok_in0);
-  const int tok0 = c * a.cs + tok_in0;
-
-  // 1. The contexts that selected cluster c, listed in (b, s) order.
   __shared__ int sh_wcount[kWavesPerBlock];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   if (threadIdx.x == 0) sh_count = 0;
   for (int i = threadIdx.x; i < kMaxCtx / 32; i += kBlock) sh_sel[i] = 0u;
   __syncthreads();
@@ -111,19 +106,90 @@ __global__ void __launch_bounds__(kBlock) head_mfma_kernel(HeadArgs a) {
     __syncthreads();
   }
   const int nctx = min(sh_count, kMaxCtx);
-  const int K = a.K, L = a.L;
-
-  // 2. -inf for every (context, position) that did not select c.
-  if (a.dense) {
-    const int total = a.B * K * ntok;
+  if (a.dense && !a.dense_filled) {
+    const int total = a.B * a.K * ntok;
     for (int i = threadIdx.x; i < total; i += kBlock) {
       const int t = i % ntok;
       const int bk = i / ntok;
-      const int b = bk / K;
+      const int b = bk / a.K;
       if (!((sh_sel[b >> 5] >> (b & 31)) & 1u)) store_dense(a, (size_t)bk * a.V + tok0 + t, -__builtin_inff());
     }
   }
+  return nctx;
+}
+
+// Epilogue of one pass: lane holds D[m = 4*(lane/16) + i][n = lane%16] of
+// each 16-row chunk; row r of the pass is A row r0 + r.
+__device__ __forceinline__ void store_pass(const HeadArgs& a, const f32x4 (&acc)[2], const int* sh_ctx, int p0,
+                                           int r0, int nr, int tok0, int tok_in0, int my_tok, int ntok, int kgrp) {
+  if (my_tok >= ntok) return;
+  const int K = a.K;
+#pragma unroll
+  for (int mc = 0; mc < 2; ++mc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = mc * 16 + 4 * kgrp + i;
+      if (r < nr) {
+        const int rr = r0 + r;
+        const int ctx = sh_ctx[p0 + rr / K];
+        const int b = ctx >> 16, s = ctx & 0xffff, k = rr % K;
+        const float v = acc[mc][i];
+        const size_t bk = (size_t)b * K + k;
+        if (a.compact) {
+          const size_t o = bk * a.L + (size_t)s * a.cs + tok_in0 + my_tok;
+          if (a.compact_bf16) static_cast<uint16_t*>(a.compact)[o] = f32_to_bf16_rne(v);
+          else static_cast<float*>(a.compact)[o] = v;
+        }
+        if (a.dense) store_dense(a, bk * a.V + tok0 + my_tok, v);
+      }
+    }
+  }
+}
+
+// -inf over the whole dense output, in 16-byte stores (whole cache lines),
+// ahead of the head kernel, which then writes only the shortlist's logits.
+// Filling per cluster slab inside the head kernel wrote 128-byte pieces that
+// straddle lines (clusters of 501 tokens do not start on line boundaries) and
+// cost about 27 us at B=32, K=4, V=128256; with this pass the dense output
+// costs about 10 us.  (An LDS-DMA variant of the head kernel, as in the
+// static-shortlist head, measured 3-5 % slower here: with about two contexts
+// per cluster the kernel is bound by the W stream, not by LDS traffic.)
+__global__ void __launch_bounds__(kBlock) dense_fill_kernel(void* dense, size_t elems, int bf16) {
+  const uint32_t pat = bf16 ? 0xff80ff80u : 0xff800000u;
+  const size_t bytes = elems * (bf16 ? 2 : 4);
+  const size_t stride = (size_t)gridDim.x * kBlock;
+  const size_t first = (size_t)blockIdx.x * kBlock + threadIdx.x;
+  if ((uintptr_t)dense % 16 == 0) {
+    const u32x4 v = {pat, pat, pat, pat};
+    for (size_t i = first; i < bytes / 16; i += stride) reinterpret_cast<u32x4*>(dense)[i] = v;
+    for (size_t i = bytes / 16 * 16 / (bf16 ? 2 : 4) + first; i < elems; i += stride) {
+      if (bf16) static_cast<uint16_t*>(dense)[i] = 0xff80u;
+      else static_cast<uint32_t*>(dense)[i] = pat;
+    }
+  } else {
+    for (size_t i = first; i < elems; i += stride) {
+      if (bf16) static_cast<uint16_t*>(dense)[i] = 0xff80u;
+      else static_cast<uint32_t*>(dense)[i] = pat;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kBlock) head_mfma_kernel(HeadArgs a) {
+  __shared__ int sh_ctx[kMaxCtx];     // (b << 16) | s of every context that selected this cluster
+  __shared__ uint32_t sh_sel[kMaxCtx / 32];
+  __shared__ __attribute__((aligned(16))) uint16_t sh_w[kSlabTok * kLdsStride];   // 33 KiB
+  __shared__ __attribute__((aligned(16))) uint16_t sh_a[kPassRows * kLdsStride];  // 16.5 KiB
+
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int c = blockIdx.x;
+  const int tok_in0 = blockIdx.y * kSlabTok;
+  const int ntok = min(kSlabTok, a.cs - tok_in0);
+  const int tok0 = c * a.cs + tok_in0;
+
+  // 1, 2. The contexts that selected cluster c; -inf for the others.
+  const int nctx = list_contexts(a, c, tok0, ntok, sh_ctx, sh_sel);
   if (nctx == 0) return;
+  const int K = a.K;
 
   // 3. Passes of up to kPassRows A rows (row r = context p*, position k).
   //    Per stage of kStageK hidden dims the block loads its 64 W rows with
@@ -200,29 +266,7 @@ __global__ void __launch_bounds__(kBlock) head_mfma_kernel(HeadArgs a) {
           }
         }
       }
-      // Epilogue: lane holds D[m = 4*(lane/16) + i][n = lane%16] of each chunk.
-      if (my_tok < ntok) {
-#pragma unroll
-        for (int mc = 0; mc < 2; ++mc) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = mc * 16 + 4 * kgrp + i;
-            if (r < nr) {
-              const int rr = r0 + r;
-              const int ctx = sh_ctx[p0 + rr / K];
-              const int b = ctx >> 16, s = ctx & 0xffff, k = rr % K;
-              const float v = acc[mc][i];
-              const size_t bk = (size_t)b * K + k;
-              if (a.compact) {
-                const size_t o = bk * L + (size_t)s * a.cs + tok_in0 + my_tok;
-                if (a.compact_bf16) static_cast<uint16_t*>(a.compact)[o] = f32_to_bf16_rne(v);
-                else static_cast<float*>(a.compact)[o] = v;
-              }
-              if (a.dense) store_dense(a, bk * a.V + tok0 + my_tok, v);
-            }
-          }
-        }
-      }
+      store_pass(a, acc, sh_ctx, p0, r0, nr, tok0, tok_in0, my_tok, ntok, kgrp);
     }
   }
 }
@@ -253,6 +297,13 @@ hipError_t launch_head(const void* h, const void* W, const int32_t* cluster_ids,
   for (int i = 0; nsel_pos && i < nsel_period; ++i) a.nsel_pos[i] = nsel_pos[i];
   const int n_clusters = V / cluster_size;
   const dim3 grid((unsigned)n_clusters, (unsigned)((cluster_size + kSlabTok - 1) / kSlabTok));
+  if (dense) {
+    const size_t elems = (size_t)B * K * V;
+    const size_t chunks = (elems * (dense_dtype == 1 ? 2 : 4) + 16 * kBlock - 1) / (16 * kBlock);
+    const unsigned blocks = (unsigned)(chunks < 4096 ? (chunks > 0 ? chunks : 1) : 4096);
+    hipLaunchKernelGGL(dense_fill_kernel, dim3(blocks), dim3(kBlock), 0, st, dense, elems, a.dense_bf16);
+    a.dense_filled = 1;
+  }
   hipLaunchKernelGGL(head_mfma_kernel, grid, dim3(kBlock), 0, st, a);
   return hipGetLastError();
 }

@@ -142,18 +142,21 @@ def copy_reference(dev, gib=1.0, reps=5):
 
 def cold_warm(call, input_bytes, dev, reps=20):
     """Median HIP-event time of one call with its inputs cache-resident (warm)
-    and after a 512 MiB write that evicts them from the 256 MB last-level
-    cache (cold).  Only meaningful for inputs well under 256 MB."""
+    and after reading 512 MiB of other data, which evicts them from the
+    256 MB last-level cache (cold).  The eviction reads rather than writes so
+    that the cold call does not also pay for writing back dirty lines.  Only
+    meaningful for inputs well under 256 MB."""
     import numpy as np
     import torch
-    flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
+    flush = torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
     out = {}
     for kind in ("warm", "cold"):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         call()
         for e0, e1 in ev:
             if kind == "cold":
-                flush.fill_(float(len(out)))
+                torch.sum(flush, dim=0, out=sink)
             e0.record()
             call()
             e1.record()
@@ -162,7 +165,7 @@ def cold_warm(call, input_bytes, dev, reps=20):
     del flush
     out["input_bytes"] = input_bytes
     out["cold_gbs"] = input_bytes / (out["cold_us"] * 1e-6) / 1e9
-    out["note"] = "median of %d calls, events around the call only; cold = after a 512 MiB fill kernel" % reps
+    out["note"] = "median of %d calls, events around the call only; cold = after a 512 MiB read" % reps
     return out
 
 

@@ -23,13 +23,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSlabTok = 64;       // tokens per block: 4 waves x 16 MFMA columns
 constexpr int kPassRows = 32;      // A rows per pass over W: two 16-row MFMA chunks
-constexpr int kStageK = 256;       // hidden dims per LDS stage
+constexpr int kStageK = 256;       // hidden dims per LDS stage (128 and 512 measured slower)
 constexpr int kLdsStride = kStageK + 8;  // bf16 per LDS row: 16-byte skew per row, no bank conflicts
-constexpr int kWLoads = kSlabTok * kStageK / 8 / kBlock;   // 16-byte W loads per thread per stage (8)
-constexpr int kALoads = kPassRows * kStageK / 8 / kBlock;  // 16-byte A loads per thread per stage (4)
-constexpr int kDepth = 1;          // stages of loads in flight ahead of the MFMAs (deeper measured slower)
 constexpr int kMaxCtx = 1024;      // contexts listed per cluster (host-checked: B <= kMaxCtx)
 
 struct HeadArgs {
@@ -74,16 +70,18 @@ __device__ __forceinline__ u32x4 load8(const uint16_t* row, int k, int d, int ve
 // (b, s) order (sh_ctx, count returned), and write -inf into the dense output
 // for every (context, position) that did not select it.  Every thread of the
 // block must call this.
+template <int NTH>
 __device__ __forceinline__ int list_contexts(const HeadArgs& a, int c, int tok0, int ntok, int* sh_ctx,
                                              uint32_t* sh_sel) {
+  constexpr int NW = NTH / kWave;
   __shared__ int sh_count;
-  __shared__ int sh_wcount[kWavesPerBlock];
+  __shared__ int sh_wcount[NW];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   if (threadIdx.x == 0) sh_count = 0;
-  for (int i = threadIdx.x; i < kMaxCtx / 32; i += kBlock) sh_sel[i] = 0u;
+  for (int i = threadIdx.x; i < kMaxCtx / 32; i += NTH) sh_sel[i] = 0u;
   __syncthreads();
   const int entries = a.B * a.S;
-  for (int e0 = 0; e0 < entries; e0 += kBlock) {
+  for (int e0 = 0; e0 < entries; e0 += NTH) {
     const int e = e0 + threadIdx.x;
     const int used = a.nsel_period ? a.nsel_pos[(e / a.S) % a.nsel_period] : a.n_sel;
     const bool hit = e < entries && e % a.S < used && a.cids[e] == c;
@@ -91,7 +89,7 @@ __device__ __forceinline__ int list_contexts(const HeadArgs& a, int c, int tok0,
     if (lane == 0) sh_wcount[wave] = __popcll(mask);
     __syncthreads();
     int before = sh_count, tot = 0;
-    for (int w = 0; w < kWavesPerBlock; ++w) {
+    for (int w = 0; w < NW; ++w) {
       if (w < wave) before += sh_wcount[w];
       tot += sh_wcount[w];
     }
@@ -108,7 +106,7 @@ __device__ __forceinline__ int list_contexts(const HeadArgs& a, int c, int tok0,
   const int nctx = min(sh_count, kMaxCtx);
   if (a.dense && !a.dense_filled) {
     const int total = a.B * a.K * ntok;
-    for (int i = threadIdx.x; i < total; i += kBlock) {
+    for (int i = threadIdx.x; i < total; i += NTH) {
       const int t = i % ntok;
       const int bk = i / ntok;
       const int b = bk / a.K;
@@ -174,35 +172,51 @@ __global__ void __launch_bounds__(kBlock) dense_fill_kernel(void* dense, size_t 
   }
 }
 
-__global__ void __launch_bounds__(kBlock) head_mfma_kernel(HeadArgs a) {
+// SLAB tokens per block (SLAB / 16 waves of 16 MFMA columns); DEPTH stages
+// of loads in flight in registers.  kFull: d % kStageK == 0 and 16-byte
+// aligned rows, so every load is a whole 16-byte piece inside its row; the
+// loads are then issued unconditionally (W rows past the slab re-read its
+// last row, A rows past the pass read h's first row, stages past the end
+// re-read the last one; none of it reaches an output), which keeps the
+// compiler's wait counts partial.  Otherwise loads are guarded per lane and
+// zero-filled past d.
+template <int SLAB, int DEPTH, bool kFull>
+__global__ void __launch_bounds__(SLAB / 16 * kWave) head_mfma_kernel(HeadArgs a) {
+  constexpr int NTH = SLAB / 16 * kWave;
+  constexpr int kCols = kStageK / 8, kRowsPerLoad = NTH / kCols;
+  constexpr int kWL = SLAB / kRowsPerLoad;        // 16-byte W loads per thread per stage
+  constexpr int kAL = kPassRows / kRowsPerLoad;   // 16-byte A loads per thread per stage
+  static_assert(SLAB % kRowsPerLoad == 0 && kPassRows % kRowsPerLoad == 0, "load split");
   __shared__ int sh_ctx[kMaxCtx];     // (b << 16) | s of every context that selected this cluster
   __shared__ uint32_t sh_sel[kMaxCtx / 32];
-  __shared__ __attribute__((aligned(16))) uint16_t sh_w[kSlabTok * kLdsStride];   // 33 KiB
-  __shared__ __attribute__((aligned(16))) uint16_t sh_a[kPassRows * kLdsStride];  // 16.5 KiB
+  __shared__ __attribute__((aligned(16))) uint16_t sh_w[SLAB * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sh_a[kPassRows * kLdsStride];
 
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int c = blockIdx.x;
-  const int tok_in0 = blockIdx.y * kSlabTok;
-  const int ntok = min(kSlabTok, a.cs - tok_in0);
+  const int tok_in0 = blockIdx.y * SLAB;
+  const int ntok = min(SLAB, a.cs - tok_in0);
   const int tok0 = c * a.cs + tok_in0;
 
   // 1, 2. The contexts that selected cluster c; -inf for the others.
-  const int nctx = list_contexts(a, c, tok0, ntok, sh_ctx, sh_sel);
+  const int nctx = list_contexts<NTH>(a, c, tok0, ntok, sh_ctx, sh_sel);
   if (nctx == 0) return;
   const int K = a.K;
 
   // 3. Passes of up to kPassRows A rows (row r = context p*, position k).
-  //    Per stage of kStageK hidden dims the block loads its 64 W rows with
-  //    fully coalesced 16-byte loads (each wave instruction covers two rows x
-  //    512 bytes) and the pass's A rows likewise, stores them to LDS, and every
+  //    Per stage of kStageK hidden dims the block loads its W rows with fully
+  //    coalesced 16-byte loads (each wave instruction covers two rows x 512
+  //    bytes) and the pass's A rows likewise, stores them to LDS, and every
   //    wave reads the lane-major MFMA fragments of its 16 tokens from LDS.
-  //    Loads run kDepth stages ahead in registers, so several hundred KiB are
-  //    in flight per CU while the MFMAs of the current stage execute.
   const int my_tok = wave * 16 + (lane & 15);  // MFMA column of this lane
   const int kgrp = lane >> 4;                  // 0..3: which 8 of the 32 k's
-  constexpr int kCols = kStageK / 8, kRowsPerLoad = kBlock / kCols;
   const int lrow = threadIdx.x / kCols, c8 = (threadIdx.x % kCols) * 8;
-  const uint16_t* wbase = a.W + (size_t)(tok0 + lrow) * a.d;
+  const uint16_t* wrow[kWL];
+#pragma unroll
+  for (int i = 0; i < kWL; ++i) {
+    const int r = kRowsPerLoad * i + lrow;
+    wrow[i] = (kFull || r < ntok) ? a.W + (size_t)(tok0 + min(r, ntok - 1)) * a.d : nullptr;
+  }
   const int ctx_per_pass = max(1, kPassRows / K);
   const int nstage = (a.d + kStageK - 1) / kStageK;
   for (int p0 = 0; p0 < nctx; p0 += ctx_per_pass) {
@@ -210,58 +224,69 @@ __global__ void __launch_bounds__(kBlock) head_mfma_kernel(HeadArgs a) {
     const int rows = np * K;
     for (int r0 = 0; r0 < rows; r0 += kPassRows) {
       const int nr = min(kPassRows, rows - r0);
-      const uint16_t* arow[kALoads];
+      const uint16_t* arow[kAL];
 #pragma unroll
-      for (int i = 0; i < kALoads; ++i) {
+      for (int i = 0; i < kAL; ++i) {
         const int r = kRowsPerLoad * i + lrow;
-        arow[i] = nullptr;
+        arow[i] = kFull ? a.h : nullptr;
         if (r < nr) {
           const int rr = r0 + r;
           const int ctx = sh_ctx[p0 + rr / K];
           arow[i] = a.h + ((size_t)(ctx >> 16) * K + rr % K) * a.d;
         }
       }
-      u32x4 wreg[kDepth][kWLoads], areg[kDepth][kALoads];
-      auto load_stage = [&](int st, u32x4 (&wr)[kWLoads], u32x4 (&ar)[kALoads]) {
-        const int k = st * kStageK + c8;
-        const bool live = st < nstage;
+      u32x4 wreg[DEPTH][kWL], areg[DEPTH][kAL];
+      auto load_stage = [&](int st, u32x4 (&wr)[kWL], u32x4 (&ar)[kAL]) {
+        if (kFull) {
+          const int k = min(st, nstage - 1) * kStageK + c8;
 #pragma unroll
-        for (int i = 0; i < kWLoads; ++i)
-          wr[i] = (live && kRowsPerLoad * i + lrow < ntok)
-                      ? load8(wbase + (size_t)(kRowsPerLoad * i) * a.d, k, a.d, a.vec_ok)
-                      : u32x4{0u, 0u, 0u, 0u};
+          for (int i = 0; i < kWL; ++i) wr[i] = *reinterpret_cast<const u32x4*>(wrow[i] + k);
 #pragma unroll
-        for (int i = 0; i < kALoads; ++i)
-          ar[i] = (live && arow[i]) ? load8(arow[i], k, a.d, a.vec_ok) : u32x4{0u, 0u, 0u, 0u};
+          for (int i = 0; i < kAL; ++i) ar[i] = *reinterpret_cast<const u32x4*>(arow[i] + k);
+        } else {
+          const int k = st * kStageK + c8;
+          const bool live = st < nstage;
+#pragma unroll
+          for (int i = 0; i < kWL; ++i)
+            wr[i] = (live && wrow[i]) ? load8(wrow[i], k, a.d, a.vec_ok) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int i = 0; i < kAL; ++i)
+            ar[i] = (live && arow[i]) ? load8(arow[i], k, a.d, a.vec_ok) : u32x4{0u, 0u, 0u, 0u};
+        }
       };
       f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
       const bool two = nr > 16;
 #pragma unroll
-      for (int j = 0; j < kDepth; ++j) load_stage(j, wreg[j], areg[j]);
-      for (int st0 = 0; st0 < nstage; st0 += kDepth) {
+      for (int j = 0; j < DEPTH; ++j) {
+        load_stage(j, wreg[j], areg[j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      for (int st0 = 0; st0 < nstage; st0 += DEPTH) {
 #pragma unroll
-        for (int j = 0; j < kDepth; ++j) {
+        for (int j = 0; j < DEPTH; ++j) {
           const int st = st0 + j;
-          if (st >= nstage) break;
           __syncthreads();
 #pragma unroll
-          for (int i = 0; i < kWLoads; ++i)
+          for (int i = 0; i < kWL; ++i)
             *reinterpret_cast<u32x4*>(&sh_w[(kRowsPerLoad * i + lrow) * kLdsStride + c8]) = wreg[j][i];
 #pragma unroll
-          for (int i = 0; i < kALoads; ++i)
+          for (int i = 0; i < kAL; ++i)
             *reinterpret_cast<u32x4*>(&sh_a[(kRowsPerLoad * i + lrow) * kLdsStride + c8]) = areg[j][i];
           __syncthreads();
-          load_stage(st + kDepth, wreg[j], areg[j]);
+          load_stage(st + DEPTH, wreg[j], areg[j]);
+          if (st < nstage) {  // uniform; the loads above stay outside it
 #pragma unroll
-          for (int q = 0; q < kStageK / 32; ++q) {
-            const int kofs = q * 32 + kgrp * 8;
-            const u32x4 bv = *reinterpret_cast<const u32x4*>(&sh_w[my_tok * kLdsStride + kofs]);
-            const bf16x8 bfrag = __builtin_bit_cast(bf16x8, bv);
-            const u32x4 a0 = *reinterpret_cast<const u32x4*>(&sh_a[(lane & 15) * kLdsStride + kofs]);
-            acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), bfrag, acc[0], 0, 0, 0);
-            if (two) {
-              const u32x4 a1 = *reinterpret_cast<const u32x4*>(&sh_a[(16 + (lane & 15)) * kLdsStride + kofs]);
-              acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), bfrag, acc[1], 0, 0, 0);
+            for (int q = 0; q < kStageK / 32; ++q) {
+              const int kofs = q * 32 + kgrp * 8;
+              const u32x4 bv = *reinterpret_cast<const u32x4*>(&sh_w[my_tok * kLdsStride + kofs]);
+              const bf16x8 bfrag = __builtin_bit_cast(bf16x8, bv);
+              const u32x4 a0 = *reinterpret_cast<const u32x4*>(&sh_a[(lane & 15) * kLdsStride + kofs]);
+              acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), bfrag, acc[0], 0, 0, 0);
+              if (two) {
+                const u32x4 a1 = *reinterpret_cast<const u32x4*>(&sh_a[(16 + (lane & 15)) * kLdsStride + kofs]);
+                acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), bfrag, acc[1], 0, 0,
+                                                                 0);
+              }
             }
           }
         }
@@ -269,6 +294,13 @@ __global__ void __launch_bounds__(kBlock) head_mfma_kernel(HeadArgs a) {
       store_pass(a, acc, sh_ctx, p0, r0, nr, tok0, tok_in0, my_tok, ntok, kgrp);
     }
   }
+}
+
+template <int SLAB, int DEPTH>
+void launch_head_cfg(const HeadArgs& a, int n_clusters, bool full, hipStream_t st) {
+  const dim3 grid((unsigned)n_clusters, (unsigned)((a.cs + SLAB - 1) / SLAB)), block(SLAB / 16 * kWave);
+  if (full) hipLaunchKernelGGL((head_mfma_kernel<SLAB, DEPTH, true>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((head_mfma_kernel<SLAB, DEPTH, false>), grid, block, 0, st, a);
 }
 
 }  // namespace
@@ -296,7 +328,6 @@ hipError_t launch_head(const void* h, const void* W, const int32_t* cluster_ids,
   a.nsel_period = nsel_pos ? nsel_period : 0;
   for (int i = 0; nsel_pos && i < nsel_period; ++i) a.nsel_pos[i] = nsel_pos[i];
   const int n_clusters = V / cluster_size;
-  const dim3 grid((unsigned)n_clusters, (unsigned)((cluster_size + kSlabTok - 1) / kSlabTok));
   if (dense) {
     const size_t elems = (size_t)B * K * V;
     const size_t chunks = (elems * (dense_dtype == 1 ? 2 : 4) + 16 * kBlock - 1) / (16 * kBlock);
@@ -304,7 +335,10 @@ hipError_t launch_head(const void* h, const void* W, const int32_t* cluster_ids,
     hipLaunchKernelGGL(dense_fill_kernel, dim3(blocks), dim3(kBlock), 0, st, dense, elems, a.dense_bf16);
     a.dense_filled = 1;
   }
-  hipLaunchKernelGGL(head_mfma_kernel, grid, dim3(kBlock), 0, st, a);
+  const bool full = a.vec_ok && d % kStageK == 0;
+  // 64-token slabs with one stage in flight: 32-token slabs (more, smaller
+  // blocks) and two stages in flight both measured slower.
+  launch_head_cfg<64, 1>(a, n_clusters, full, st);
   return hipGetLastError();
 }
 

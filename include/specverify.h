@@ -17,8 +17,14 @@
  *     row i; at the first mismatch emit that argmax and stop.  LLMs-from-Scratch
  *     lesson 25, "Greedy case".
  *   - Shortlisted drafter head: draft logits only on the union of the clusters
- *     each context selects.  DynaSpec summary (lowest.today, arXiv 2510.13847),
- *     "Model architecture", items 1, 3 and 4.
+ *     each context selects (per context, or per context and draft position),
+ *     and verify of a draft stored as those shortlist logits.  DynaSpec
+ *     summary (lowest.today, arXiv 2510.13847), "Model architecture", items
+ *     1, 3 and 4.
+ *   - Drafter head on one static shortlist shared by every context (the
+ *     FR-Spec / VocabTrim baselines of the DynaSpec summary).
+ *   - KV-cache commit of the accepted drafts after a verify step.
+ *     Speculative Decoding lesson, "KV-cache management".
  *
  * Conventions shared by every entry point:
  *   - All array arguments are device pointers (hipMalloc / torch CUDA tensors),

@@ -330,8 +330,9 @@ def main():
         n = res[0].cpu().numpy()
         rows = np.where(n >= 0, np.minimum(n, K - 1) + 1, 0) if K > 0 else np.zeros(B)
         need = int(2 * rows.sum()) * V * esz            # target and draft rows 0..min(n, K-1)
-        stats_ms = float(sum(ee_launch[0:2 * K:2]))       # the per-position statistics launches
-        decide_ms = float(sum(ee_launch[1:2 * K:2]))
+        # launches 0..K-1: position i's statistics (and the decision of i - 1),
+        # then the sampling pass (decides K - 1) and the pick
+        phase_ms = float(sum(ee_launch[0:K]))
         early = {
             "mode": "sample_early_exit",
             "value": B * (K + 1) / (ee_ms * 1e-3),
@@ -340,9 +341,10 @@ def main():
             "outputs_identical_to_full_schedule": same,
             "rows_read_fraction": float(rows.sum()) / max(1, B * K),
             "statistics_bytes_needed": need,
-            "statistics_ms": stats_ms,
-            "decision_ms": decide_ms,
-            "statistics_gbs": need / (stats_ms * 1e-3) / 1e9 if stats_ms > 0 else None,
+            "phase_launches_ms": phase_ms,
+            "sampling_ms": float(ee_launch[K]) if len(ee_launch) > K else None,
+            "pick_ms": float(ee_launch[K + 1]) if len(ee_launch) > K + 1 else None,
+            "statistics_gbs": need / (phase_ms * 1e-3) / 1e9 if phase_ms > 0 else None,
             "kernels_ms": {"launches": ee_launch, "events_step": ee_ev},
         }
 
@@ -359,8 +361,8 @@ def main():
         rows = np.where(n >= 0, np.minimum(n, K - 1) + 1, 0) if K > 0 else np.zeros(B, dtype=np.int64)
         dom_bytes = int(2 * rows.sum()) * V * esz
         step_bytes = dom_bytes + int((n == K).sum()) * V * esz
-        dom_name = "ee_stats_kernel, all positions (statistics of the rows up to each first rejection)"
-        dom_ms = float(sum(launch_ms[0:2 * K:2])) if K > 0 else launch_ms[0]
+        dom_name = "ee_phase_kernel, all positions (statistics of the rows up to each first rejection)"
+        dom_ms = float(sum(launch_ms[0:K])) if K > 0 else launch_ms[0]
     else:
         step_bytes = B * (K + 1) * V * esz
         dom_bytes = step_bytes

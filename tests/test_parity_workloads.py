@@ -97,6 +97,40 @@ def test_b64_k4_mean_tokens_vs_expectation(sweep):
     assert abs(mean - expect.mean()) < 5 * se
 
 
+def test_acceptance_falls_as_divergence_grows():
+    """The B=64, K=4, V=151936 sweep (draft noise sigma 0.1, 0.5, 1.0, 2.0):
+    the mean KL(P_t || P_d) grows and the GPU's mean accepted length falls
+    with it (the speculative-sampling pages' observation that acceptance
+    drops as the draft diverges), each mean within 5 standard errors of the
+    exact expectation from beta = sum_v min(P_t, P_d)."""
+    import speculative_sampling_verification_vocab_amd as sv
+    kls, means = [], []
+    for sweep in range(4):
+        c = workload_case("b64_k4_v151936_bf16", sweep=sweep, device=DEV)
+        B, K, T = c.B, c.K, c.temperature
+        lpt = torch.log_softmax(c.target[:, :K].double() / T, -1)
+        lpd = torch.log_softmax(c.draft.double() / T, -1)
+        kls.append(float((lpt.exp() * (lpt - lpd)).sum(-1).mean()))
+        beta = torch.minimum(lpt.exp(), lpd.exp()).sum(-1).cpu().numpy()
+        expect, prod = np.ones(B), np.ones(B)
+        for i in range(K):
+            prod = prod * beta[:, i]
+            expect += prod
+        vals = []
+        for tr in range(20):
+            tok = gumbel_max_tokens(c.draft, T, (0, 3, sweep, 2, 2000 + tr))
+            uni = verify_uniforms(B, K, (0, 3, sweep, 3, 2000 + tr), DEV)
+            n, _ = sv.spec_verify(c.target, c.draft, tok, uni, T)
+            vals.append((n.double() + 1).cpu().numpy())
+        v = np.concatenate(vals)
+        means.append(v.mean())
+        se = v.std() / math.sqrt(v.size)
+        print(f"sigma idx {sweep}: KL {kls[-1]:.4f} mean tokens {v.mean():.4f} exact {expect.mean():.4f}", flush=True)
+        assert abs(v.mean() - expect.mean()) < 5 * se + 1e-9
+    assert all(kls[i] < kls[i + 1] for i in range(3)), kls
+    assert all(means[i] > means[i + 1] for i in range(3)), means
+
+
 @pytest.mark.timeout(900)
 def test_b256_k7_v262144_bf16_fifty_seeds():
     """Full B=256, K=7, V=262144 batches, 50 seeds, in the configuration the

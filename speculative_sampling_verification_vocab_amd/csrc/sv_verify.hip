@@ -108,14 +108,6 @@ __device__ __forceinline__ int sparse_rank(const VerifyArgs& a, int b, int i, in
   return -1;
 }
 
-// Index of token v in the compact draft row (b, i), or -1 off the shortlist.
-__device__ __forceinline__ int sparse_index(const VerifyArgs& a, int b, int i, int v) {
-  if (v < 0 || v >= a.V) return -1;
-  const int c = v / a.cs;
-  const int r = sparse_rank(a, b, i, c);
-  return r < 0 ? -1 : r * a.cs + (v - c * a.cs);
-}
-
 // Storage bits of the draft logits at ids v0 .. v0 + kVec - 1 of row (b, i):
 // the compact entry where the id is on the shortlist, -inf elsewhere.
 // Rank lookups go through `tab` (rank of every cluster of the row, in LDS)

@@ -613,12 +613,19 @@ __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
   int n;
   if constexpr (kFromRows) {
     // Early exit: a sequence that reached position K - 1 is decided here (by
-    // every wave; wave 0 of the first block writes the outputs); the others
-    // ended earlier and left their record in rows[b].
+    // wave 0 of each block, which shares the record through LDS; wave 0 of
+    // the first block writes the outputs); the others ended earlier and left
+    // their record in rows[b].
     if (K == 0) {
       n = 0;
     } else if (K == 1 || a.cont[(size_t)(K - 2) * a.B + b] != 0) {
-      ee_decide(a, b, K - 1, g == 0 && threadIdx.x < kWave, &sr);
+      __shared__ SampleRowInfo sh_sr;
+      if (wave == 0) {
+        ee_decide(a, b, K - 1, g == 0, &sr);
+        if (lane == 0) sh_sr = sr;
+      }
+      __syncthreads();
+      sr = sh_sr;
       n = sr.n;
     } else {
       sr = a.rows[b];
@@ -956,7 +963,7 @@ __global__ void __launch_bounds__(kBlock) pick_kernel(VerifyArgs a) {
 constexpr int kEETPW = 1;
 
 // Phase i of the early-exit schedule: statistics of target and draft row i
-// for the sequences that accepted positions 0..i-1.  For i > 0 every wave
+// for the sequences that accepted positions 0..i-1.  For i > 0 every block
 // first decides position i - 1 of its sequence (its statistics are complete:
 // the previous launch produced them); block 0 of the target row writes the
 // outputs of that decision.
@@ -974,8 +981,16 @@ __global__ void __launch_bounds__(kBlock) ee_phase_kernel(VerifyArgs a, int i) {
       if (writer && threadIdx.x == 0) a.cont[(size_t)(i - 1) * a.B + b] = 0;
       return;
     }
-    SampleRowInfo sr;
-    if (!ee_decide(a, b, i - 1, writer, &sr)) return;
+    // Wave 0 decides for the block; the others wait for its answer.  (Every
+    // wave deciding for itself measured 4 % slower over the phases.)
+    __shared__ int sh_go;
+    if (wave == 0) {
+      SampleRowInfo sr;
+      const int go = ee_decide(a, b, i - 1, writer, &sr);
+      if ((threadIdx.x & (kWave - 1)) == 0) sh_go = go;
+    }
+    __syncthreads();
+    if (!sh_go) return;
   }
   for (int j = 0; j < kEETPW; ++j) {
     const int t = (g * kEETPW + j) * kWavesPerBlock + wave;

@@ -44,6 +44,7 @@ struct VerifyShape {
   int NT_s;      // sampling-pass tiles per row
   int NG_s;      // sampling-pass blocks per row
   int TPW_s;     // sampling-pass tiles per wave
+  int TPW_e;     // early-exit phases: statistics tiles per wave
 };
 
 struct VerifyWorkspace {

@@ -61,6 +61,7 @@ struct VerifyArgs {
   int NT, NG;            // statistics pass: tiles (kTile ids) and blocks per row
   int NTs, NGs;          // sampling pass: tiles (kTileS ids) and blocks per row
   int TPWs;              // sampling pass: tiles per wave
+  int TPWe;              // early-exit phases: statistics tiles per wave
   float s_hi, s_lo;      // log2(e)/T as a float pair
   float dmin;            // clamp for x - m in the accurate exponential: -200 / s_hi
   double s64;            // log2(e)/T in double
@@ -955,12 +956,14 @@ __global__ void __launch_bounds__(kBlock) pick_kernel(VerifyArgs a) {
 // decisions bit for bit.
 // ---------------------------------------------------------------------------
 
-// Statistics tiles per wave in the early-exit phases.  (Two or four, which
-// amortise the decision prologue over more tiles, measured within 2 % at
-// B=256 and slower for small batches.  Loading the tile before the decision,
-// so that the two latencies overlap, measured 13 % slower over the phases:
-// the tiles of sequences that reject at i - 1 are read for nothing.)
-constexpr int kEETPW = 1;
+// Statistics tiles per wave in the early-exit phases (a.TPWe): two when the
+// phase has at least kEEBlocksForTwo blocks at one tile per wave, which halves
+// the decisions taken per position (B=256, K=7, V=262144: phases 255 -> 242
+// us), else one (two measured 3-16 % slower for B=8 and B=64).  Loading the
+// tile before the decision, so that the two latencies overlap, measured 13 %
+// slower over the phases: the tiles of sequences that reject at i - 1 are
+// read for nothing.
+constexpr int kEEBlocksForTwo = 4096;  // phase blocks at one tile per wave from which waves take two
 
 // Phase i of the early-exit schedule: statistics of target and draft row i
 // for the sequences that accepted positions 0..i-1.  For i > 0 every block
@@ -970,7 +973,7 @@ constexpr int kEETPW = 1;
 template <typename T, bool kAligned>
 __global__ void __launch_bounds__(kBlock) ee_phase_kernel(VerifyArgs a, int i) {
   const int wave = threadIdx.x / kWave;
-  const int NGe = (a.NT + kEETPW * kWavesPerBlock - 1) / (kEETPW * kWavesPerBlock);
+  const int NGe = (a.NT + a.TPWe * kWavesPerBlock - 1) / (a.TPWe * kWavesPerBlock);
   const int b = blockIdx.x / (2 * NGe), rem = blockIdx.x % (2 * NGe);
   const int which = rem / NGe, g = rem % NGe;
   if (i > 0) {
@@ -992,8 +995,8 @@ __global__ void __launch_bounds__(kBlock) ee_phase_kernel(VerifyArgs a, int i) {
     __syncthreads();
     if (!sh_go) return;
   }
-  for (int j = 0; j < kEETPW; ++j) {
-    const int t = (g * kEETPW + j) * kWavesPerBlock + wave;
+  for (int j = 0; j < a.TPWe; ++j) {
+    const int t = (g * a.TPWe + j) * kWavesPerBlock + wave;
     if (t >= a.NT) break;
     stats_row_block<T, kAligned>(a, b, which == 0 ? i : a.K + i, t / kWavesPerBlock);
   }
@@ -1137,6 +1140,7 @@ VerifyShape make_shape(int B, int K, int V, int dtype, bool aligned) {
     }
   }
   s.NG_s = (s.NT_s + s.TPW_s * kWavesPerBlock - 1) / (s.TPW_s * kWavesPerBlock);
+  s.TPW_e = (long long)B * 2 * s.NG >= kEEBlocksForTwo ? 2 : 1;
   return s;
 }
 
@@ -1192,6 +1196,7 @@ static VerifyArgs verify_args(const VerifyShape& s, const VerifyIO& io, const Ve
   a.NTs = s.NT_s;
   a.NGs = s.NG_s;
   a.TPWs = s.TPW_s;
+  a.TPWe = s.TPW_e;
   a.s64 = log2e_over(io.temperature);
   a.s_hi = (float)a.s64;
   a.s_lo = (float)(a.s64 - (double)a.s_hi);
@@ -1273,7 +1278,7 @@ hipError_t launch_early_exit_pipeline(const VerifyShape& s, const VerifyIO& io, 
     ++k;
   };
   hipError_t e = hipSuccess;
-  const int NGe = (s.NT + kEETPW * kWavesPerBlock - 1) / (kEETPW * kWavesPerBlock);
+  const int NGe = (s.NT + s.TPW_e * kWavesPerBlock - 1) / (s.TPW_e * kWavesPerBlock);
   const dim3 phase_grid((unsigned)((size_t)s.B * 2 * NGe));
   for (int i = 0; i < s.K && e == hipSuccess; ++i) {
     record();

@@ -64,6 +64,7 @@ def check_early_exit(case, vs_oracle=True):
     (5, 0, 9000, "bf16"),      # no draft positions: bonus token only
     (4, 20, 3000, "bf16"),     # K > 16: the full schedule's generic combine path
     (3, 4, 300000, "bf16"),    # more than 64 statistics tiles per row
+    (512, 2, 20000, "bf16"),   # enough phase blocks for two tiles per wave; 5 tiles per row (odd)
 ])
 def test_early_exit_shapes(B, K, V, dtype):
     print(f"case B={B} K={K} V={V} {dtype}", flush=True)

@@ -25,7 +25,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPassRows = 32;      // A rows per pass over W: two 16-row MFMA chunks
 constexpr int kStageK = 256;       // hidden dims per LDS stage (128 and 512 measured slower)
-constexpr int kLdsStride = kStageK + 8;  // bf16 per LDS row: 16-byte skew per row, no bank conflicts
+// LDS rows of a stage are unpadded; the 16-byte chunks of row r are stored
+// XOR-permuted by r % 16, so a fragment read (16 rows, one chunk) and a row
+// store both touch distinct banks.  Without the 16-byte row skew the block
+// needs 53.4 KB, and three blocks fit a CU instead of two (1-2 % faster).
+constexpr int kLdsStride = kStageK;
+// Element offset of (row, 8-aligned column) in a staged LDS tile.
+__device__ __forceinline__ int lds_at(int row, int col) { return row * kLdsStride + (((col >> 3) ^ (row & 15)) << 3); }
 constexpr int kMaxCtx = 1024;      // contexts listed per cluster (host-checked: B <= kMaxCtx)
 
 struct HeadArgs {
@@ -268,22 +274,22 @@ __global__ void __launch_bounds__(SLAB / 16 * kWave) head_mfma_kernel(HeadArgs a
           __syncthreads();
 #pragma unroll
           for (int i = 0; i < kWL; ++i)
-            *reinterpret_cast<u32x4*>(&sh_w[(kRowsPerLoad * i + lrow) * kLdsStride + c8]) = wreg[j][i];
+            *reinterpret_cast<u32x4*>(&sh_w[lds_at(kRowsPerLoad * i + lrow, c8)]) = wreg[j][i];
 #pragma unroll
           for (int i = 0; i < kAL; ++i)
-            *reinterpret_cast<u32x4*>(&sh_a[(kRowsPerLoad * i + lrow) * kLdsStride + c8]) = areg[j][i];
+            *reinterpret_cast<u32x4*>(&sh_a[lds_at(kRowsPerLoad * i + lrow, c8)]) = areg[j][i];
           __syncthreads();
           load_stage(st + DEPTH, wreg[j], areg[j]);
           if (st < nstage) {  // uniform; the loads above stay outside it
 #pragma unroll
             for (int q = 0; q < kStageK / 32; ++q) {
               const int kofs = q * 32 + kgrp * 8;
-              const u32x4 bv = *reinterpret_cast<const u32x4*>(&sh_w[my_tok * kLdsStride + kofs]);
+              const u32x4 bv = *reinterpret_cast<const u32x4*>(&sh_w[lds_at(my_tok, kofs)]);
               const bf16x8 bfrag = __builtin_bit_cast(bf16x8, bv);
-              const u32x4 a0 = *reinterpret_cast<const u32x4*>(&sh_a[(lane & 15) * kLdsStride + kofs]);
+              const u32x4 a0 = *reinterpret_cast<const u32x4*>(&sh_a[lds_at(lane & 15, kofs)]);
               acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), bfrag, acc[0], 0, 0, 0);
               if (two) {
-                const u32x4 a1 = *reinterpret_cast<const u32x4*>(&sh_a[(16 + (lane & 15)) * kLdsStride + kofs]);
+                const u32x4 a1 = *reinterpret_cast<const u32x4*>(&sh_a[lds_at(16 + (lane & 15), kofs)]);
                 acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), bfrag, acc[1], 0, 0,
                                                                  0);
               }

@@ -83,7 +83,7 @@ size_t verify_workspace_layout(const VerifyShape& s, int mode, void* base, Verif
 int sample_launches(const VerifyShape& s);
 hipError_t launch_sample_pipeline(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws,
                                   hipStream_t st, void* const* events, int n_events);
-// SAMPLE_EARLY_EXIT: K + 2 launches (position i's statistics, each wave
+// SAMPLE_EARLY_EXIT: K + 2 launches (position i's statistics, each block
 // first deciding position i - 1 of its sequence; then sampling, which decides
 // position K - 1, and pick); events as above.
 int early_exit_launches(const VerifyShape& s);

@@ -341,8 +341,9 @@ __device__ __forceinline__ bool accept_test(const VerifyArgs& a, int d, double x
   return (double)u < thr;
 }
 
-// Decision of position j for sequence b, taken by one wave (every wave that
-// needs it takes it; the results are identical).  Returns 1 if the sequence
+// Decision of position j for sequence b, taken by one wave (wave 0 of every
+// block that needs it, which shares the result through LDS; every block gets
+// the same result).  Returns 1 if the sequence
 // accepted position j and has positions left, else 0 with *sr filled for the
 // sampling pass (sr->n = j at a rejection, K when every position was
 // accepted, -1 for a fault).  The writer wave also stores the outputs that

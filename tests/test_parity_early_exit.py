@@ -65,6 +65,7 @@ def check_early_exit(case, vs_oracle=True):
     (4, 20, 3000, "bf16"),     # K > 16: the full schedule's generic combine path
     (3, 4, 300000, "bf16"),    # more than 64 statistics tiles per row
     (512, 2, 20000, "bf16"),   # enough phase blocks for two tiles per wave; 5 tiles per row (odd)
+    (3, 64, 3000, "bf16"),     # K = SPEC_MAX_K: 66 launches
 ])
 def test_early_exit_shapes(B, K, V, dtype):
     print(f"case B={B} K={K} V={V} {dtype}", flush=True)

@@ -94,6 +94,38 @@ def test_zero_uniforms_and_near_one():
     check_case(c)
 
 
+@pytest.mark.parametrize("sigma", [0.0, 0.3])
+def test_sample_max_k(sigma):
+    """K = SPEC_MAX_K = 64 draft positions: every accept decision, the first
+    rejection or the bonus row at position 64 (sigma = 0: identical rows)."""
+    print(f"case K=64 sigma={sigma}", flush=True)
+    c = _case(3, 64, 3000, "bf16", sigma=sigma, key=(23, int(sigma * 10)))
+    rep, out, orc = check_case(c)
+    if sigma == 0.0:
+        assert np.all(out[0] == 64)
+
+
+@pytest.mark.parametrize("V,dtype", [(600000, "bf16"), (300000, "f32")])
+def test_sample_long_rows(V, dtype):
+    """147 statistics tiles and 293 sampling tiles per row: the combine over
+    more than 64 tiles and the pick over more tiles than one block's threads."""
+    print(f"case V={V} dtype={dtype}", flush=True)
+    c = _case(2, 3, V, dtype, key=(24, V))
+    check_case(c)
+
+
+def test_greedy_max_k_and_long_rows():
+    for B, K, V in ((3, 64, 3000), (2, 3, 600000)):
+        print(f"case greedy B={B} K={K} V={V}", flush=True)
+        g = torch.Generator().manual_seed(K + V)
+        x = torch.randn(B, K + 1, V, generator=g).to(torch.bfloat16)
+        tok = torch.argmax(x[:, :K].float(), dim=-1)
+        tok[:, K // 2] = (tok[:, K // 2] + 1) % V    # a mismatch half way
+        c = VerifyCase(x, None, tok.to(torch.int32), verify_uniforms(B, K, (2,)), 0.0, "bf16")
+        rep, out, orc = check_case(c, mode="greedy")
+        assert np.all(out[0] == K // 2)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("V", [50257, 4096, 7])
 def test_greedy(dtype, V):

@@ -16,7 +16,7 @@ struct TileStat {
 // Per-tile partial of the sampling pass (see sample_kernel).
 struct SampleTile {
   double mt, md;   // tile maxima of the target / draft row (as double)
-  double zt, zd;   // sums of the accurate 2^((x - tile max) * s) over the tile
+  double zt, zd;   // sums of 2^((x - tile max) * s) over the tile (fp64)
   double g, h;     // the same sums restricted to the residual's positive set
 };
 

@@ -14,8 +14,8 @@
 //     block then re-reads only what the output token at n needs: its tiles of
 //     target and draft row n at a rejection (residual (P_t - P_d)_+, "Step 2"),
 //     or of target row K when every draft was accepted (bonus token, step 6),
-//     recomputing every element with a compensated exponential and summing in
-//     double.  Small batches use one tile per wave, large ones up to eight so
+//     recomputing every element as 2^((x - m) * s) from the exact difference
+//     x - m and summing in double.  Small batches use one tile per wave, large ones up to eight so
 //     that the prologue is paid less often.
 //  3. pick_kernel (one block per sequence) turns the tile masses into an
 //     inverse-CDF choice of tile, then scans that one tile in token-id order.
@@ -24,9 +24,9 @@
 // the end-of-kernel cache write-back instead of per-block fences.
 //
 // The statistics pass is deliberately cheap (its normalisers only decide
-// accept tests, ~1e-7 relative is ample); the sampling pass recomputes the
-// normalisers of the row pair it samples from with the accurate exponential,
-// so the inverse-CDF boundaries carry only per-element rounding.  At a
+// accept tests, and its fp32 tile sums are ample for that); the sampling pass
+// recomputes the normalisers of the row pair it samples from, summing in
+// double, so the inverse-CDF boundaries carry only per-element rounding.  At a
 // rejection it takes the statistics pass's tile maxima as its exponent
 // references, so it needs no reduction before the exponentials and both
 // sampling kernels read the same references.
@@ -62,8 +62,8 @@ struct VerifyArgs {
   int NTs, NGs;          // sampling pass: tiles (kTileS ids) and blocks per row
   int TPWs;              // sampling pass: tiles per wave
   int TPWe;              // early-exit phases: statistics tiles per wave
-  float s_hi, s_lo;      // log2(e)/T as a float pair
-  float dmin;            // clamp for x - m in the accurate exponential: -200 / s_hi
+  float s_hi;            // log2(e)/T rounded to float
+  float dmin;            // clamp for x - m in exp2_diff: -200 / s_hi
   double s64;            // log2(e)/T in double
   double T;
   TileStat* part_a;      // [B][2K][NT]
@@ -528,7 +528,8 @@ __device__ __forceinline__ float tile_rho(float mt, float md, const SampleRowInf
   return (float)r;
 }
 
-// Accurate 2^((x - m) * s) for a whole tile slice; 0 when m is -inf (the tile is all -inf).
+// 2^((x - m) * s) for a whole tile slice, as the sampling pass computes it; 0
+// when m is -inf (the tile is all -inf).
 template <int N>
 __device__ __forceinline__ void tile_exp(const float (&x)[N], float m, const VerifyArgs& a, float (&e)[N]) {
   if (m == kNegInf) {
@@ -536,7 +537,7 @@ __device__ __forceinline__ void tile_exp(const float (&x)[N], float m, const Ver
     for (int i = 0; i < N; ++i) e[i] = 0.0f;
   } else {
 #pragma unroll
-    for (int i = 0; i < N; ++i) e[i] = exp2_accurate(x[i], m, a.s_hi, a.s_lo, a.dmin);
+    for (int i = 0; i < N; ++i) e[i] = exp2_diff(x[i], m, a.s_hi, a.dmin);
   }
 }
 
@@ -567,12 +568,12 @@ __device__ __forceinline__ void residual_tile(const VerifyArgs& a, int b, int t,
   const int lane = threadIdx.x & (kWave - 1);
   double zt = 0.0, zd = 0.0, gs = 0.0, hs = 0.0;
   // A reference of -inf means the whole statistics tile is -inf: x - m is NaN
-  // there, the clamp in exp2_accurate turns it into 2^-200, and v_exp_f32
+  // there, the clamp in exp2_diff turns it into 2^-200, and v_exp_f32
   // returns 0.
 #pragma unroll
   for (int i = 0; i < P; ++i) {
-    const float e = exp2_accurate(raw_elem<T>(cx, i), mt, a.s_hi, a.s_lo, a.dmin);
-    const float f = exp2_accurate(raw_elem<T>(cy, i), md, a.s_hi, a.s_lo, a.dmin);
+    const float e = exp2_diff(raw_elem<T>(cx, i), mt, a.s_hi, a.dmin);
+    const float f = exp2_diff(raw_elem<T>(cy, i), md, a.s_hi, a.dmin);
     const double et = (double)e, ed = (double)f;
     const double in = e * rho > f ? 1.0 : 0.0;
     zt += et;
@@ -596,7 +597,7 @@ __device__ __forceinline__ void bonus_tile(const VerifyArgs& a, int b, int t, co
   double zt = 0.0;
   if (mt != kNegInf) {
 #pragma unroll
-    for (int i = 0; i < P; ++i) zt += (double)exp2_accurate(raw_elem<T>(cx, i), mt, a.s_hi, a.s_lo, a.dmin);
+    for (int i = 0; i < P; ++i) zt += (double)exp2_diff(raw_elem<T>(cx, i), mt, a.s_hi, a.dmin);
   }
   zt = wave_sum(zt);
   if (lane == 0) a.part_b[(size_t)b * a.NTs + t] = SampleTile{(double)mt, (double)kNegInf, zt, 0.0, 0.0, 0.0};
@@ -770,7 +771,7 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
     block_max2(mm, unused, sh_f);
     mref_t = mm;
   }
-  // Normalisers of the sampled rows from the accurate per-element values.
+  // Normalisers of the sampled rows from the per-element values the sampling pass summed in double.
   double zbt = 0.0, zbd = 0.0;
   if (isfinite(mref_t)) {
     for (int tt = threadIdx.x; tt < NT; tt += kBlock) {
@@ -1200,7 +1201,6 @@ static VerifyArgs verify_args(const VerifyShape& s, const VerifyIO& io, const Ve
   a.TPWe = s.TPW_e;
   a.s64 = log2e_over(io.temperature);
   a.s_hi = (float)a.s64;
-  a.s_lo = (float)(a.s64 - (double)a.s_hi);
   a.dmin = (float)(-200.0 / (double)a.s_hi);
   a.T = (double)io.temperature;
   a.part_a = ws.part_a;

@@ -1035,33 +1035,45 @@ __device__ void finalize_greedy(const GreedyArgs& a, int b) {
   __shared__ int sh_arg[kMaxK + 1];
   __shared__ int sh_bad;
   const int K = a.K, R = K + 1;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   if (threadIdx.x == 0) sh_bad = 0;
   __syncthreads();
-  if ((int)threadIdx.x < R) {
-    const int r = threadIdx.x;
+  // Row r's argmax over its tile records: one wave per row, lane l merging
+  // records l, l + 64, ..., then a butterfly.  The merge keeps the largest
+  // value and, among equal ones, the lowest id, so its order does not matter.
+  for (int r = wave; r < R; r += kWavesPerBlock) {
     const ArgTile* p = a.part + ((size_t)b * R + r) * a.NT;
     float best = kNegInf;
     int idx = 0x7fffffff;
-    for (int t = 0; t < a.NT; ++t) argmax_merge(best, idx, p[t].v, p[t].i);
-    if (!isfinite(best)) atomicOr(&sh_bad, 1);
-    sh_arg[r] = idx;
+    for (int t = lane; t < a.NT; t += kWave) argmax_merge(best, idx, p[t].v, p[t].i);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ob = __shfl_xor(best, o);
+      const int oi = __shfl_xor(idx, o);
+      argmax_merge(best, idx, ob, oi);
+    }
+    if (lane == 0) {
+      if (!isfinite(best)) atomicOr(&sh_bad, 1);
+      sh_arg[r] = idx;
+    }
   }
   if ((int)threadIdx.x < K) {
     const int d = a.tokens[(size_t)b * K + threadIdx.x];
     if (d < 0 || d >= a.V) atomicOr(&sh_bad, 1);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (wave == 0) {
+    // n = the first position whose draft differs from the argmax (K <= 64: one ballot)
     const bool bad = sh_bad != 0;
-    int n = K;
-    for (int i = 0; i < K; ++i)
-      if (a.tokens[(size_t)b * K + i] != sh_arg[i]) {
-        n = i;
-        break;
-      }
+    const int d = lane < K ? a.tokens[(size_t)b * K + lane] : -1;
+    const uint64_t miss = __ballot(lane < K && d != sh_arg[lane]);
+    const int n = miss ? (int)__builtin_ctzll(miss) : K;
     int32_t* out = a.out_tokens + (size_t)b * R;
-    for (int i = 0; i <= K; ++i) out[i] = bad ? -1 : (i < n ? a.tokens[(size_t)b * K + i] : (i == n ? sh_arg[n] : -1));
-    a.accepted_len[b] = bad ? -1 : n;
+    for (int i = lane; i <= K; i += kWave) {
+      const int di = i < K ? a.tokens[(size_t)b * K + i] : -1;
+      out[i] = bad ? -1 : (i < n ? di : (i == n ? sh_arg[n] : -1));
+    }
+    if (lane == 0) a.accepted_len[b] = bad ? -1 : n;
   }
   for (int i = threadIdx.x; i < K; i += kBlock) {
     if (a.p_t_out) a.p_t_out[(size_t)b * K + i] = __builtin_nanf("");

@@ -40,6 +40,17 @@ __device__ __forceinline__ int tile_offset(int e, int lane) {
   return (e / V8) * (kWave * V8) + lane * V8 + (e % V8);
 }
 
+// One 16-byte streaming load of logits: nontemporal, so the line is not kept
+// in the caches for reuse.  A read-only probe over 1.88 GB in 8 KiB pieces per
+// wave streams at 6.8 TB/s this way against 6.06 TB/s with plain loads, and the
+// statistics pass went from 314 to 281 us at B=256, K=7, V=262144.  The
+// sampling pass keeps plain loads (its raw-tile loader below): the rows it
+// re-reads can still sit in the last-level cache, and nontemporal loads made
+// it 1-2 us slower.
+__device__ __forceinline__ u32x4 stream16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 // Load the lane's L*kVec elements of tile t (tiles of kWave*L*kVec ids) of a
 // row of V logits as float; ids >= V read as -inf.  kAligned requires a
 // 16-byte aligned row and V % kVec == 0, so a 16-byte vector is either fully
@@ -58,13 +69,13 @@ __device__ __forceinline__ void load_tile(const T* __restrict__ row, int V, int 
     // length is not a tile multiple) loads without per-vector range checks.
     if (t * (kWave * L * V8) + (first + kL) * (kWave * V8) <= V) {
 #pragma unroll
-      for (int j = 0; j < kL; ++j) raw[j] = *reinterpret_cast<const u32x4*>(row + base + j * (kWave * V8));
+      for (int j = 0; j < kL; ++j) raw[j] = stream16(row + base + j * (kWave * V8));
     } else {
 #pragma unroll
       for (int j = 0; j < kL; ++j) {
         const int off = base + j * (kWave * V8);
         if (off < V) {
-          raw[j] = *reinterpret_cast<const u32x4*>(row + off);
+          raw[j] = stream16(row + off);
         } else {
           const uint32_t ninf = sizeof(T) == 2 ? 0xff80ff80u : 0xff800000u;
           raw[j] = u32x4{ninf, ninf, ninf, ninf};

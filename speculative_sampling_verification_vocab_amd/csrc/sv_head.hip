@@ -246,7 +246,8 @@ __global__ void __launch_bounds__(SLAB / 16 * kWave) head_mfma_kernel(HeadArgs a
         if (kFull) {
           const int k = min(st, nstage - 1) * kStageK + c8;
 #pragma unroll
-          for (int i = 0; i < kWL; ++i) wr[i] = *reinterpret_cast<const u32x4*>(wrow[i] + k);
+          for (int i = 0; i < kWL; ++i)  // W streams once per pass: nontemporal
+            wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[i] + k));
 #pragma unroll
           for (int i = 0; i < kAL; ++i) ar[i] = *reinterpret_cast<const u32x4*>(arow[i] + k);
         } else {

@@ -39,6 +39,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+LLC_BYTES = 256 << 20   # MI355X last-level (Infinity) cache
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HEAD_WORKLOAD = "shortlist_head_b32_k4_d4096_v128256"
 PROFILE_PMC = os.path.join(ROOT, "profiles", "stats_kernel_b256_k7_v262144_bf16_pmc.md")
@@ -272,6 +273,18 @@ def main():
 
     ws = sv.Workspace(dev)
     stream = torch.cuda.current_stream(dev)
+    # Inputs larger than the 256 MB last-level cache: consecutive steps
+    # alternate between two copies of the batch (same values, other
+    # addresses).  With one copy, the rows that step i's sampling pass reads
+    # (~240 MB at B=256, K=7, V=262144) are still cached when step i+1's
+    # statistics pass reads them again, which no serving loop sees: new
+    # logits arrive every step.
+    in_bytes = case.target.numel() * esz + (case.draft.numel() * esz if case.draft is not None else 0)
+    sets = [case]
+    if in_bytes > LLC_BYTES:
+        sets.append(type(case)(case.target.clone(), case.draft.clone() if case.draft is not None else None,
+                               case.draft_tokens.clone(), case.uniforms.clone(), case.temperature, case.dtype))
+        torch.cuda.synchronize()
 
     def timed(mode, steps, warmup):
         """Two passes of `steps` verify calls after `warmup` untimed ones.
@@ -284,19 +297,20 @@ def main():
         L = sv.spec_verify_launch_count(B, K, V, case.target.dtype, mode)
         NE = L + 1
         sampling = mode != "greedy"
-        draft = case.draft if sampling else None
-        uni = case.uniforms if sampling else None
 
-        def step(evs=None):
-            return sv.spec_verify(case.target, draft, case.draft_tokens, uni, case.temperature, mode,
-                                  workspace=ws, events=evs)
+        def step(i, evs=None):
+            c = sets[i % len(sets)]
+            return sv.spec_verify(c.target, c.draft if sampling else None, c.draft_tokens,
+                                  c.uniforms if sampling else None, c.temperature, mode, workspace=ws, events=evs)
 
-        for _ in range(warmup):
-            step()
+        for i in range(warmup):
+            step(i)
         torch.cuda.synchronize()
         start = time.perf_counter()
-        for _ in range(steps):
-            res = step()
+        for i in range(steps):
+            r = step(i)
+            if i % len(sets) == 0:
+                res = r  # outputs of the first copy (the batch itself)
         torch.cuda.synchronize()
         ms = (time.perf_counter() - start) * 1e3 / steps
 
@@ -305,7 +319,7 @@ def main():
             e.record(stream)  # creates the underlying hipEvent
         torch.cuda.synchronize()
         for s in range(steps):
-            step(evs[NE * s:NE * s + NE])
+            step(s, evs[NE * s:NE * s + NE])
         torch.cuda.synchronize()
 
         def span(i, j, f=np.mean):

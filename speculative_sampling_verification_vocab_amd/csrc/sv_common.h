@@ -44,9 +44,8 @@ __device__ __forceinline__ int tile_offset(int e, int lane) {
 // in the caches for reuse.  A read-only probe over 1.88 GB in 8 KiB pieces per
 // wave streams at 6.8 TB/s this way against 6.06 TB/s with plain loads, and the
 // statistics pass went from 314 to 281 us at B=256, K=7, V=262144.  The
-// sampling pass keeps plain loads (its raw-tile loader below): the rows it
-// re-reads can still sit in the last-level cache, and nontemporal loads made
-// it 1-2 us slower.
+// sampling pass keeps plain loads (its raw-tile loader below): nontemporal
+// ones measured the same there.
 __device__ __forceinline__ u32x4 stream16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }

@@ -165,7 +165,8 @@ __global__ void __launch_bounds__(kBlock) dense_fill_kernel(void* dense, size_t 
   const size_t first = (size_t)blockIdx.x * kBlock + threadIdx.x;
   if ((uintptr_t)dense % 16 == 0) {
     const u32x4 v = {pat, pat, pat, pat};
-    for (size_t i = first; i < bytes / 16; i += stride) reinterpret_cast<u32x4*>(dense)[i] = v;
+    for (size_t i = first; i < bytes / 16; i += stride)  // nontemporal: about 3 us less over 33 MB
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dense) + i);
     for (size_t i = bytes / 16 * 16 / (bf16 ? 2 : 4) + first; i < elems; i += stride) {
       if (bf16) static_cast<uint16_t*>(dense)[i] = 0xff80u;
       else static_cast<uint32_t*>(dense)[i] = pat;

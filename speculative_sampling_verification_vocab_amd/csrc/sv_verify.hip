@@ -681,26 +681,30 @@ __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
 }
 
 // Two block-wide sums in one round of LDS traffic.
-__device__ __forceinline__ void block_sum2(double& x, double& y, double* sh) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+__device__ __forceinline__ void block_sum4(double& x, double& y, double& z, double& w, double* sh) {
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   x = wave_sum(x);
   y = wave_sum(y);
+  z = wave_sum(z);
+  w = wave_sum(w);
   if (lane == 0) {
-    sh[w] = x;
-    sh[kWavesPerBlock + w] = y;
+    sh[wv] = x;
+    sh[kWavesPerBlock + wv] = y;
+    sh[2 * kWavesPerBlock + wv] = z;
+    sh[3 * kWavesPerBlock + wv] = w;
   }
   __syncthreads();
-  x = 0.0;
-  y = 0.0;
+  x = y = z = w = 0.0;
 #pragma unroll
   for (int i = 0; i < kWavesPerBlock; ++i) {
     x += sh[i];
     y += sh[kWavesPerBlock + i];
+    z += sh[2 * kWavesPerBlock + i];
+    w += sh[3 * kWavesPerBlock + i];
   }
   __syncthreads();
 }
 
-// Block-wide maximum of two floats, and minimum of two ints, in one round each.
 __device__ __forceinline__ void block_max2(float& x, float& y, float* sh) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   x = wave_max(x);
@@ -742,7 +746,7 @@ __device__ __forceinline__ void block_min2(int& x, int& y, int* sh) {
 // for one memory round trip before the tile choice and one for the tile.
 template <typename T, bool kAligned, bool kSparse = false>
 __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
-  __shared__ double sh_d[2 * kWavesPerBlock];
+  __shared__ double sh_d[4 * kWavesPerBlock];
   __shared__ float sh_f[2 * kWavesPerBlock];
   __shared__ int sh_i[2 * kWavesPerBlock];
   __shared__ double sh_scan[kWavesPerBlock];
@@ -771,16 +775,26 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
     block_max2(mm, unused, sh_f);
     mref_t = mm;
   }
-  // Normalisers of the sampled rows from the per-element values the sampling pass summed in double.
-  double zbt = 0.0, zbd = 0.0;
+  // Tile weights 2^((tile reference - row reference) * s) of the target and
+  // draft rows.  One pass gives the rows' normalisers and the residual's two
+  // positive-set masses; a thread that owns one tile keeps its weights for the
+  // scan below.
+  auto w_t = [&](double mt) { return mt == kNegInfD ? 0.0 : exp2((mt - (double)mref_t) * a.s64); };
+  auto w_d = [&](double md) { return md == kNegInfD ? 0.0 : exp2((md - (double)sr.m_d) * a.s64); };
+  double zbt = 0.0, zbd = 0.0, G = 0.0, H = 0.0, wt0 = 0.0, wd0 = 0.0;
   if (isfinite(mref_t)) {
     for (int tt = threadIdx.x; tt < NT; tt += kBlock) {
       const SampleTile q = tile_at(tt);
-      if (q.mt != kNegInfD) zbt += q.zt * exp2((q.mt - (double)mref_t) * a.s64);
-      if (resid && q.md != kNegInfD) zbd += q.zd * exp2((q.md - (double)sr.m_d) * a.s64);
+      const double wt = w_t(q.mt), wd = resid ? w_d(q.md) : 0.0;
+      wt0 = wt;
+      wd0 = wd;
+      zbt += q.zt * wt;
+      zbd += q.zd * wd;
+      G += q.g * wt;
+      H += q.h * wd;
     }
   }
-  block_sum2(zbt, zbd, sh_d);
+  block_sum4(zbt, zbd, G, H, sh_d);
   if (!isfinite(mref_t) || !(zbt > 0.0) || !isfinite(zbt) || (resid && (!(zbd > 0.0) || !isfinite(zbd)))) {
     // A sampled row without a finite maximum: the sequence is faulty.
     for (int i = threadIdx.x; i <= K; i += kBlock) a.out_tokens[(size_t)b * (K + 1) + i] = -1;
@@ -788,24 +802,17 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
     return;
   }
 
-  // Tile scale factors: P_t(v) = e_t(v) * gt, P_d(v) = e_d(v) * gd.
-  auto scale_t = [&](double mt) { return mt == kNegInfD ? 0.0 : exp2((mt - (double)mref_t) * a.s64) / zbt; };
-  auto scale_d = [&](double md) { return md == kNegInfD ? 0.0 : exp2((md - (double)sr.m_d) * a.s64) / zbd; };
-  auto tile_mass = [&](const SampleTile& q, bool fallback) -> double {
-    if (!resid || fallback) return q.zt * scale_t(q.mt);
-    return q.g * scale_t(q.mt) - q.h * scale_d(q.md);
-  };
-
-  double S = 0.0, S_fb = 0.0;
-  for (int tt = threadIdx.x; tt < NT; tt += kBlock) {
-    const SampleTile q = tile_at(tt);
-    S += tile_mass(q, false);
-    if (resid) S_fb += tile_mass(q, true);
-  }
-  block_sum2(S, S_fb, sh_d);
-  // Rejection with no residual mass left by rounding: sample P_t instead.
+  // P_t(v) = e_t(v) * w_t / Z_t and P_d(v) = e_d(v) * w_d / Z_d within a tile.
+  const double izt = 1.0 / zbt, izd = resid ? 1.0 / zbd : 0.0;
+  // Residual mass S = sum (P_t - P_d) over the positive set; a rejection whose
+  // residual rounding left no mass samples P_t instead (total mass 1).
+  double S = resid ? G * izt - H * izd : 1.0;
   const bool fallback = resid && !(S > 0.0);
-  if (fallback) S = S_fb;
+  if (fallback) S = 1.0;
+  auto tile_mass = [&](const SampleTile& q, double wt, double wd) -> double {
+    if (!resid || fallback) return q.zt * wt * izt;
+    return q.g * wt * izt - q.h * wd * izd;
+  };
   const double target = (double)sh_u[n] * S;
 
   // Tile holding the inverse-CDF point: block scan over tiles in id order.
@@ -813,7 +820,11 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
   double cbefore = 0.0, offset = 0.0;
   for (int c0 = 0; c0 < NT; c0 += kBlock) {
     const int tt = c0 + threadIdx.x;
-    const double ms = tt < NT ? tile_mass(tile_at(tt), fallback) : 0.0;
+    double ms = 0.0;
+    if (tt < NT) {
+      const SampleTile q = tile_at(tt);
+      ms = cached ? tile_mass(q, wt0, wd0) : tile_mass(q, w_t(q.mt), resid ? w_d(q.md) : 0.0);
+    }
     double incl = wave_inclusive_scan(ms, lane);
     if (lane == kWave - 1) sh_scan[wave] = incl;
     __syncthreads();
@@ -883,8 +894,8 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
     float unused = kNegInf;
     block_max2(mt, unused, sh_f);
   }
-  const double gt = scale_t((double)mt);
-  const double gd = use_d ? scale_d((double)md) : 0.0;
+  const double gt = w_t((double)mt) * izt;
+  const double gd = use_d ? w_d((double)md) * izd : 0.0;
   tile_exp(x, mt, a, e);
   double w[V8];
   if (use_d) {

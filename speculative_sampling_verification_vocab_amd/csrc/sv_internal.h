@@ -45,6 +45,7 @@ struct VerifyShape {
   int NG_s;      // sampling-pass blocks per row
   int TPW_s;     // sampling-pass tiles per wave
   int TPW_e;     // early-exit phases: statistics tiles per wave
+  bool decide;   // SAMPLE: a separate decision launch before the sampling pass
 };
 
 struct VerifyWorkspace {
@@ -77,9 +78,10 @@ VerifyShape make_shape(int B, int K, int V, int dtype, bool aligned);
 // mode: 0 SAMPLE, 1 GREEDY, 2 SAMPLE_EARLY_EXIT (spec_mode_t values).
 size_t verify_workspace_layout(const VerifyShape& s, int mode, void* base, VerifyWorkspace* out);
 
-// SAMPLE: three launches (statistics, sampling with accept decisions, pick).
-// events[k] (if present, k < n_events) is recorded before launch k and
-// events[3] after the last one.
+// SAMPLE: statistics, then either decisions and sampling (s.decide) or
+// sampling with the decisions in its prologue, then pick: four or three
+// launches.  events[k] (if present, k < n_events) is recorded before launch k
+// and events[launches] after the last one.
 int sample_launches(const VerifyShape& s);
 hipError_t launch_sample_pipeline(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws,
                                   hipStream_t st, void* const* events, int n_events);

@@ -1,23 +1,25 @@
 // Speculative-sampling verify kernels for gfx950.
 //
-// SAMPLE mode runs three kernels on the caller's stream.
+// SAMPLE mode runs three or four kernels on the caller's stream.
 //
 //  1. stats_kernel streams target rows 0..K-1 and draft rows 0..K-1 once.
 //     One wave owns one tile (8 KiB) of one row: 16-byte loads, a per-lane
 //     maximum, 2^((x - max) * log2(e)/T) with v_exp_f32, and a wave reduction
 //     to a (tile max, tile sum) partial.
-//  2. sample_kernel: every block first combines its sequence's partials into
-//     (max, Z) per row, evaluates P_t,i(d_i) and P_d,i(d_i) in double, takes
-//     every accept decision u < min(1, P_t/P_d) and finds the first rejection
-//     n (Speculative Decoding lesson, nextadmin.net, "Core algorithm" steps
-//     4-5, "Step 1"); the sequence's first block writes those outputs.  The
-//     block then re-reads only what the output token at n needs: its tiles of
-//     target and draft row n at a rejection (residual (P_t - P_d)_+, "Step 2"),
-//     or of target row K when every draft was accepted (bonus token, step 6),
-//     recomputing every element as 2^((x - m) * s) from the exact difference
-//     x - m and summing in double.  Small batches use one tile per wave, large ones up to eight so
-//     that the prologue is paid less often.
-//  3. pick_kernel (one block per sequence) turns the tile masses into an
+//  2. The accept decisions: combine the sequence's partials into (max, Z) per
+//     row, evaluate P_t,i(d_i) and P_d,i(d_i) in double, take every decision
+//     u < min(1, P_t/P_d) and find the first rejection n (Speculative Decoding
+//     lesson, nextadmin.net, "Core algorithm" steps 4-5, "Step 1").  Large
+//     batches run them in decide_kernel, one block per sequence; small ones in
+//     the prologue of every sampling block (the sequence's first block writes
+//     the outputs), which saves a launch.
+//  3. sample_kernel re-reads only what the output token at n needs: its tiles
+//     of target and draft row n at a rejection (residual (P_t - P_d)_+,
+//     "Step 2"), or of target row K when every draft was accepted (bonus
+//     token, step 6), recomputing every element as 2^((x - m) * s) from the
+//     exact difference x - m and summing in double.  Small batches use one
+//     tile per wave, large ones up to eight.
+//  4. pick_kernel (one block per sequence) turns the tile masses into an
 //     inverse-CDF choice of tile, then scans that one tile in token-id order.
 //
 // Kernel boundaries order the passes: partial results cross XCDs through
@@ -409,7 +411,6 @@ __device__ int ee_decide(const VerifyArgs& a, int b, int j, bool writer, SampleR
   return n == -2 ? 1 : 0;
 }
 
-template <typename T>
 __device__ int accept_sequence(const VerifyArgs& a, int b, bool write, SampleRowInfo* info) {
   __shared__ float sh_m[2 * kMaxK];
   __shared__ double sh_z[2 * kMaxK];
@@ -606,7 +607,9 @@ __device__ __forceinline__ void bonus_tile(const VerifyArgs& a, int b, int t, co
 // Block `blk` of the sampling pass.
 // kFromRows: n and the row record come from the early-exit decisions
 // (a.rows) instead of this block's own accept prologue.
-template <typename T, bool kAligned, bool kFromRows = false, bool kSparse = false>
+// kDecided: decide_kernel has taken every accept decision and left the
+// record in rows[b].
+template <typename T, bool kAligned, bool kFromRows = false, bool kSparse = false, bool kDecided = false>
 __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int K = a.K;
@@ -614,7 +617,10 @@ __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
   const int b = blk / a.NGs;
   SampleRowInfo sr;
   int n;
-  if constexpr (kFromRows) {
+  if constexpr (kDecided) {
+    sr = a.rows[b];
+    n = K == 0 ? 0 : sr.n;
+  } else if constexpr (kFromRows) {
     // Early exit: a sequence that reached position K - 1 is decided here (by
     // wave 0 of each block, which shares the record through LDS; wave 0 of
     // the first block writes the outputs); the others ended earlier and left
@@ -635,7 +641,7 @@ __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
       n = sr.n;
     }
   } else {
-    n = accept_sequence<T>(a, b, g == 0, &sr);
+    n = accept_sequence(a, b, g == 0, &sr);
   }
   if (n < 0) return;  // faulty sequence: outputs already written
   const bool resid = n < K;
@@ -950,9 +956,20 @@ __global__ void __launch_bounds__(kBlock) stats_kernel(VerifyArgs a) {
   stats_block<T, kAligned, kSparse>(a, blockIdx.x);
 }
 
-template <typename T, bool kAligned, bool kSparse = false>
+// Every accept decision of sequence blockIdx.x and its first rejection
+// (Speculative Decoding lesson, "Core algorithm" steps 4-5, "Step 1"): the
+// outputs up to the first rejection, P(d) at each position, and the record
+// the sampling and pick kernels read.  Large batches take the decisions here
+// once per sequence; small ones in the prologue of every sampling block,
+// which saves this launch.
+__global__ void __launch_bounds__(kBlock) decide_kernel(VerifyArgs a) {
+  SampleRowInfo sr;
+  accept_sequence(a, blockIdx.x, true, &sr);
+}
+
+template <typename T, bool kAligned, bool kSparse = false, bool kDecided = false>
 __global__ void __launch_bounds__(kBlock) sample_kernel(VerifyArgs a) {
-  sample_block<T, kAligned, false, kSparse>(a, blockIdx.x);
+  sample_block<T, kAligned, false, kSparse, kDecided>(a, blockIdx.x);
 }
 
 template <typename T, bool kAligned, bool kSparse = false>
@@ -1167,6 +1184,9 @@ VerifyShape make_shape(int B, int K, int V, int dtype, bool aligned) {
   }
   s.NG_s = (s.NT_s + s.TPW_s * kWavesPerBlock - 1) / (s.TPW_s * kWavesPerBlock);
   s.TPW_e = (long long)B * 2 * s.NG >= kEEBlocksForTwo ? 2 : 1;
+  // A separate decision launch pays off once blocks cover several sampling
+  // tiles (B=256, K=7, V=262144: 353 -> 348 us; B=8: 21.8 -> 24.5 us with it).
+  s.decide = s.TPW_s > 1;
   return s;
 }
 
@@ -1247,7 +1267,7 @@ static VerifyArgs verify_args(const VerifyShape& s, const VerifyIO& io, const Ve
   return a;
 }
 
-int sample_launches(const VerifyShape& s) { return s.B == 0 ? 0 : 3; }
+int sample_launches(const VerifyShape& s) { return s.B == 0 ? 0 : (s.decide ? 4 : 3); }
 
 template <bool kSparse>
 static hipError_t sample_pipeline(const VerifyShape& s, const VerifyArgs& a, hipStream_t st, void* const* events,
@@ -1264,10 +1284,22 @@ static hipError_t sample_pipeline(const VerifyShape& s, const VerifyArgs& a, hip
                   stats_kernel<uint16_t, true, kSparse>, stats_kernel<uint16_t, false, kSparse>,
                   stats_kernel<float, true, kSparse>, stats_kernel<float, false, kSparse>, a);
   record();
-  if (e == hipSuccess)
-    e = dispatch4(s.dtype, s.aligned, dim3((unsigned)((size_t)s.B * s.NG_s)), st,
-                  sample_kernel<uint16_t, true, kSparse>, sample_kernel<uint16_t, false, kSparse>,
-                  sample_kernel<float, true, kSparse>, sample_kernel<float, false, kSparse>, a);
+  const dim3 sgrid((unsigned)((size_t)s.B * s.NG_s));
+  if (s.decide) {
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(decide_kernel, dim3((unsigned)s.B), dim3(kBlock), 0, st, a);
+      e = hipGetLastError();
+    }
+    record();
+    if (e == hipSuccess)
+      e = dispatch4(s.dtype, s.aligned, sgrid, st, sample_kernel<uint16_t, true, kSparse, true>,
+                    sample_kernel<uint16_t, false, kSparse, true>, sample_kernel<float, true, kSparse, true>,
+                    sample_kernel<float, false, kSparse, true>, a);
+  } else if (e == hipSuccess) {
+    e = dispatch4(s.dtype, s.aligned, sgrid, st, sample_kernel<uint16_t, true, kSparse>,
+                  sample_kernel<uint16_t, false, kSparse>, sample_kernel<float, true, kSparse>,
+                  sample_kernel<float, false, kSparse>, a);
+  }
   record();
   if (e == hipSuccess)
     e = dispatch4(s.dtype, s.aligned, dim3((unsigned)s.B), st, pick_kernel<uint16_t, true, kSparse>,

@@ -47,6 +47,7 @@ def _budget(K, k_max, nc):
     (5, 2, 7000, 7, [100, 30], "f32"),           # 7-id clusters: a lane's 8 ids cross clusters
     (4, 1, 4096, 256, [3], "bf16"),
     (3, 0, 5010, 501, [], "bf16"),               # no drafts: bonus token only
+    (512, 2, 20000, 50, [20, 10], "bf16"),       # large batch: decisions in a launch of their own
 ])
 def test_sparse_shapes(B, K, V, cs, n_sel, dtype):
     print(f"case B={B} K={K} V={V} cs={cs} n_sel={n_sel} {dtype}", flush=True)

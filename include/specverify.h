@@ -257,7 +257,8 @@ spec_status_t spec_draft_head_positions(const void* h, const void* W, const int3
  * take the vector-load path.
  * Errors: SPEC_ERR_INVALID_ARG for NULL or misaligned buffers or bad sizes;
  * SPEC_ERR_UNSUPPORTED if V % cluster_size != 0 or the output needs more than
- * 2^31 - 1 tiles of 128 x 32.
+ * 2^31 - 1 output tiles (one block each; tiles are 128 x 128, 128 x 32 or
+ * 64 x 32 depending on the shape and alignment).
  */
 spec_status_t spec_draft_head_static(const void* h, const void* W, const int32_t* cluster_ids, int32_t M,
                                      int32_t d, int32_t V, int32_t cluster_size, int32_t n_sel, void* logits,

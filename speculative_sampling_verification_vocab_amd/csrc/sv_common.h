@@ -291,19 +291,42 @@ __device__ __forceinline__ int block_min(int v, int* sh) {
 // float32 argument.  Used where relative errors of ~1e-7 are harmless.
 __device__ __forceinline__ float exp2_fast(float a) { return __builtin_amdgcn_exp2f(a); }
 
-// 2^((x - m) * s) for the sampling pass.  x - m is exact for bf16 operands
-// whose exponents are within 16 of each other (rounded once for fp32), the
-// product is rounded once and v_exp_f32 adds under one ulp.  A compensated
-// form that recovers the product's rounding error with an FMA and applies it
-// as the factor (1 + lo*ln2) costs five more instructions per element (10 us
-// per B=256, K=7, V=262144 call) and measured the same excused-disagreement
-// rate against the fp64 oracle over 250 seeds of that batch (4 and 5 of
-// 512,000 decisions), so it is not used.  d is clamped at dmin = -200/s: a
-// tile whose reference is -inf (all of it -inf) gives NaN there, which the
-// clamp turns into 2^-200, returned as 0.
-__device__ __forceinline__ float exp2_diff(float x, float m, float s, float dmin) {
-  const float d = fmaxf(x - m, dmin);
-  return __builtin_amdgcn_exp2f(d * s);
+// Exponentials of the sampling pass.  A tile with reference (maximum) m
+// takes hi = RN(m * s) once; each element is then 2^RN(x * s - hi): one FMA
+// (x * s - hi exact before its single rounding) and v_exp_f32, under one ulp.
+// The exact remainder lo = m * s - hi is put back where tiles are combined, as
+// the factor 2^-lo on the tile's weight and in the positive-set ratio, so
+// every value is 2^((x - m) * s) to within that rounding.  An earlier form,
+// RN((x - m) * s) with a clamp for -inf tiles, took three instructions per
+// element instead of one and has the same per-element error (a float32-exact
+// emulation over B=256, K=7, V=262144 rows: RMS 2.95e-7 against fp64 for
+// both); a compensated form that also recovered the product's rounding
+// error took five more and gave no better agreement with the fp64 oracle.
+// A reference of -inf (a tile that is all -inf) gets hi = +inf, so every
+// element's argument is -inf and its value 0 without a per-element select.
+__device__ __forceinline__ float exp_ref_hi(float m, float s) {
+#pragma clang fp contract(off)
+  return m == -__builtin_inff() ? __builtin_inff() : m * s;
+}
+
+// lo = m * s - RN(m * s), exact; |lo| <= 2^-25 |m * s|; 0 when m is -inf.
+__device__ __forceinline__ float exp_ref_lo(float m, float s) {
+#pragma clang fp contract(off)
+  if (m == -__builtin_inff()) return 0.0f;
+  const float hi = m * s;
+  return __builtin_fmaf(m, s, -hi);
+}
+
+// 2^-lo in fp64: e^-t with t = lo ln 2, five Taylor terms (relative error
+// under t^5 / 120 < 1e-17 while |t| < 1e-3, i.e. |m * s| below about 4.8e4).
+__device__ __forceinline__ double exp_ref_scale(float m, float s) {
+  const double t = (double)exp_ref_lo(m, s) * 0.69314718055994530942;
+  if (__builtin_fabs(t) >= 1e-3) return exp(-t);
+  return 1.0 + t * (-1.0 + t * (0.5 + t * (-1.0 / 6.0 + t * (1.0 / 24.0))));
+}
+
+__device__ __forceinline__ float exp2_ref(float x, float s, float hi) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(x, s, -hi));
 }
 
 }  // namespace sv

@@ -65,7 +65,6 @@ struct VerifyArgs {
   int TPWs;              // sampling pass: tiles per wave
   int TPWe;              // early-exit phases: statistics tiles per wave
   float s_hi;            // log2(e)/T rounded to float
-  float dmin;            // clamp for x - m in exp2_diff: -200 / s_hi
   double s64;            // log2(e)/T in double
   double T;
   TileStat* part_a;      // [B][2K][NT]
@@ -517,14 +516,15 @@ __device__ int accept_sequence(const VerifyArgs& a, int b, bool write, SampleRow
 
 // Per-tile ratio that decides the residual's positive set: element v of a tile
 // with maxima (mt, md) is in the set iff e_t * rho > e_d, i.e. P_t(v) > P_d(v)
-// with the statistics-pass normalisers.  Both sampling kernels evaluate this
-// same function, so they agree on the set.
-__device__ __forceinline__ float tile_rho(float mt, float md, const SampleRowInfo& sr, double s64) {
+// with the statistics-pass normalisers, where e_t, e_d are the elements'
+// exp2_ref values (so the references' remainders lo enter the ratio).  Both
+// sampling kernels evaluate this same function, so they agree on the set.
+__device__ __forceinline__ float tile_rho(float mt, float md, const SampleRowInfo& sr, double s64, float s_hi) {
 #pragma clang fp contract(off)
   if (mt == kNegInf) return 0.0f;
   if (md == kNegInf) return 1e30f;
   const double lr = ((double)mt - (double)sr.m_t - ((double)md - (double)sr.m_d)) * s64 +
-                    log2(sr.za_d) - log2(sr.za_t);
+                    log2(sr.za_d) - log2(sr.za_t) + ((double)exp_ref_lo(md, s_hi) - (double)exp_ref_lo(mt, s_hi));
   const double r = exp2(fmin(fmax(lr, -99.0), 99.0));
   return (float)r;
 }
@@ -533,13 +533,9 @@ __device__ __forceinline__ float tile_rho(float mt, float md, const SampleRowInf
 // when m is -inf (the tile is all -inf).
 template <int N>
 __device__ __forceinline__ void tile_exp(const float (&x)[N], float m, const VerifyArgs& a, float (&e)[N]) {
-  if (m == kNegInf) {
+  const float hi = exp_ref_hi(m, a.s_hi);
 #pragma unroll
-    for (int i = 0; i < N; ++i) e[i] = 0.0f;
-  } else {
-#pragma unroll
-    for (int i = 0; i < N; ++i) e[i] = exp2_diff(x[i], m, a.s_hi, a.dmin);
-  }
+  for (int i = 0; i < N; ++i) e[i] = exp2_ref(x[i], a.s_hi, hi);
 }
 
 // Value of v in lane l (l the same in every lane of the wave).
@@ -562,19 +558,18 @@ constexpr int kSubTiles = kTile<T> / kTileS<T>;  // sampling tiles per statistic
 
 // Residual tile sums of tile t from packed slices cx (target) and cy (draft)
 // with references (mt, md) and positive-set ratio rho.
+// ht and hd are exp_ref_hi of the references mt and md; the sums are in units
+// of 2^(x * s - h), which pick_block rescales by 2^-lo.
 template <typename T, int NL>
-__device__ __forceinline__ void residual_tile(const VerifyArgs& a, int b, int t, float mt, float md, float rho,
-                                              const u32x4 (&cx)[NL], const u32x4 (&cy)[NL]) {
+__device__ __forceinline__ void residual_tile(const VerifyArgs& a, int b, int t, float mt, float md, float ht,
+                                              float hd, float rho, const u32x4 (&cx)[NL], const u32x4 (&cy)[NL]) {
   constexpr int P = NL * Elem<T>::kVec;
   const int lane = threadIdx.x & (kWave - 1);
   double zt = 0.0, zd = 0.0, gs = 0.0, hs = 0.0;
-  // A reference of -inf means the whole statistics tile is -inf: x - m is NaN
-  // there, the clamp in exp2_diff turns it into 2^-200, and v_exp_f32
-  // returns 0.
 #pragma unroll
   for (int i = 0; i < P; ++i) {
-    const float e = exp2_diff(raw_elem<T>(cx, i), mt, a.s_hi, a.dmin);
-    const float f = exp2_diff(raw_elem<T>(cy, i), md, a.s_hi, a.dmin);
+    const float e = exp2_ref(raw_elem<T>(cx, i), a.s_hi, ht);
+    const float f = exp2_ref(raw_elem<T>(cy, i), a.s_hi, hd);
     const double et = (double)e, ed = (double)f;
     const double in = e * rho > f ? 1.0 : 0.0;
     zt += et;
@@ -597,8 +592,9 @@ __device__ __forceinline__ void bonus_tile(const VerifyArgs& a, int b, int t, co
   const float mt = wave_max(raw_lane_max<T>(cx));
   double zt = 0.0;
   if (mt != kNegInf) {
+    const float ht = exp_ref_hi(mt, a.s_hi);
 #pragma unroll
-    for (int i = 0; i < P; ++i) zt += (double)exp2_diff(raw_elem<T>(cx, i), mt, a.s_hi, a.dmin);
+    for (int i = 0; i < P; ++i) zt += (double)exp2_ref(raw_elem<T>(cx, i), a.s_hi, ht);
   }
   zt = wave_sum(zt);
   if (lane == 0) a.part_b[(size_t)b * a.NTs + t] = SampleTile{(double)mt, (double)kNegInf, zt, 0.0, 0.0, 0.0};
@@ -669,8 +665,9 @@ __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
     ref_t = a.part_a[((size_t)b * R + n) * a.NT + T0 + lane].m;
     // a sparse draft row has no dense tiles: its row maximum is the reference
     ref_d = kSparse ? sr.m_d : a.part_a[((size_t)b * R + K + n) * a.NT + T0 + lane].m;
-    rho_l = tile_rho(ref_t, ref_d, sr, a.s64);
+    rho_l = tile_rho(ref_t, ref_d, sr, a.s64, a.s_hi);
   }
+  const float hi_t = exp_ref_hi(ref_t, a.s_hi), hi_d = exp_ref_hi(ref_d, a.s_hi);
   for (int j = 0; j < a.TPWs; ++j) {
     const int t = tile_of(j);
     if (t >= a.NTs) break;
@@ -680,7 +677,8 @@ __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
       if constexpr (kSparse) sparse_tile_raw<T>(a, b, n, t, lane, cy, tab);
       else load_raw<T, kAligned, kLoadsS>(drow, a.V, t, lane, cy);
       const int lt = t / kSubTiles<T> - T0;
-      residual_tile<T>(a, b, t, lane_value(ref_t, lt), lane_value(ref_d, lt), lane_value(rho_l, lt), cx, cy);
+      residual_tile<T>(a, b, t, lane_value(ref_t, lt), lane_value(ref_d, lt), lane_value(hi_t, lt),
+                       lane_value(hi_d, lt), lane_value(rho_l, lt), cx, cy);
     } else {
       bonus_tile<T>(a, b, t, cx);
     }
@@ -783,11 +781,16 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
     mref_t = mm;
   }
   // Tile weights 2^((tile reference - row reference) * s) of the target and
-  // draft rows.  One pass gives the rows' normalisers and the residual's two
-  // positive-set masses; a thread that owns one tile keeps its weights for the
-  // scan below.
-  auto w_t = [&](double mt) { return mt == kNegInfD ? 0.0 : exp2((mt - (double)mref_t) * a.s64); };
-  auto w_d = [&](double md) { return md == kNegInfD ? 0.0 : exp2((md - (double)sr.m_d) * a.s64); };
+  // draft rows, times 2^-lo of the tile reference (the sampling pass's sums
+  // are relative to RN(reference * s)).  One pass gives the rows' normalisers
+  // and the residual's two positive-set masses; a thread that owns one tile
+  // keeps its weights for the scan below.
+  auto w_t = [&](double mt) {
+    return mt == kNegInfD ? 0.0 : exp2((mt - (double)mref_t) * a.s64) * exp_ref_scale((float)mt, a.s_hi);
+  };
+  auto w_d = [&](double md) {
+    return md == kNegInfD ? 0.0 : exp2((md - (double)sr.m_d) * a.s64) * exp_ref_scale((float)md, a.s_hi);
+  };
   double zbt = 0.0, zbd = 0.0, G = 0.0, H = 0.0, wt0 = 0.0, wd0 = 0.0;
   if (isfinite(mref_t)) {
     for (int tt = threadIdx.x; tt < NT; tt += kBlock) {
@@ -902,12 +905,12 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
     block_max2(mt, unused, sh_f);
   }
   const double gt = w_t((double)mt) * izt;
-  const double gd = use_d ? w_d((double)md) * izd : 0.0;
   tile_exp(x, mt, a, e);
   double w[V8];
   if (use_d) {
+    const double gd = w_d((double)md) * izd;
     tile_exp(y, md, a, f);
-    const float rho = tile_rho(mt, md, sr, a.s64);
+    const float rho = tile_rho(mt, md, sr, a.s64, a.s_hi);
 #pragma unroll
     for (int k = 0; k < V8; ++k) w[k] = e[k] * rho > f[k] ? (double)e[k] * gt - (double)f[k] * gd : 0.0;
   } else {
@@ -1245,7 +1248,6 @@ static VerifyArgs verify_args(const VerifyShape& s, const VerifyIO& io, const Ve
   a.TPWe = s.TPW_e;
   a.s64 = log2e_over(io.temperature);
   a.s_hi = (float)a.s64;
-  a.dmin = (float)(-200.0 / (double)a.s_hi);
   a.T = (double)io.temperature;
   a.part_a = ws.part_a;
   a.rows = ws.rows;

@@ -214,3 +214,22 @@ def test_chi_square_on_gpu():
         p = scipy.stats.chisquare(cnt, pt[i] * cnt.sum()).pvalue
         assert p > 1e-3 / (K + 1), (i, p)
         assert 0.5 * np.abs(cnt / cnt.sum() - pt[i]).sum() < 0.01
+
+
+@pytest.mark.parametrize("mode", ["sample", "greedy", "sample_early_exit"])
+def test_empty_batch(mode):
+    """B = 0 launches nothing and returns empty outputs; the next call on the
+    same stream is unaffected."""
+    import speculative_sampling_verification_vocab_amd as sv
+    print(f"case empty batch mode={mode}", flush=True)
+    dev = torch.device("cuda", 0)
+    t = torch.empty((0, 4, 100), dtype=torch.bfloat16, device=dev)
+    d = torch.empty((0, 3, 100), dtype=torch.bfloat16, device=dev)
+    tok = torch.empty((0, 3), dtype=torch.int32, device=dev)
+    uni = torch.empty((0, 4, 2), dtype=torch.float32, device=dev)
+    assert sv.spec_verify_launch_count(0, 3, 100, torch.bfloat16, mode) == 0
+    acc, out = sv.spec_verify(t, d, tok, uni, 1.0, mode)
+    torch.cuda.synchronize()
+    assert acc.shape == (0,) and out.shape == (0, 4)
+    c = _case(3, 3, 5000, "bf16", key=(26,))
+    check_case(c)

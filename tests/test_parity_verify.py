@@ -233,3 +233,37 @@ def test_empty_batch(mode):
     assert acc.shape == (0,) and out.shape == (0, 4)
     c = _case(3, 3, 5000, "bf16", key=(26,))
     check_case(c)
+
+
+def test_offsets_past_4_gib():
+    """A 4.25 GiB target tensor (B=17, K=1, V=2^26 bf16): the last sequence's
+    rows start at byte 2^32 of the target and 2^31 of the draft, so addresses
+    beyond 32 bits are exercised.  That sequence is checked against the oracle
+    in SAMPLE and GREEDY; SAMPLE_EARLY_EXIT gives SAMPLE's outputs."""
+    import speculative_sampling_verification_vocab_amd as sv
+    from tests.parity_util import compare
+    print("case offsets past 4 GiB: B=17 K=1 V=2^26 bf16", flush=True)
+    dev = torch.device("cuda", 0)
+    B, K, V = 17, 1, 1 << 26
+    c = verify_case(B, K, V, "bf16", target_std=3.0, zipf_s=1.1, sigma=0.7, temperature=1.0, key=(27,),
+                    device=dev)
+    assert c.target.numel() * 2 > (1 << 32) and c.draft.numel() * 2 > (1 << 31)
+    outs = {}
+    for m in ("sample", "sample_early_exit", "greedy"):
+        res = sv.spec_verify(c.target, c.draft, c.draft_tokens, c.uniforms,
+                             c.temperature if m != "greedy" else 0.0, m, return_probs=True)
+        torch.cuda.synchronize()
+        outs[m] = [r.cpu().numpy() for r in res]
+    np.testing.assert_array_equal(outs["sample_early_exit"][0], outs["sample"][0])
+    np.testing.assert_array_equal(outs["sample_early_exit"][1], outs["sample"][1])
+    s = slice(B - 1, B)
+    last = VerifyCase(c.target[s].cpu(), c.draft[s].cpu(), c.draft_tokens[s].cpu(), c.uniforms[s].cpu(),
+                      c.temperature, c.dtype)
+    del c
+    for m in ("sample", "greedy"):
+        o = outs[m]
+        greedy = m == "greedy"
+        rep = compare(o[0][s], o[1][s], run_oracle(last, m), K, greedy=greedy,
+                      gpu_pt=None if greedy else o[2][s], gpu_pd=None if greedy else o[3][s])
+        assert not rep.failures, rep.failures
+        assert rep.prob_max_rel < 1e-5

@@ -46,7 +46,7 @@ def _load():
             P = ctypes.c_void_p
             i32 = ctypes.c_int32
             lib.oracle_verify.argtypes = [P, P, ctypes.c_int, P, P, i32, i32, i32, ctypes.c_float,
-                                          ctypes.c_int, P, P, P, P, P, P, P, P]
+                                          ctypes.c_int, P, P, P, P, P, P, P, P, P, P]
             lib.oracle_verify.restype = ctypes.c_int
             lib.oracle_row_stats.argtypes = [P, ctypes.c_int, i32, i32, ctypes.c_float, P, P]
             lib.oracle_row_stats.restype = ctypes.c_int
@@ -89,13 +89,15 @@ def _np(x, dtype):
     return np.ascontiguousarray(x, dtype=dtype)
 
 
-def verify(target, draft, draft_tokens, uniforms, temperature, mode=SAMPLE, threads=1):
+def verify(target, draft, draft_tokens, uniforms, temperature, mode=SAMPLE, threads=1, probe_token=None):
     """Run the oracle over a batch.
 
     target [B,K+1,V] and draft [B,K,V]: bf16 torch tensors, uint16 bit arrays or
     float32 arrays.  draft may be None in GREEDY mode.  Returns a dict of numpy
     arrays: accepted_len, out_tokens, p_target, p_draft, accept_margin,
-    sample_margin, residual_mass, fallbacks.
+    sample_margin, residual_mass, fallbacks, and probe_gap when probe_token
+    (int32 [B], a token per sequence) is given: the normalised mass between
+    u*S and that token's cumulative interval at the oracle's sampled position.
     """
     lib = _load()
     tgt, dt = _as_logits(target)
@@ -115,6 +117,10 @@ def verify(target, draft, draft_tokens, uniforms, temperature, mode=SAMPLE, thre
         p_target=np.empty((B, K), np.float64), p_draft=np.empty((B, K), np.float64),
         accept_margin=np.empty((B, K), np.float64), sample_margin=np.empty(B, np.float64),
         residual_mass=np.empty(B, np.float64), fallbacks=np.empty(B, np.int32))
+    probe = None
+    if probe_token is not None:
+        probe = _np(probe_token, np.int32).reshape(B)
+        out["probe_gap"] = np.empty(B, np.float64)
 
     def run(b0, b1):
         n = b1 - b0
@@ -126,7 +132,9 @@ def verify(target, draft, draft_tokens, uniforms, temperature, mode=SAMPLE, thre
                           _ptr(out["accepted_len"][sl]), _ptr(out["out_tokens"][sl]),
                           _ptr(out["p_target"][sl]), _ptr(out["p_draft"][sl]),
                           _ptr(out["accept_margin"][sl]), _ptr(out["sample_margin"][sl]),
-                          _ptr(out["residual_mass"][sl]), _ptr(out["fallbacks"][sl]))
+                          _ptr(out["residual_mass"][sl]), _ptr(out["fallbacks"][sl]),
+                          _ptr(probe[sl]) if probe is not None else None,
+                          _ptr(out["probe_gap"][sl]) if probe is not None else None)
 
     if threads <= 1 or B <= 1:
         run(0, B)

@@ -93,6 +93,14 @@ static int row_ok(double m, double Z) { return isfinite(m) && isfinite(Z) && Z >
  *                         chosen token, divided by S
  *   residual_mass [B]     S of the sampled distribution (1 - beta for a residual)
  *   fallbacks     [B]     1 where S <= 0 forced the fallback to P_t
+ * Optional probe (both NULL, or both given):
+ *   probe_token   [B]     a token id per sequence (for instance another
+ *                         implementation's pick at the same position n)
+ *   probe_gap     [B] out the mass of the sampled distribution that lies
+ *                         between u*S and that token's cumulative interval
+ *                         [C_{g-1}, C_g], divided by S: 0 when u*S falls inside
+ *                         it, NaN for a faulty sequence, in GREEDY mode, or for
+ *                         an id outside [0, V)
  * Returns 0.
  */
 int oracle_verify(const void* target, const void* draft, int dtype,
@@ -101,7 +109,8 @@ int oracle_verify(const void* target, const void* draft, int dtype,
                   int32_t* accepted_len, int32_t* out_tokens,
                   double* p_target, double* p_draft,
                   double* accept_margin, double* sample_margin,
-                  double* residual_mass, int32_t* fallbacks) {
+                  double* residual_mass, int32_t* fallbacks,
+                  const int32_t* probe_token, double* probe_gap) {
   const double T = (double)temperature;
   double* mt = (double*)malloc(sizeof(double) * (size_t)(K + 1));
   double* Zt = (double*)malloc(sizeof(double) * (size_t)(K + 1));
@@ -126,6 +135,7 @@ int oracle_verify(const void* target, const void* draft, int dtype,
     }
     if (sample_margin) sample_margin[b] = NAN;
     if (residual_mass) residual_mass[b] = NAN;
+    if (probe_gap) probe_gap[b] = NAN;
     if (fallbacks) fallbacks[b] = 0;
 
     if (mode == OR_GREEDY) {
@@ -228,6 +238,19 @@ int oracle_verify(const void* target, const void* draft, int dtype,
     }
     if (sample_margin) sample_margin[b] = margin;
     if (residual_mass) residual_mass[b] = S;
+
+    /* Distance of u*S from the probe token's interval [C_{g-1}, C_g], in the
+     * same cumulative sums as the pick above. */
+    if (probe_token && probe_gap && probe_token[b] >= 0 && probe_token[b] < V) {
+      const int32_t g = probe_token[b];
+      double Cg0 = 0.0;
+      for (int32_t v = 0; v < g; ++v) Cg0 += w[v];
+      const double Cg1 = Cg0 + w[g];
+      double gap = 0.0;
+      if (target_mass < Cg0) gap = Cg0 - target_mass;
+      else if (target_mass > Cg1) gap = target_mass - Cg1;
+      probe_gap[b] = gap / S;
+    }
 
     accepted_len[b] = n;
     for (int32_t i = 0; i < n; ++i) out[i] = d[i];

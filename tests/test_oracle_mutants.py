@@ -13,7 +13,9 @@ import tempfile
 import pytest
 
 import oracle
+from tests import test_oracle_enumeration as enum_pins
 from tests import test_oracle_kv as kv_pins
+from tests import test_oracle_margins as margin_pins
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
@@ -35,6 +37,19 @@ MUTANTS = {
     "emit_draft_at_rejection": ("out[n] = pick;", "out[n] = n < K ? d[n] : pick;"),
     "zero_ratio_accepts": ("double ratio = pd > 0.0 ? pt / pd : INFINITY;",
                            "double ratio = pd > 0.0 ? pt / pd : 0.0;"),
+    # tie-band outputs and the rounding fallbacks
+    "sample_margin_lower_gap_only": ("margin = (lo < hi ? lo : hi) / S;", "margin = lo / S;"),
+    "sample_margin_not_divided_by_mass": ("margin = (lo < hi ? lo : hi) / S;", "margin = (lo < hi ? lo : hi);"),
+    "accept_margin_against_ratio": ("accept_margin[(size_t)b * K + i] = fabs(ui - thr);",
+                                    "accept_margin[(size_t)b * K + i] = fabs(ui - ratio);"),
+    "no_crossing_picks_smallest": ("for (int32_t v = V - 1; v >= 0; --v) if (w[v] > 0.0) { pick = v; break; }",
+                                   "for (int32_t v = 0; v < V; ++v) if (w[v] > 0.0) { pick = v; break; }"),
+    "no_crossing_picks_last_id": ("for (int32_t v = V - 1; v >= 0; --v) if (w[v] > 0.0) { pick = v; break; }",
+                                  "pick = V - 1;"),
+    "no_zero_residual_fallback": ("if (!(S > 0.0)) {", "if (0) {"),
+    "zero_residual_fallback_uncounted": ("if (fallbacks) fallbacks[b] = 1;", "(void)0;"),
+    "probe_interval_without_own_weight": ("const double Cg1 = Cg0 + w[g];", "const double Cg1 = Cg0;"),
+    "probe_gap_not_divided_by_mass": ("probe_gap[b] = gap / S;", "probe_gap[b] = gap;"),
     "kv_commit_off_by_one": ("(size_t)Lmax + (size_t)(len + j)) * (size_t)row_bytes;",
                              "(size_t)Lmax + (size_t)(len + j + 1)) * (size_t)row_bytes;"),
     "kv_commit_includes_rejected": ("for (int32_t j = 0; j < n; ++j) {", "for (int32_t j = 0; j <= n && j < K; ++j) {"),
@@ -55,6 +70,20 @@ PINS = [
     pins.test_inverse_cdf_skips_zero_weight_tokens,
     pins.test_expected_tokens_closed_form,
     lambda: pins.test_chi_square_output_follows_target(2.0),
+    lambda: enum_pins.test_oracle_law_equals_the_exact_law("v4_k3"),
+    lambda: enum_pins.test_oracle_law_equals_the_exact_law("v3_k2_t07"),
+    margin_pins.test_accept_margin_below_threshold_exact,
+    margin_pins.test_accept_margin_above_threshold_exact,
+    margin_pins.test_accept_margin_is_measured_against_the_clamped_threshold,
+    margin_pins.test_accept_margin_with_zero_draft_probability,
+    margin_pins.test_sample_margin_of_a_residual_upper_gap_nearer,
+    margin_pins.test_sample_margin_of_a_residual_lower_gap_nearer,
+    margin_pins.test_sample_margin_of_a_bonus_token,
+    margin_pins.test_probe_gap_of_a_residual,
+    margin_pins.test_probe_gap_of_a_bonus_token,
+    margin_pins.test_probe_gap_undefined_cases,
+    margin_pins.test_zero_residual_falls_back_to_the_target_row,
+    margin_pins.test_no_crossing_takes_the_largest_id_of_positive_weight,
     kv_pins.test_exercise_prefix_plus_accepted_drafts,
     kv_pins.test_multi_step_cache_holds_the_committed_stream,
     kv_pins.test_status_cases_commit_nothing,
@@ -68,7 +97,8 @@ def _build_mutant(name, old, new, tmp):
     with open(path, "w") as f:
         f.write(src.replace(old, new))
     so = os.path.join(tmp, f"lib{name}.so")
-    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", so, path, "-lm"])
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
+                           "-o", so, path, "-lm"])
     return so
 
 
@@ -91,3 +121,24 @@ def test_mutant_is_caught(name, monkeypatch):
                 caught.append(getattr(pin, "__name__", "pin"))
                 break
         assert caught, f"mutant {name} passed every pin"
+
+
+@pytest.mark.parametrize("name", ["no_clamp", "scalar_residual", "residual_uses_previous_draft_row",
+                                  "bonus_from_last_draft_position", "last_rejection",
+                                  "emit_draft_at_rejection", "temperature_multiplies"])
+def test_enumeration_pin_alone_catches_rule_mutants(name, monkeypatch):
+    """The exact-law pin by itself rejects every mutant of the rule's steps.
+    (The strictness mutants, <= for < in the accept test and >= for > in the
+    inverse CDF, change the output only on boundaries of measure zero; the
+    boundary pins catch them, and an infinite ratio concerns only tokens the
+    draft gives probability 0, which the enumeration never proposes.)"""
+    old, new = MUTANTS[name]
+    real = oracle._load()
+    with tempfile.TemporaryDirectory() as tmp:
+        lib = ctypes.CDLL(_build_mutant(name, old, new, tmp))
+        lib.oracle_verify.argtypes = real.oracle_verify.argtypes
+        lib.oracle_verify.restype = real.oracle_verify.restype
+        monkeypatch.setattr(oracle, "_lib", lib)
+        with pytest.raises(AssertionError):
+            for case in sorted(enum_pins.CASES):
+                enum_pins.test_oracle_law_equals_the_exact_law(case)

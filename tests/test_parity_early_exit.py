@@ -46,7 +46,7 @@ def check_early_exit(case, vs_oracle=True):
             assert not np.any(np.isnan(ee[k][b, :upto]))
             assert np.all(np.isnan(ee[k][b, upto:]))
     if vs_oracle:
-        orc = dict(run_oracle(case))
+        orc = dict(run_oracle(case, gpu=ee))
         for key, k in (("p_target", 2), ("p_draft", 3)):
             q = np.array(orc[key], dtype=np.float64, copy=True)
             q[np.isnan(ee[k])] = np.nan

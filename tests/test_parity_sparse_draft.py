@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from tests.parity_util import PROB_RTOL, compare, run_gpu
+from tests.parity_util import PROB_RTOL, compare, probe_tokens, run_gpu
 from workloads import VerifyCase, sparse_draft_case
 
 pytestmark = pytest.mark.gpu
@@ -29,7 +29,7 @@ def run_sparse(c):
 def check_sparse(c):
     out = run_sparse(c)
     orc = oracle.verify(c.target.cpu(), c.dense_draft.cpu(), c.draft_tokens.cpu(), c.uniforms.cpu(),
-                        c.temperature, threads=oracle.default_threads())
+                        c.temperature, threads=oracle.default_threads(), probe_token=probe_tokens(out[0], out[1]))
     rep = compare(out[0], out[1], orc, c.K, gpu_pt=out[2], gpu_pd=out[3])
     assert not rep.failures, rep.failures[:5]
     assert rep.prob_max_rel <= PROB_RTOL, rep.prob_max_rel
@@ -77,7 +77,9 @@ def test_full_shortlist_matches_dense_verify():
     assert torch.equal(c.compact.float().reshape(8, 3, -1), c.dense_draft.float())
     rep, out, orc = check_sparse(c)
     dense = run_gpu(VerifyCase(c.target, c.dense_draft, c.draft_tokens, c.uniforms, c.temperature, "bf16"))
-    rep2 = compare(dense[0], dense[1], orc, c.K)
+    orc2 = oracle.verify(c.target, c.dense_draft, c.draft_tokens, c.uniforms, c.temperature,
+                         probe_token=probe_tokens(dense[0], dense[1]))
+    rep2 = compare(dense[0], dense[1], orc2, c.K)
     assert not rep2.failures
     np.testing.assert_array_equal(out[0], dense[0])
 

@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests.parity_util import Report, check_case, compare, run_gpu, run_oracle
+from tests.parity_util import Report, check_case, compare, probe_tokens, run_gpu, run_oracle
 from workloads import gumbel_max_tokens, verify_uniforms, workload_case
 
 pytestmark = pytest.mark.gpu
@@ -144,7 +144,7 @@ def test_b256_k7_v262144_bf16_fifty_seeds():
         out = run_gpu(c)
         c = _to_host(c)
         orc = oracle.verify(c.target, c.draft, c.draft_tokens, c.uniforms, c.temperature,
-                            threads=oracle.default_threads())
+                            threads=oracle.default_threads(), probe_token=probe_tokens(out[0], out[1]))
         rep = compare(out[0], out[1], orc, c.K, gpu_pt=out[2], gpu_pd=out[3])
         total.merge(rep)
         print(f"seed {trial}: excused {rep.excused} failures {len(rep.failures)} "

@@ -171,6 +171,7 @@ def workload_case(name: str, *, sweep: int = 0, trial: int = 0, device="cpu",
                            (greedy=True: argmax drafts, temperature 0)
     b64_k4_v151936_bf16  : target N(0,2^2), sigma in (0.1, 0.5, 1.0, 2.0)[sweep], T=1
     b256_k7_v262144_bf16 : target N(0,3^2)+Zipf(1.1), sigma 0.7, T=1
+                           (greedy=True: argmax drafts)
     """
     wid = WORKLOAD_IDS[name]
     key = (0, wid, sweep)
@@ -188,7 +189,7 @@ def workload_case(name: str, *, sweep: int = 0, trial: int = 0, device="cpu",
                            temperature=1.0, key=key + (trial,), device=device)
     if name == "b256_k7_v262144_bf16":
         return verify_case(256, 7, 262144, "bf16", target_std=3.0, zipf_s=1.1, sigma=0.7,
-                           temperature=1.0, key=key + (trial,), device=device)
+                           temperature=1.0, key=key + (trial,), device=device, greedy_drafts=greedy)
     raise KeyError(name)
 
 

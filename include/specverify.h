@@ -50,7 +50,14 @@ extern "C" {
 #define SPEC_ABI_VERSION 1
 #define SPEC_MAX_K 64
 
-typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
+/*
+ * The dtype, mode and status arguments are fixed-width integers with named
+ * values (not C enum types), so any value a caller passes is well defined on
+ * both sides of the ABI; an unknown value is rejected with
+ * SPEC_ERR_INVALID_ARG.
+ */
+typedef int32_t spec_dtype_t;
+enum { SPEC_F32 = 0, SPEC_BF16 = 1 };
 /*
  * SAMPLE: the Leviathan/Chen rule (accept with probability min(1, P_t/P_d)
  *   left to right, resample (P_t - P_d)_+ at the first rejection, bonus token
@@ -64,14 +71,16 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
  *   rejection, and a non-finite row after it does not mark the sequence
  *   faulty (draft tokens are still checked at every position).
  */
-typedef enum { SPEC_MODE_SAMPLE = 0, SPEC_MODE_GREEDY = 1, SPEC_MODE_SAMPLE_EARLY_EXIT = 2 } spec_mode_t;
-typedef enum {
+typedef int32_t spec_mode_t;
+enum { SPEC_MODE_SAMPLE = 0, SPEC_MODE_GREEDY = 1, SPEC_MODE_SAMPLE_EARLY_EXIT = 2 };
+typedef int32_t spec_status_t;
+enum {
   SPEC_OK = 0,
-  SPEC_ERR_INVALID_ARG = 1, /* NULL pointer, negative size, bad temperature, bad enum, overflow */
+  SPEC_ERR_INVALID_ARG = 1, /* NULL pointer, negative size, bad temperature, unknown dtype or mode, overflow */
   SPEC_ERR_UNSUPPORTED = 2, /* K > SPEC_MAX_K, V > 2^30, a grid too large for one launch, V % cluster_size != 0 */
   SPEC_ERR_WORKSPACE = 3,   /* workspace NULL, too small, or not 256-byte aligned */
   SPEC_ERR_HIP = 4          /* a HIP launch failed */
-} spec_status_t;
+};
 
 /* Library ABI version (SPEC_ABI_VERSION of the build). */
 int spec_abi_version(void);
@@ -217,6 +226,17 @@ spec_status_t spec_draft_head_shortlist(const void* h, const void* W, const int3
                                         float* logits_compact, void* dense_out,
                                         spec_dtype_t dense_dtype,
                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Clusters selected at draft position t (0-based) under the position-aware
+ * budget k_c(t) of the DynaSpec summary ("Model architecture" item 3): k_max
+ * at t = 0 and t = 1, floor(k_max / ((t + 1) * 2)) for t >= 2.  The budget
+ * reaches 0 at t >= k_max / 2 (t >= 8 for k_max = 16): such a position has no
+ * shortlist, so a draft must stop before it (spec_draft_head_positions accepts
+ * n_sel = 0 and writes nothing for it; spec_verify_sparse_draft needs
+ * n_sel >= 1).  Host function, no GPU work.  Returns -1 if t < 0 or k_max < 1.
+ */
+int32_t spec_position_budget(int32_t t, int32_t k_max);
 
 /*
  * Shortlisted drafter head with a shortlist per draft position (DynaSpec

@@ -123,7 +123,7 @@ int oracle_verify(const void* target, const void* draft, int dtype,
     const size_t drow0 = (size_t)b * (size_t)K * (size_t)V;
     int32_t* out = out_tokens + (size_t)b * (size_t)(K + 1);
     const int32_t* d = tokens + (size_t)b * (size_t)K;
-    const float* u = uniforms + (size_t)b * (size_t)(K + 1) * 2;
+    const float* u = uniforms ? uniforms + (size_t)b * (size_t)(K + 1) * 2 : NULL; /* NULL in GREEDY mode */
     int faulty = 0;
     int32_t n = K;
 

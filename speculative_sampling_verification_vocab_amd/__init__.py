@@ -44,9 +44,12 @@ def _need_gpu(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _stream_of(device: torch.device, stream=None):
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
 def _stream_handle(device: torch.device, stream=None):
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(_stream_of(device, stream).cuda_stream)
 
 
 def spec_verify_workspace_bytes(B: int, K: int, V: int, dtype: torch.dtype, mode: str = "sample") -> int:
@@ -61,26 +64,39 @@ def spec_verify_launch_count(B: int, K: int, V: int, dtype: torch.dtype, mode: s
 class Workspace:
     """A device scratch buffer reused across calls; it grows to the largest size asked for.
 
-    Calls that share one Workspace must be ordered on the GPU (same stream)."""
+    Calls that share one Workspace must be ordered on the GPU (same stream, or
+    synchronised).  The buffer is allocated on the stream of the call that
+    grows it, and every use on another stream is recorded with the caching
+    allocator (``record_stream``), so a buffer that is replaced is not handed
+    out again while kernels on any stream that used it may still run."""
 
     def __init__(self, device):
         self.device = torch.device(device)
         self.buf = torch.empty(0, dtype=torch.uint8, device=self.device)
+        self._stream = None
 
-    def get(self, nbytes: int) -> torch.Tensor:
+    def get(self, nbytes: int, stream=None) -> torch.Tensor:
+        s = _stream_of(self.device, stream)
         if self.buf.numel() < nbytes:
-            self.buf = torch.empty(max(nbytes, 2 * self.buf.numel()), dtype=torch.uint8, device=self.device)
+            with torch.cuda.stream(s):
+                self.buf = torch.empty(max(nbytes, 2 * self.buf.numel()), dtype=torch.uint8, device=self.device)
+            self._stream = s
+        elif s != self._stream:
+            self.buf.record_stream(s)
         return self.buf
 
 
 _default_ws = {}
 
 
-def _workspace_for(device) -> Workspace:
-    key = torch.device(device)
-    if key not in _default_ws:
-        _default_ws[key] = Workspace(key)
-    return _default_ws[key]
+def _workspace_for(device, stream=None) -> Workspace:
+    """The default workspace of (device, stream): calls on different streams never share scratch."""
+    dev = torch.device(device)
+    key = (dev, _stream_of(dev, stream).cuda_stream)
+    ws = _default_ws.get(key)
+    if ws is None:
+        ws = _default_ws[key] = Workspace(dev)
+    return ws
 
 
 def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: Optional[torch.Tensor],
@@ -135,7 +151,7 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_token
     pt = torch.empty((B, K), dtype=torch.float32, device=dev) if return_probs else None
     pd = torch.empty((B, K), dtype=torch.float32, device=dev) if return_probs else None
     need = lib.spec_verify_workspace_bytes(B, K, V, dt, _MODES[mode])
-    ws = (workspace or _workspace_for(dev)).get(need)
+    ws = (workspace or _workspace_for(dev, stream)).get(need, stream)
     args = [_ptr(target), _ptr(draft) if sampling else None,
             _ptr(draft_tokens) if K > 0 else None, _ptr(uniforms) if sampling else None,
             B, K, V, dt, ctypes.c_float(temperature if sampling else 0.0), _MODES[mode],
@@ -215,13 +231,11 @@ def spec_kv_commit(cache: torch.Tensor, staging: torch.Tensor, accepted_len: tor
 
 
 def position_budget(t: int, k_max: int) -> int:
-    """Clusters selected for draft position t (0-based) under DynaSpec's
-    position-aware budget (DynaSpec summary, "Model architecture" item 3):
-    k_max for t in {0, 1}, floor(k_max / ((t + 1) * 2)) after that, and at
-    least one cluster so that every position keeps a shortlist."""
-    if t < 0 or k_max < 1:
+    """Clusters selected at draft position t (spec_position_budget of the C ABI)."""
+    r = int(_native.load().spec_position_budget(int(t), int(k_max)))
+    if r < 0:
         raise ValueError("t >= 0 and k_max >= 1")
-    return k_max if t < 2 else max(1, k_max // ((t + 1) * 2))
+    return r
 
 
 def spec_verify_sparse_draft(target: torch.Tensor, draft_compact: torch.Tensor, cluster_ids: torch.Tensor,
@@ -268,7 +282,7 @@ def spec_verify_sparse_draft(target: torch.Tensor, draft_compact: torch.Tensor, 
     pt = torch.empty((B, K), dtype=torch.float32, device=dev) if return_probs else None
     pd = torch.empty((B, K), dtype=torch.float32, device=dev) if return_probs else None
     need = lib.spec_verify_workspace_bytes(B, K, V, dt, _MODES["sample"])
-    ws = (workspace or _workspace_for(dev)).get(need)
+    ws = (workspace or _workspace_for(dev, stream)).get(need, stream)
     st = lib.spec_verify_sparse_draft(_ptr(target), _ptr(draft_compact) if K > 0 else None,
                                       _ptr(cluster_ids) if K > 0 else None, ns, L, S, int(cluster_size),
                                       _ptr(draft_tokens) if K > 0 else None, _ptr(uniforms), B, K, V, dt,

@@ -65,6 +65,8 @@ def load() -> ctypes.CDLL:
         lib.spec_draft_head_positions.restype = ctypes.c_int
         lib.spec_draft_head_static.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, ctypes.c_int, P]
         lib.spec_draft_head_static.restype = ctypes.c_int
+        lib.spec_position_budget.argtypes = [i32, i32]
+        lib.spec_position_budget.restype = i32
         lib.spec_kv_commit.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_int, P]
         lib.spec_kv_commit.restype = ctypes.c_int
         _lib = lib

@@ -4,19 +4,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace sv {
+#include "sv_host.h"
 
-constexpr int kWave = 64;
-constexpr int kWavesPerBlock = 4;
-constexpr int kBlock = kWave * kWavesPerBlock;
-constexpr int kLoads = 8;   // 16-byte loads per lane per tile of the streaming passes
-constexpr int kLoadsS = 4;  // 16-byte loads per lane per tile of the sampling pass
-constexpr int kMaxK = 64;
+namespace sv {
 
 // Storage element types: bf16 logits are handled as their uint16 bit patterns.
 template <typename T> struct Elem;
-template <> struct Elem<uint16_t> { static constexpr int kVec = 8; };
-template <> struct Elem<float> { static constexpr int kVec = 4; };
+template <> struct Elem<uint16_t> { static constexpr int kVec = vec_elems(2); };
+template <> struct Elem<float> { static constexpr int kVec = vec_elems(4); };
 
 template <typename T> constexpr int kPerLane = Elem<T>::kVec * kLoads;    // 64 bf16, 32 f32
 template <typename T> constexpr int kTile = kWave * kPerLane<T>;           // 4096 bf16, 2048 f32

@@ -32,7 +32,7 @@ constexpr int kStageK = 256;       // hidden dims per LDS stage (128 and 512 mea
 constexpr int kLdsStride = kStageK;
 // Element offset of (row, 8-aligned column) in a staged LDS tile.
 __device__ __forceinline__ int lds_at(int row, int col) { return row * kLdsStride + (((col >> 3) ^ (row & 15)) << 3); }
-constexpr int kMaxCtx = 1024;      // contexts listed per cluster (host-checked: B <= kMaxCtx)
+constexpr int kMaxCtx = kHeadMaxCtx;  // contexts listed per cluster (host-checked: B <= kMaxCtx)
 
 struct HeadArgs {
   const uint16_t* h;    // bf16 [B, K, d]
@@ -350,6 +350,5 @@ hipError_t launch_head(const void* h, const void* W, const int32_t* cluster_ids,
   return hipGetLastError();
 }
 
-int head_max_contexts() { return kMaxCtx; }
 
 }  // namespace sv

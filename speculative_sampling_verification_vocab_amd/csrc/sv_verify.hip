@@ -49,10 +49,6 @@ namespace sv {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
-// Sampling tiles per wave: several amortise the per-block accept prologue
-// over more work; small batches take fewer so the grid still fills the chip.
-constexpr int kMaxTilesPerWaveS = 8;
-constexpr int kSampleBlocksWanted = 1024;  // 4 per CU
 
 struct VerifyArgs {
   const void* target;
@@ -997,7 +993,6 @@ __global__ void __launch_bounds__(kBlock) pick_kernel(VerifyArgs a) {
 // tile before the decision, so that the two latencies overlap, measured 13 %
 // slower over the phases: the tiles of sequences that reject at i - 1 are
 // read for nothing.
-constexpr int kEEBlocksForTwo = 4096;  // phase blocks at one tile per wave from which waves take two
 
 // Phase i of the early-exit schedule: statistics of target and draft row i
 // for the sequences that accepted positions 0..i-1.  For i > 0 every block
@@ -1163,74 +1158,6 @@ double log2e_over(float temperature) { return 1.4426950408889634073599 / (double
 
 }  // namespace
 
-int tile_elems(int dtype) { return dtype == 1 ? kTile<uint16_t> : kTile<float>; }
-
-VerifyShape make_shape(int B, int K, int V, int dtype, bool aligned) {
-  VerifyShape s;
-  s.B = B;
-  s.K = K;
-  s.V = V;
-  s.dtype = dtype;
-  s.aligned = aligned;
-  s.tile = tile_elems(dtype);
-  s.NT = (V + s.tile - 1) / s.tile;
-  s.NG = (s.NT + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int tile_s = dtype == 1 ? kTileS<uint16_t> : kTileS<float>;
-  s.NT_s = (V + tile_s - 1) / tile_s;
-  s.TPW_s = 1;
-  for (int tpw = kMaxTilesPerWaveS; tpw > 1; tpw /= 2) {
-    const long long blocks = (long long)B * ((s.NT_s + tpw * kWavesPerBlock - 1) / (tpw * kWavesPerBlock));
-    if (blocks >= kSampleBlocksWanted) {
-      s.TPW_s = tpw;
-      break;
-    }
-  }
-  s.NG_s = (s.NT_s + s.TPW_s * kWavesPerBlock - 1) / (s.TPW_s * kWavesPerBlock);
-  s.TPW_e = (long long)B * 2 * s.NG >= kEEBlocksForTwo ? 2 : 1;
-  // A separate decision launch pays off once blocks cover several sampling
-  // tiles (B=256, K=7, V=262144: 353 -> 348 us; B=8: 21.8 -> 24.5 us with it).
-  s.decide = s.TPW_s > 1;
-  return s;
-}
-
-static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-size_t verify_workspace_layout(const VerifyShape& s, int mode, void* base, VerifyWorkspace* out) {
-  const size_t B = (size_t)s.B, K = (size_t)s.K;
-  const bool greedy = mode == 1, early = mode == 2;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t at = off;
-    off = align256(off + bytes);
-    return at;
-  };
-  size_t o_pa = 0, o_rows = 0, o_pb = 0, o_pg = 0, o_gx = 0, o_cont = 0;
-  if (greedy) {
-    o_pg = take(B * (K + 1) * (size_t)s.NT * sizeof(ArgTile));
-  } else {
-    o_pa = take(B * 2 * K * (size_t)s.NT * sizeof(TileStat));
-    o_rows = take(B * sizeof(SampleRowInfo));
-    o_pb = take(B * (size_t)s.NT_s * sizeof(SampleTile));
-    o_gx = take(B * 2 * (K > 0 ? K : 1) * sizeof(float));
-    if (early) o_cont = take(B * (K > 0 ? K : 1) * sizeof(int32_t));
-  }
-  if (out && base) {
-    VerifyWorkspace w{};
-    char* p = static_cast<char*>(base);
-    if (greedy) {
-      w.part_g = reinterpret_cast<ArgTile*>(p + o_pg);
-    } else {
-      w.part_a = reinterpret_cast<TileStat*>(p + o_pa);
-      w.rows = reinterpret_cast<SampleRowInfo*>(p + o_rows);
-      w.part_b = reinterpret_cast<SampleTile*>(p + o_pb);
-      w.gx = reinterpret_cast<float*>(p + o_gx);
-      if (early) w.cont = reinterpret_cast<int32_t*>(p + o_cont);
-    }
-    *out = w;
-  }
-  return off;
-}
-
 static VerifyArgs verify_args(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws) {
   VerifyArgs a{};
   a.target = io.target;
@@ -1268,8 +1195,6 @@ static VerifyArgs verify_args(const VerifyShape& s, const VerifyIO& io, const Ve
   a.p_d_out = io.p_draft;
   return a;
 }
-
-int sample_launches(const VerifyShape& s) { return s.B == 0 ? 0 : (s.decide ? 4 : 3); }
 
 template <bool kSparse>
 static hipError_t sample_pipeline(const VerifyShape& s, const VerifyArgs& a, hipStream_t st, void* const* events,
@@ -1324,8 +1249,6 @@ hipError_t launch_sample_pipeline(const VerifyShape& s, const VerifyIO& io, cons
   return io.cids ? sample_pipeline<true>(s, a, st, events, n_events)
                  : sample_pipeline<false>(s, a, st, events, n_events);
 }
-
-int early_exit_launches(const VerifyShape& s) { return s.B == 0 ? 0 : s.K + 2; }
 
 hipError_t launch_early_exit_pipeline(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws,
                                       hipStream_t st, void* const* events, int n_events) {

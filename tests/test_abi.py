@@ -194,3 +194,23 @@ def test_sparse_draft_validation(lib):
     assert call(L=2003) == INVALID                       # 4 clusters of 501 do not fit L
     assert call(S=9) == INVALID                          # more slots than clusters
     assert call(T=0.0) == INVALID
+
+
+def test_position_budget_matches_the_printed_formula(lib):
+    """spec_position_budget against k_c(t) of the DynaSpec summary ("Model
+    architecture" item 3), evaluated by hand (tests/golden)."""
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", "dynaspec_position_budget.json")) as f:
+        g = json.load(f)
+    for key, want in g.items():
+        if not key.startswith("k_max_"):
+            continue
+        k_max = int(key[len("k_max_"):])
+        assert [lib.spec_position_budget(t, k_max) for t in range(len(want))] == want, key
+    assert lib.spec_position_budget(-1, 16) == -1
+    assert lib.spec_position_budget(0, 0) == -1
+    assert lib.spec_position_budget(2 ** 31 - 1, 2 ** 31 - 1) == 0        # no overflow in (t + 1) * 2
+    from speculative_sampling_verification_vocab_amd import position_budget
+    assert [position_budget(t, 16) for t in range(5)] == [16, 16, 2, 2, 1]
+    with pytest.raises(ValueError):
+        position_budget(-1, 16)

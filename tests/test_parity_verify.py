@@ -263,7 +263,39 @@ def test_offsets_past_4_gib():
     for m in ("sample", "greedy"):
         o = outs[m]
         greedy = m == "greedy"
-        rep = compare(o[0][s], o[1][s], run_oracle(last, m), K, greedy=greedy,
+        rep = compare(o[0][s], o[1][s], run_oracle(last, m, gpu=(o[0][s], o[1][s])), K, greedy=greedy,
                       gpu_pt=None if greedy else o[2][s], gpu_pd=None if greedy else o[3][s])
         assert not rep.failures, rep.failures
         assert rep.prob_max_rel < 1e-5
+
+
+def test_concurrent_streams_use_separate_default_workspaces():
+    """Two calls on two streams at once, without explicit workspaces: each
+    stream gets its own default scratch, so both match their single-stream
+    results (and the oracle)."""
+    import speculative_sampling_verification_vocab_amd as sv
+    print("case concurrent streams: 2 x (B=64 K=4 V=40000 bf16)", flush=True)
+    dev = torch.device("cuda", 0)
+    cases = [verify_case(64, 4, 40000, "bf16", target_std=3.0, zipf_s=1.1, sigma=0.7, temperature=1.0,
+                         key=(31, j), device=dev) for j in range(2)]
+    ref = []
+    for c in cases:
+        res = sv.spec_verify(c.target, c.draft, c.draft_tokens, c.uniforms, c.temperature, "sample")
+        ref.append([r.cpu().numpy() for r in res])
+    streams = [torch.cuda.Stream(dev) for _ in cases]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream(dev))
+    outs = []
+    for rep in range(3):
+        outs = []
+        for c, s in zip(cases, streams):
+            with torch.cuda.stream(s):
+                outs.append(sv.spec_verify(c.target, c.draft, c.draft_tokens, c.uniforms, c.temperature, "sample"))
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            np.testing.assert_array_equal(o[0].cpu().numpy(), r[0])
+            np.testing.assert_array_equal(o[1].cpu().numpy(), r[1])
+    for c, r in zip(cases, ref):
+        hc = VerifyCase(c.target.cpu(), c.draft.cpu(), c.draft_tokens.cpu(), c.uniforms.cpu(), c.temperature, c.dtype)
+        rep = compare(r[0], r[1], run_oracle(hc, gpu=r), c.K)
+        assert not rep.failures, rep.failures[:3]

@@ -166,6 +166,35 @@ spec_status_t spec_verify_timed(const void* target_logits, const void* draft_log
                                 void* const* events, int32_t n_events);
 
 /*
+ * spec_verify for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same call without the workspace argument.  Its kernels use the library's
+ * own scratch instead, a static device array of SPEC_NOALLOC_SCRATCH_BYTES on
+ * every GPU the library runs on (held until the process ends), located once
+ * per device on the first call made with that device current.  The call
+ * allocates nothing.
+ *
+ * Arguments, rule, outputs and errors are those of spec_verify, and the
+ * outputs are identical to spec_verify's.  In addition:
+ *   - SPEC_ERR_WORKSPACE (before anything is enqueued) when the shape needs
+ *     more than SPEC_NOALLOC_SCRATCH_BYTES (spec_verify_workspace_bytes()
+ *     gives the need; B=256, K=7, V=262144 bf16 SAMPLE needs about 3.4 MB);
+ *   - SPEC_ERR_INVALID_ARG when `stream` belongs to another device than the
+ *     current one; SPEC_ERR_HIP when the scratch cannot be located.
+ * Every call on one GPU shares that GPU's scratch, which keeps the previous
+ * call's contents (the kernels need no cleared memory).  Calls ordered on one
+ * stream are safe; calls that overlap on one GPU (several streams, or threads
+ * without ordering) race on the scratch.
+ */
+#define SPEC_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+spec_status_t spec_verify_noalloc(const void* target_logits, const void* draft_logits,
+                                  const int32_t* draft_tokens, const float* uniforms,
+                                  int32_t B, int32_t K, int32_t V, spec_dtype_t dtype,
+                                  float temperature, spec_mode_t mode,
+                                  int32_t* accepted_len, int32_t* out_tokens,
+                                  float* p_target_at_draft, float* p_draft_at_draft, void* stream);
+
+/*
  * Verify with a sparse draft (DynaSpec summary: the drafter's logits exist
  * only on a shortlist, the union of the clusters selected for the context
  * and position; verification keeps the full vocabulary and the exact rule).

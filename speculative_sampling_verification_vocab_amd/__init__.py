@@ -18,7 +18,7 @@ import torch
 from . import _native
 from ._native import SpecVerifyError  # noqa: F401
 
-__all__ = ["spec_verify", "spec_verify_workspace_bytes", "spec_verify_launch_count", "spec_draft_head_shortlist",
+__all__ = ["spec_verify", "spec_verify_noalloc", "spec_verify_workspace_bytes", "spec_verify_launch_count", "spec_draft_head_shortlist",
            "spec_kv_commit", "spec_verify_sparse_draft", "position_budget", "spec_draft_head_positions",
            "spec_draft_head_static",
            "Workspace", "SpecVerifyError", "abi_version"]
@@ -115,36 +115,8 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_token
     accepted_len and out_tokens, reading only the rows up to each sequence's
     first rejection; probabilities after it are NaN) or "greedy".
     """
-    if mode not in _MODES:
-        raise ValueError(f"mode must be one of {list(_MODES)}")
-    _need_gpu(target, "target")
-    if target.dim() != 3:
-        raise ValueError("target must be [B, K+1, V]")
-    B, K1, V = target.shape
-    K = K1 - 1
-    dt = _DTYPES.get(target.dtype)
-    if dt is None:
-        raise ValueError("logits must be bfloat16 or float32")
+    B, K, V, dt, sampling = _check_verify_inputs(target, draft, draft_tokens, uniforms, mode)
     dev = target.device
-    sampling = mode in _SAMPLING
-    if sampling and K > 0:
-        if draft is None:
-            raise ValueError("draft logits are required in sample mode")
-        _need_gpu(draft, "draft")
-        if draft.dtype != target.dtype or tuple(draft.shape) != (B, K, V):
-            raise ValueError("draft must match target dtype and be [B, K, V]")
-    if K > 0:
-        if draft_tokens is None:
-            raise ValueError("draft_tokens are required when K > 0")
-        _need_gpu(draft_tokens, "draft_tokens")
-        if draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != (B, K):
-            raise ValueError("draft_tokens must be int32 [B, K]")
-    if sampling:
-        if uniforms is None:
-            raise ValueError("uniforms are required in sample mode")
-        _need_gpu(uniforms, "uniforms")
-        if uniforms.dtype != torch.float32 or tuple(uniforms.shape) != (B, K + 1, 2):
-            raise ValueError("uniforms must be float32 [B, K+1, 2]")
     lib = _native.load()
     acc = torch.empty(B, dtype=torch.int32, device=dev)
     out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
@@ -166,6 +138,65 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_token
     if return_probs:
         return acc, out, pt, pd
     return acc, out
+
+
+def _check_verify_inputs(target, draft, draft_tokens, uniforms, mode):
+    """Shape and dtype checks shared by spec_verify and spec_verify_noalloc."""
+    if mode not in _MODES:
+        raise ValueError(f"mode must be one of {list(_MODES)}")
+    _need_gpu(target, "target")
+    if target.dim() != 3:
+        raise ValueError("target must be [B, K+1, V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dt = _DTYPES.get(target.dtype)
+    if dt is None:
+        raise ValueError("logits must be bfloat16 or float32")
+    sampling = mode in _SAMPLING
+    if sampling and K > 0:
+        if draft is None:
+            raise ValueError("draft logits are required in sample mode")
+        _need_gpu(draft, "draft")
+        if draft.dtype != target.dtype or tuple(draft.shape) != (B, K, V):
+            raise ValueError("draft must match target dtype and be [B, K, V]")
+    if K > 0:
+        if draft_tokens is None:
+            raise ValueError("draft_tokens are required when K > 0")
+        _need_gpu(draft_tokens, "draft_tokens")
+        if draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != (B, K):
+            raise ValueError("draft_tokens must be int32 [B, K]")
+    if sampling:
+        if uniforms is None:
+            raise ValueError("uniforms are required in sample mode")
+        _need_gpu(uniforms, "uniforms")
+        if uniforms.dtype != torch.float32 or tuple(uniforms.shape) != (B, K + 1, 2):
+            raise ValueError("uniforms must be float32 [B, K+1, 2]")
+    return B, K, V, dt, sampling
+
+
+def spec_verify_noalloc(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: Optional[torch.Tensor],
+                        uniforms: Optional[torch.Tensor], temperature: float = 1.0, mode: str = "sample", *,
+                        out: Sequence[torch.Tensor], stream=None):
+    """spec_verify into caller-owned outputs with the library's static scratch
+    (spec_verify_noalloc of the C ABI): neither this call nor the library
+    allocates device memory.  out = (accepted_len int32 [B], out_tokens int32
+    [B, K+1]) or those plus (p_target, p_draft) float32 [B, K].  Calls that
+    overlap on one GPU race on the shared scratch."""
+    B, K, V, dt, sampling = _check_verify_inputs(target, draft, draft_tokens, uniforms, mode)
+    if len(out) not in (2, 4):
+        raise ValueError("out must hold 2 or 4 tensors")
+    want = [((B,), torch.int32), ((B, K + 1), torch.int32), ((B, K), torch.float32), ((B, K), torch.float32)]
+    for t, (shape, dtype) in zip(out, want):
+        _need_gpu(t, "out")
+        if tuple(t.shape) != shape or t.dtype != dtype:
+            raise ValueError(f"out tensor must be {dtype} {list(shape)}")
+    pt, pd = (out[2], out[3]) if len(out) == 4 else (None, None)
+    st = _native.load().spec_verify_noalloc(
+        _ptr(target), _ptr(draft) if sampling else None, _ptr(draft_tokens) if K > 0 else None,
+        _ptr(uniforms) if sampling else None, B, K, V, dt, ctypes.c_float(temperature if sampling else 0.0),
+        _MODES[mode], _ptr(out[0]), _ptr(out[1]), _ptr(pt), _ptr(pd), _stream_handle(target.device, stream))
+    _native.check(st, "spec_verify_noalloc")
+    return tuple(out)
 
 
 def spec_draft_head_shortlist(h: torch.Tensor, W: torch.Tensor, cluster_ids: torch.Tensor, cluster_size: int, *,

@@ -51,6 +51,8 @@ def load() -> ctypes.CDLL:
                        P, P, P, P, P, sz, P]
         lib.spec_verify.argtypes = verify_args
         lib.spec_verify.restype = ctypes.c_int
+        lib.spec_verify_noalloc.argtypes = verify_args[:-3] + [P]
+        lib.spec_verify_noalloc.restype = ctypes.c_int
         lib.spec_verify_timed.argtypes = verify_args + [P, i32]
         lib.spec_verify_timed.restype = ctypes.c_int
         lib.spec_verify_launch_count.argtypes = [i32, i32, i32, ctypes.c_int, ctypes.c_int]

@@ -4,12 +4,51 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/specverify.h"
 #include "sv_internal.h"
+
+// Scratch of spec_verify_noalloc: one copy per GPU, at a different device
+// address on each.  In host code this name is only a stand-in for the symbol:
+// the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[SPEC_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
 using sv::check_shape;
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, null until located
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch, located on first use with
+// that device current.  `stream` (if not null) must belong to that device.
+spec_status_t noalloc_scratch(void* stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SPEC_ERR_HIP;
+  if (dev >= kMaxDevices) return SPEC_ERR_UNSUPPORTED;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) return SPEC_ERR_HIP;
+    if (sdev != dev) return SPEC_ERR_INVALID_ARG;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return SPEC_ERR_HIP;
+      }
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SPEC_OK;
+}
 
 struct SparseDraft {
   const int32_t* cids;
@@ -116,6 +155,31 @@ spec_status_t spec_verify_timed(const void* target_logits, const void* draft_log
   return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, B, K, V, dtype, temperature, mode,
                      accepted_len, out_tokens, p_target_at_draft, p_draft_at_draft, workspace, workspace_bytes,
                      stream, events, n_events);
+}
+
+spec_status_t spec_verify_noalloc(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                                  const float* uniforms, int32_t B, int32_t K, int32_t V, spec_dtype_t dtype,
+                                  float temperature, spec_mode_t mode, int32_t* accepted_len, int32_t* out_tokens,
+                                  float* p_target_at_draft, float* p_draft_at_draft, void* stream) {
+  // Every argument check of spec_verify first, with the scratch size as the
+  // workspace size and a stand-in address: nothing is located or enqueued
+  // for a call that fails them.
+  sv::VerifyShape s{};
+  size_t need = 0;
+  bool empty = false;
+  void* const stand_in = reinterpret_cast<void*>((uintptr_t)256);
+  const spec_status_t sc =
+      sv::validate_verify(target_logits, draft_logits, draft_tokens, uniforms, B, K, V, dtype, temperature, mode,
+                          accepted_len, out_tokens, stand_in, SPEC_NOALLOC_SCRATCH_BYTES, false, &s, &need, &empty);
+  if (sc != SPEC_OK) return sc;
+  void* ws = nullptr;
+  if (!empty) {
+    const spec_status_t ss = noalloc_scratch(stream, &ws);
+    if (ss != SPEC_OK) return ss;
+  }
+  return verify_impl(target_logits, draft_logits, draft_tokens, uniforms, B, K, V, dtype, temperature, mode,
+                     accepted_len, out_tokens, p_target_at_draft, p_draft_at_draft, empty ? stand_in : ws,
+                     SPEC_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0);
 }
 
 spec_status_t spec_verify_sparse_draft(const void* target_logits, const void* draft_compact,

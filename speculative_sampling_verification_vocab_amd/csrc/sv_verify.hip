@@ -340,15 +340,15 @@ __device__ __forceinline__ bool accept_test(const VerifyArgs& a, int d, double x
 
 // Decision of position j for sequence b, taken by one wave (wave 0 of every
 // block that needs it, which shares the result through LDS; every block gets
-// the same result).  Returns 1 if the sequence
-// accepted position j and has positions left, else 0 with *sr filled for the
-// sampling pass (sr->n = j at a rejection, K when every position was
-// accepted, -1 for a fault).  The writer wave also stores the outputs that
+// the same result).  Returns the record for the sampling pass with n = -2 if
+// the sequence accepted position j and has positions left, else n = j at a
+// rejection, K when every position was accepted, -1 for a fault.  (Returned
+// by value and inlined, so the record stays in registers.)  The writer wave also stores the outputs that
 // position j determines: P_t(d_j), P_d(d_j), cont[j][b], and at the
 // sequence's end accepted_len, out_tokens (position n is left for
 // pick_kernel) and rows[b].  The caller has checked that the sequence reached
 // position j.
-__device__ int ee_decide(const VerifyArgs& a, int b, int j, bool writer, SampleRowInfo* sr) {
+__device__ __forceinline__ SampleRowInfo ee_decide(const VerifyArgs& a, int b, int j, bool writer) {
   const int lane = threadIdx.x & (kWave - 1);
   const int K = a.K, R = 2 * K;
   const int32_t* tok = a.tokens + (size_t)b * K;
@@ -365,9 +365,13 @@ __device__ int ee_decide(const VerifyArgs& a, int b, int j, bool writer, SampleR
   float mt, md;
   double zt, zd;
   if (a.NT <= kWave) {
-    const TileStat none{kNegInf, 0.0f};
-    const TileStat qt = lane < a.NT ? pb[(size_t)j * a.NT + lane] : none;
-    const TileStat qd = lane < a.NT ? pb[(size_t)(K + j) * a.NT + lane] : none;
+    // loaded into values (a select between the partial and a local default by
+    // address would put the default in scratch memory)
+    TileStat qt{kNegInf, 0.0f}, qd{kNegInf, 0.0f};
+    if (lane < a.NT) {
+      qt = pb[(size_t)j * a.NT + lane];
+      qd = pb[(size_t)(K + j) * a.NT + lane];
+    }
     combine_row(qt, a, mt, zt);
     combine_row(qd, a, md, zd);
   } else {
@@ -379,9 +383,10 @@ __device__ int ee_decide(const VerifyArgs& a, int b, int j, bool writer, SampleR
   const bool acc = accept_test(a, d, xt, xd, mt, md, zt, zd, u, pt, pd, bad);
   bad = bad || bad_tok;
   const int n = bad ? -1 : (!acc ? j : (j == K - 1 ? K : -2));  // -2: goes on to position j + 1
-  if (n == -1) *sr = SampleRowInfo{0.0f, 0.0f, 1.0, 1.0, -1};
-  else if (n == K) *sr = SampleRowInfo{0.0f, 0.0f, 1.0, 1.0, K};
-  else *sr = SampleRowInfo{mt, md, zt, zd, n};
+  SampleRowInfo sr;
+  if (n == -1) sr = SampleRowInfo{0.0f, 0.0f, 1.0, 1.0, -1};
+  else if (n == K) sr = SampleRowInfo{0.0f, 0.0f, 1.0, 1.0, K};
+  else sr = SampleRowInfo{mt, md, zt, zd, n};
   if (writer) {
     if (lane == 0) {
       if (a.p_t_out) a.p_t_out[(size_t)b * K + j] = bad ? __builtin_nanf("") : (float)pt;
@@ -399,14 +404,16 @@ __device__ int ee_decide(const VerifyArgs& a, int b, int j, bool writer, SampleR
         a.out_tokens[(size_t)b * (K + 1) + q] = (n >= 0 && q < n) ? tok[q] : -1;
       if (lane == 0) {
         a.accepted_len[b] = n;
-        a.rows[b] = *sr;
+        a.rows[b] = sr;
       }
     }
   }
-  return n == -2 ? 1 : 0;
+  return sr;
 }
 
-__device__ int accept_sequence(const VerifyArgs& a, int b, bool write, SampleRowInfo* info) {
+// Returns the record for the sampling pass (n = -1 for a faulty sequence; by
+// value and inlined, so it stays in registers).
+__device__ __forceinline__ SampleRowInfo accept_sequence(const VerifyArgs& a, int b, bool write) {
   __shared__ float sh_m[2 * kMaxK];
   __shared__ double sh_z[2 * kMaxK];
   __shared__ int sh_acc[kMaxK];
@@ -414,10 +421,7 @@ __device__ int accept_sequence(const VerifyArgs& a, int b, bool write, SampleRow
   __shared__ int sh_n;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int K = a.K, R = 2 * K;
-  if (K == 0) {
-    *info = SampleRowInfo{0.0f, 0.0f, 1.0, 1.0};
-    return 0;
-  }
+  if (K == 0) return SampleRowInfo{0.0f, 0.0f, 1.0, 1.0, 0};
   if (threadIdx.x == 0) sh_bad = 0;
   // Loads that do not depend on each other go first: the drafted tokens,
   // their logits (recorded by the statistics pass) and the accept uniforms.
@@ -491,8 +495,8 @@ __device__ int accept_sequence(const VerifyArgs& a, int b, bool write, SampleRow
   }
   __syncthreads();
   const int n = sh_n;
-  if (n >= 0 && n < K) *info = SampleRowInfo{sh_m[n], sh_m[K + n], sh_z[n], sh_z[K + n]};
-  else *info = SampleRowInfo{0.0f, 0.0f, 1.0, 1.0};
+  const SampleRowInfo info = n >= 0 && n < K ? SampleRowInfo{sh_m[n], sh_m[K + n], sh_z[n], sh_z[K + n], n}
+                                             : SampleRowInfo{0.0f, 0.0f, 1.0, 1.0, n};
   if (write) {
     const int i = threadIdx.x;
     if (i < K) {
@@ -504,10 +508,10 @@ __device__ int accept_sequence(const VerifyArgs& a, int b, bool write, SampleRow
     if (i <= K) a.out_tokens[(size_t)b * (K + 1) + i] = (n >= 0 && i < n) ? d : -1;
     if (i == 0) {
       a.accepted_len[b] = n;
-      a.rows[b] = SampleRowInfo{info->m_t, info->m_d, info->za_t, info->za_d, n};
+      a.rows[b] = info;
     }
   }
-  return n;
+  return info;
 }
 
 // Per-tile ratio that decides the residual's positive set: element v of a tile
@@ -622,7 +626,7 @@ __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
     } else if (K == 1 || a.cont[(size_t)(K - 2) * a.B + b] != 0) {
       __shared__ SampleRowInfo sh_sr;
       if (wave == 0) {
-        ee_decide(a, b, K - 1, g == 0, &sr);
+        sr = ee_decide(a, b, K - 1, g == 0);
         if (lane == 0) sh_sr = sr;
       }
       __syncthreads();
@@ -633,7 +637,8 @@ __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
       n = sr.n;
     }
   } else {
-    n = accept_sequence(a, b, g == 0, &sr);
+    sr = accept_sequence(a, b, g == 0);
+    n = sr.n;
   }
   if (n < 0) return;  // faulty sequence: outputs already written
   const bool resid = n < K;
@@ -962,8 +967,7 @@ __global__ void __launch_bounds__(kBlock) stats_kernel(VerifyArgs a) {
 // once per sequence; small ones in the prologue of every sampling block,
 // which saves this launch.
 __global__ void __launch_bounds__(kBlock) decide_kernel(VerifyArgs a) {
-  SampleRowInfo sr;
-  accept_sequence(a, blockIdx.x, true, &sr);
+  (void)accept_sequence(a, blockIdx.x, true);
 }
 
 template <typename T, bool kAligned, bool kSparse = false, bool kDecided = false>
@@ -1017,8 +1021,7 @@ __global__ void __launch_bounds__(kBlock) ee_phase_kernel(VerifyArgs a, int i) {
     // wave deciding for itself measured 4 % slower over the phases.)
     __shared__ int sh_go;
     if (wave == 0) {
-      SampleRowInfo sr;
-      const int go = ee_decide(a, b, i - 1, writer, &sr);
+      const int go = ee_decide(a, b, i - 1, writer).n == -2 ? 1 : 0;
       if ((threadIdx.x & (kWave - 1)) == 0) sh_go = go;
     }
     __syncthreads();

@@ -535,8 +535,13 @@ def bench_static_head(hc, steps, warmup, dev):
     (FR-Spec / VocabTrim): the same h and W, a fixed set of 32768 token ids at
     cluster size 1 (FR-Spec's shortlist size) and of 16 clusters of 501
     (N = 8016).  Times spec_draft_head_static (W rows gathered inside the
-    kernel) with fp32 and bf16 logits, and, for context, torch's bf16 GEMM
-    (F.linear, i.e. hipBLASLt) on a pre-gathered contiguous W_S."""
+    kernel) with fp32 and bf16 logits.  Each timed call takes the next of 8
+    different shortlists of that size, so W_S is read from HBM rather than
+    left in the 256 MB last-level cache by the previous call (the figure
+    with one shortlist repeated is reported as `us_fp32_out_warm`).  Narrow
+    shortlists split d over blocks through a workspace; the single-launch
+    form is reported beside it.  For context, torch's bf16 GEMM (F.linear,
+    i.e. hipBLASLt) on a pre-gathered contiguous W_S, warm."""
     import numpy as np
     import torch
     import torch.nn.functional as F
@@ -547,40 +552,48 @@ def bench_static_head(hc, steps, warmup, dev):
     V = hc.W.shape[0]
     M = B * K
     h2 = hc.h.reshape(M, d)
+    ws = sv.Workspace(dev)
 
     def med(fn, n):
-        for _ in range(warmup):
-            fn()
+        for i in range(warmup):
+            fn(i)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        for e0, e1 in ev:
+        for i, (e0, e1) in enumerate(ev):
             e0.record()
-            fn()
+            fn(i)
             e1.record()
         torch.cuda.synchronize()
         return float(np.median([a.elapsed_time(b) for a, b in ev]))
 
     shapes = []
     for name, cs, n_sel, seed in (("frspec_32768_tokens", 1, 32768, 11), ("clusters_16x501", 501, 16, 12)):
-        g = torch.Generator().manual_seed(seed)
-        ids = torch.sort(torch.randperm(V // cs, generator=g)[:n_sel]).values.to(torch.int32).to(dev)
+        sets = []
+        for r in range(8):
+            g = torch.Generator().manual_seed(seed + 1000 * r)
+            sets.append(torch.sort(torch.randperm(V // cs, generator=g)[:n_sel]).values.to(torch.int32).to(dev))
         N = n_sel * cs
         o32 = torch.empty((M, N), dtype=torch.float32, device=dev)
         o16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        n = max(steps, 20)
-        ms32 = med(lambda: sv.spec_draft_head_static(h2, hc.W, ids, cs, out=o32), n)
-        ms16 = med(lambda: sv.spec_draft_head_static(h2, hc.W, ids, cs, dtype=torch.bfloat16, out=o16), n)
-        rows = (ids.long()[:, None] * cs + torch.arange(cs, device=dev)[None, :]).reshape(-1)
+        n = max(steps, 24)
+        ms32 = med(lambda i: sv.spec_draft_head_static(h2, hc.W, sets[i % 8], cs, out=o32, workspace=ws), n)
+        ms16 = med(lambda i: sv.spec_draft_head_static(h2, hc.W, sets[i % 8], cs, dtype=torch.bfloat16, out=o16,
+                                                       workspace=ws), n)
+        ms32_one = med(lambda i: sv.spec_draft_head_static(h2, hc.W, sets[i % 8], cs, out=o32, split=False), n)
+        ms32_warm = med(lambda i: sv.spec_draft_head_static(h2, hc.W, sets[0], cs, out=o32, workspace=ws), n)
+        rows = (sets[0].long()[:, None] * cs + torch.arange(cs, device=dev)[None, :]).reshape(-1)
         Ws = hc.W[rows].contiguous()
-        ms_blas = med(lambda: F.linear(h2, Ws), n)
+        ms_blas = med(lambda i: F.linear(h2, Ws), n)
         del Ws
         flops = 2.0 * M * N * d
         b32 = N * d * 2 + M * d * 2 + M * N * 4
         b16 = N * d * 2 + M * d * 2 + M * N * 2
         ach = b32 / (ms32 * 1e-3) / 1e9
+        split = sv._native.load().spec_draft_head_static_workspace_bytes(M, d, V, cs, n_sel) > 0
         shapes.append({
-            "shortlist": name, "M": M, "N": N, "d": d, "cluster_size": cs,
-            "us_fp32_out": ms32 * 1e3, "us_bf16_out": ms16 * 1e3,
-            "roofline": {"bound": "hbm", "kernel": "head_static_kernel", "achieved": ach, "peak": HBM_PEAK_GBS,
+            "shortlist": name, "M": M, "N": N, "d": d, "cluster_size": cs, "k_split": split,
+            "us_fp32_out": ms32 * 1e3, "us_bf16_out": ms16 * 1e3, "us_fp32_out_single_launch": ms32_one * 1e3,
+            "us_fp32_out_warm": ms32_warm * 1e3,
+            "roofline": {"bound": "hbm", "kernel": "head_static_dma_kernel", "achieved": ach, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                          "traffic": traffic_from_profile(STATIC_PROFILE_PMC, STATIC_SOURCES)
                          if name.startswith("frspec") else None,
@@ -591,7 +604,7 @@ def bench_static_head(hc, steps, warmup, dev):
                      "busy_frac_pmc": profile_value(MFMA_PROFILE_PMC, "mfma_busy_frac head_static_kernel "
                                                     + ("n32768_fp32" if name.startswith("frspec") else "n8016"),
                                                     MFMA_SOURCES)},
-            "blas_reference": {"op": "torch F.linear bf16 on a pre-gathered contiguous W_S (hipBLASLt)",
+            "blas_reference": {"op": "torch F.linear bf16 on a pre-gathered contiguous W_S (hipBLASLt), warm",
                                "us": ms_blas * 1e3},
         })
     return shapes

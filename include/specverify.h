@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 1
+#define SPEC_ABI_VERSION 2
 #define SPEC_MAX_K 64
 
 /*
@@ -302,16 +302,33 @@ spec_status_t spec_draft_head_positions(const void* h, const void* W, const int3
  *                order (the output columns follow it); an id outside that
  *                range contributes zero columns (not checked on the host).
  *   logits       [M, N] of out_dtype out (bf16 rounds to nearest even).
+ *   workspace    NULL, or a 256-byte aligned device buffer of at least
+ *                spec_draft_head_static_workspace_bytes() bytes.  For narrow
+ *                shortlists (fewer than 192 output tiles of 128 x 128: N up
+ *                to about 24k at M = 128) it lets the kernel split the d
+ *                dimension over several blocks per output tile: the slices'
+ *                fp32 partial tiles go to the workspace and a second launch
+ *                adds them in a fixed order (results are deterministic, and
+ *                differ from the unsplit sum only by fp32 rounding order).
+ *                With NULL the head runs in one launch without splitting.
+ *                The contents need no initialisation.
  * Any alignment of whole elements works; 16-byte aligned h and W with d % 8 == 0
- * take the vector-load path.
+ * take the vector-load path (the split needs d % 64 == 0 as well).
  * Errors: SPEC_ERR_INVALID_ARG for NULL or misaligned buffers or bad sizes;
- * SPEC_ERR_UNSUPPORTED if V % cluster_size != 0 or the output needs more than
- * 2^31 - 1 output tiles (one block each; tiles are 128 x 128, 128 x 32 or
- * 64 x 32 depending on the shape and alignment).
+ * SPEC_ERR_WORKSPACE for a workspace that is too small or not 256-byte
+ * aligned; SPEC_ERR_UNSUPPORTED if V % cluster_size != 0 or the output needs
+ * more than 2^31 - 1 output tiles (one block each; tiles are 128 x 128,
+ * 128 x 32 or 64 x 32 depending on the shape and alignment).
  */
 spec_status_t spec_draft_head_static(const void* h, const void* W, const int32_t* cluster_ids, int32_t M,
                                      int32_t d, int32_t V, int32_t cluster_size, int32_t n_sel, void* logits,
-                                     spec_dtype_t out_dtype, void* stream);
+                                     spec_dtype_t out_dtype, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/* Workspace bytes that let spec_draft_head_static split d over several blocks
+ * per output tile for this shape (0: the shape does not split). */
+size_t spec_draft_head_static_workspace_bytes(int32_t M, int32_t d, int32_t V, int32_t cluster_size,
+                                             int32_t n_sel);
 
 /*
  * KV-cache commit after a verify step (Speculative Decoding lesson,

@@ -362,11 +362,13 @@ def spec_draft_head_positions(h: torch.Tensor, W: torch.Tensor, cluster_ids: tor
 
 def spec_draft_head_static(h: torch.Tensor, W: torch.Tensor, cluster_ids: torch.Tensor, cluster_size: int,
                            dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
-                           stream=None) -> torch.Tensor:
+                           stream=None, workspace: Optional[Workspace] = None, split: bool = True) -> torch.Tensor:
     """Drafter head over one shortlist shared by every context (see
     spec_draft_head_static in specverify.h).  h bf16 [..., d] (all leading
     dims are rows), W bf16 [V, d], cluster_ids int32 [n_sel].  Returns logits
-    [..., n_sel * cluster_size] of dtype."""
+    [..., n_sel * cluster_size] of dtype.  With split (default) narrow
+    shortlists split d over blocks through a workspace (the stream's default
+    one unless given); split=False runs the single-launch kernel."""
     for t, name in ((h, "h"), (W, "W"), (cluster_ids, "cluster_ids")):
         _need_gpu(t, name)
     if h.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
@@ -385,9 +387,16 @@ def spec_draft_head_static(h: torch.Tensor, W: torch.Tensor, cluster_ids: torch.
         out = torch.empty(shape, dtype=dtype, device=h.device)
     elif out.dtype != dtype or tuple(out.shape) != shape or not out.is_contiguous():
         raise ValueError("out must be contiguous with shape h.shape[:-1] + (N,) and dtype")
-    st = _native.load().spec_draft_head_static(_ptr(h.contiguous()), _ptr(W.contiguous()),
-                                               _ptr(cluster_ids.contiguous()), M, d, V, int(cluster_size),
-                                               cluster_ids.numel(), _ptr(out), dt,
-                                               _stream_handle(h.device, stream))
+    lib = _native.load()
+    ws, wsb = None, 0
+    need = lib.spec_draft_head_static_workspace_bytes(M, d, V, int(cluster_size), cluster_ids.numel()) \
+        if split and M > 0 and cluster_ids.numel() > 0 else 0
+    if need:
+        buf = (workspace or _workspace_for(h.device, stream)).get(need, stream)
+        ws, wsb = _ptr(buf), buf.numel()
+    st = lib.spec_draft_head_static(_ptr(h.contiguous()), _ptr(W.contiguous()),
+                                    _ptr(cluster_ids.contiguous()), M, d, V, int(cluster_size),
+                                    cluster_ids.numel(), _ptr(out), dt, ws, wsb,
+                                    _stream_handle(h.device, stream))
     _native.check(st, "spec_draft_head_static")
     return out

@@ -65,7 +65,9 @@ def load() -> ctypes.CDLL:
         lib.spec_verify_sparse_draft.restype = ctypes.c_int
         lib.spec_draft_head_positions.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, i32, P, ctypes.c_int, P]
         lib.spec_draft_head_positions.restype = ctypes.c_int
-        lib.spec_draft_head_static.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, ctypes.c_int, P]
+        lib.spec_draft_head_static.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, ctypes.c_int, P, sz, P]
+        lib.spec_draft_head_static_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        lib.spec_draft_head_static_workspace_bytes.restype = sz
         lib.spec_draft_head_static.restype = ctypes.c_int
         lib.spec_position_budget.argtypes = [i32, i32]
         lib.spec_position_budget.restype = i32

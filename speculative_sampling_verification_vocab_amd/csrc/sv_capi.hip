@@ -238,16 +238,26 @@ spec_status_t spec_draft_head_positions(const void* h, const void* W, const int3
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
+size_t spec_draft_head_static_workspace_bytes(int32_t M, int32_t d, int32_t V, int32_t cluster_size,
+                                             int32_t n_sel) {
+  if (M < 1 || d < 1 || V < 1 || cluster_size < 1 || n_sel < 1 || V % cluster_size != 0) return 0;
+  const long long N = (long long)n_sel * cluster_size;
+  if (N > 0x7fffffffLL) return 0;
+  return sv::head_static_workspace_bytes(M, d, (int32_t)N);
+}
+
 spec_status_t spec_draft_head_static(const void* h, const void* W, const int32_t* cluster_ids, int32_t M,
                                      int32_t d, int32_t V, int32_t cluster_size, int32_t n_sel, void* logits,
-                                     spec_dtype_t out_dtype, void* stream) {
+                                     spec_dtype_t out_dtype, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
   bool empty = false;
-  const spec_status_t sc =
-      sv::validate_head_static(h, W, cluster_ids, M, d, V, cluster_size, n_sel, logits, out_dtype, &empty);
+  const spec_status_t sc = sv::validate_head_static(h, W, cluster_ids, M, d, V, cluster_size, n_sel, logits,
+                                                    out_dtype, workspace, workspace_bytes, &empty);
   if (sc != SPEC_OK || empty) return sc;
   (void)hipGetLastError();
-  const hipError_t e = sv::launch_head_static(h, W, cluster_ids, M, d, V, cluster_size, n_sel, logits,
-                                              out_dtype == SPEC_BF16 ? 1 : 0, static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      sv::launch_head_static(h, W, cluster_ids, M, d, V, cluster_size, n_sel, logits, out_dtype == SPEC_BF16 ? 1 : 0,
+                             static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 

@@ -287,10 +287,39 @@ inline spec_status_t validate_head_positions(const void* h, const void* W, const
   return SPEC_OK;
 }
 
+// Launch plan of spec_draft_head_static.  Rows of d % 64 == 0 dims with
+// 16-byte alignment take the LDS-DMA kernel: 128 x 128 output tiles when the
+// shortlist gives at least kStaticWideTiles of them (M = 128: N >= 24577),
+// else, with a workspace, 128 x 128 tiles whose K stages are split over
+// ksplit blocks (fp32 partial tiles in the workspace, added in a fixed order
+// by a second launch), or, without one, 64 x 32 tiles over the whole K.
+// Other shapes take the register-staged kernel (no split).
+constexpr long long kStaticWideTiles = 192;
+constexpr int kStaticMaxSplit = 8;
+
+inline int head_static_split(int32_t M, int32_t d, int32_t N) {
+  if (M < 1 || N < 1 || d % 64 != 0) return 1;
+  const long long t128 = (long long)((M + 127) / 128) * ((N + 127) / 128);
+  if (t128 >= kStaticWideTiles) return 1;
+  // about one block per CU (256): 63 tiles at M = 128, N = 8016 take 4 slices
+  long long s = (256 + t128 / 2) / t128;
+  const long long stages = d / 64;
+  if (s > kStaticMaxSplit) s = kStaticMaxSplit;
+  if (s > stages / 4) s = stages / 4;  // at least four stages per slice
+  return s < 1 ? 1 : (int)s;
+}
+
+// Workspace bytes that let spec_draft_head_static split K (0: no split).
+inline size_t head_static_workspace_bytes(int32_t M, int32_t d, int32_t N) {
+  const int s = head_static_split(M, d, N);
+  return s > 1 ? align256((size_t)s * (size_t)M * (size_t)N * sizeof(float)) : 0;
+}
+
 // spec_draft_head_static.
 inline spec_status_t validate_head_static(const void* h, const void* W, const int32_t* cluster_ids, int32_t M,
                                           int32_t d, int32_t V, int32_t cluster_size, int32_t n_sel,
-                                          const void* logits, spec_dtype_t out_dtype, bool* empty) {
+                                          const void* logits, spec_dtype_t out_dtype, const void* workspace,
+                                          size_t workspace_bytes, bool* empty) {
   if (M < 0 || d < 1 || V < 1 || cluster_size < 1 || n_sel < 0) return SPEC_ERR_INVALID_ARG;
   if (!valid_dtype(out_dtype)) return SPEC_ERR_INVALID_ARG;
   if (V % cluster_size != 0) return SPEC_ERR_UNSUPPORTED;
@@ -304,6 +333,9 @@ inline spec_status_t validate_head_static(const void* h, const void* W, const in
   const size_t N = (size_t)n_sel * (size_t)cluster_size;
   if ((size_t)M * N > SIZE_MAX / 8 || (size_t)M * (size_t)d > SIZE_MAX / 8) return SPEC_ERR_INVALID_ARG;
   if (((N + 31) / 32) * (((size_t)M + 127) / 128) > 0x7fffffffu) return SPEC_ERR_UNSUPPORTED;  // 1-D grid of tiles
+  if (workspace && ((uintptr_t)workspace % 256 != 0 ||
+                    workspace_bytes < head_static_workspace_bytes(M, d, (int32_t)N)))
+    return SPEC_ERR_WORKSPACE;
   return SPEC_OK;
 }
 

@@ -34,8 +34,10 @@ hipError_t launch_head(const void* h, const void* W, const int32_t* cluster_ids,
                        int L = 0, int compact_dtype = 0);
 
 // Head over one shortlist shared by every row: C[M, n_sel*cs] = h[M, d] * W_S^T.
+// partial (null: no K split) holds head_static_workspace_bytes(M, d, N).
 hipError_t launch_head_static(const void* h, const void* W, const int32_t* cluster_ids, int M, int d, int V,
-                              int cluster_size, int n_sel, void* out, int out_dtype, hipStream_t st);
+                              int cluster_size, int n_sel, void* out, int out_dtype, float* partial,
+                              hipStream_t st);
 
 // KV-cache commit: copy, then lengths and status (two launches).
 hipError_t launch_kv_commit(void* cache, const void* staging, const int32_t* accepted_len, int32_t* cache_len,

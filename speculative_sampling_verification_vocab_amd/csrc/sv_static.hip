@@ -50,6 +50,9 @@ struct StaticArgs {
   void* out;             // [M, N] fp32 or bf16
   int out_bf16;
   int pair16;            // bf16 out, N even, out 4-byte aligned: dword stores of column pairs
+  int ksplit;            // LDS-DMA kernel: blocks per output tile, each over a slice of the K stages
+  int split_stages;      // stages per slice
+  float* partial;        // ksplit > 1: fp32 partial tiles [ksplit][M][N], added by head_static_reduce_kernel
 };
 
 __device__ __forceinline__ uint16_t to_bf16_rne(float f) {
@@ -344,7 +347,8 @@ __device__ __forceinline__ void dma16(const uint16_t* g, uint8_t* lds) {
 // Every thread of the block must call this.
 template <int kMt, int kNt, int TM, int TN>
 __device__ __forceinline__ void store_block_tile(const StaticArgs& a, const f32x4 (&acc)[TM][TN], float* stage,
-                                                 int m0, int n0, bool own, int mw, int nw, int lane) {
+                                                 int m0, int n0, bool own, int mw, int nw, int lane, void* dst,
+                                                 bool dst_bf16) {
   constexpr int kLd = kNt + 4;  // row stride in floats: the four row groups of a write land on distinct banks
   if (own) {
 #pragma unroll
@@ -360,9 +364,9 @@ __device__ __forceinline__ void store_block_tile(const StaticArgs& a, const f32x
   constexpr int kTpr = kNt / 4;
   const int nthreads = blockDim.x;
   const int c4 = (threadIdx.x % kTpr) * 4;
-  const int esz = a.out_bf16 ? 2 : 4;
-  const bool vec = (size_t)a.N * esz % (a.out_bf16 ? 8 : 16) == 0 &&
-                   (uintptr_t)a.out % (a.out_bf16 ? 8 : 16) == 0 && n0 + kNt <= a.N;
+  const int esz = dst_bf16 ? 2 : 4;
+  const bool vec = (size_t)a.N * esz % (dst_bf16 ? 8 : 16) == 0 &&
+                   (uintptr_t)dst % (dst_bf16 ? 8 : 16) == 0 && n0 + kNt <= a.N;
   uint32_t keep = 0;  // bit e: column n0 + c4 + e is stored with its value (not zero)
 #pragma unroll
   for (int e = 0; e < 4; ++e)
@@ -376,19 +380,19 @@ __device__ __forceinline__ void store_block_tile(const StaticArgs& a, const f32x
     for (int e = 0; e < 4; ++e) v[e] = (keep >> e & 1u) ? src[e] : 0.0f;
     const size_t o = (size_t)m * a.N + n0 + c4;
     if (vec) {
-      if (a.out_bf16) {
+      if (dst_bf16) {
         const uint32_t lo = (uint32_t)to_bf16_rne(v[0]) | ((uint32_t)to_bf16_rne(v[1]) << 16);
         const uint32_t hi = (uint32_t)to_bf16_rne(v[2]) | ((uint32_t)to_bf16_rne(v[3]) << 16);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = uint2{lo, hi};
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(dst) + o) = uint2{lo, hi};
       } else {
-        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o) = float4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<float4*>(static_cast<float*>(dst) + o) = float4{v[0], v[1], v[2], v[3]};
       }
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (n0 + c4 + e >= a.N) break;
-        if (a.out_bf16) static_cast<uint16_t*>(a.out)[o + e] = to_bf16_rne(v[e]);
-        else static_cast<float*>(a.out)[o + e] = v[e];
+        if (dst_bf16) static_cast<uint16_t*>(dst)[o + e] = to_bf16_rne(v[e]);
+        else static_cast<float*>(dst)[o + e] = v[e];
       }
     }
   }
@@ -414,6 +418,11 @@ __global__ void __launch_bounds__(kWave * WM * WN * WK) head_static_dma_kernel(S
   const int wm = wmn / WN, wn = wmn % WN;
   int v = blockIdx.x;
   if (a.remap) v = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  // Slice-major order: the blocks of one K slice are consecutive, so an XCD's
+  // share of the grid reuses the same slice of h from its L2.
+  const int tiles = (int)(gridDim.x / (unsigned)a.ksplit);
+  const int split = v / tiles;
+  v -= split * tiles;
   const int n0 = (v / a.m_tiles) * kNt, m0 = (v % a.m_tiles) * kMt;
 
   // DMA instruction j of this wave covers tile rows 8 * (j * NW + wave) ..;
@@ -436,12 +445,14 @@ __global__ void __launch_bounds__(kWave * WM * WN * WK) head_static_dma_kernel(S
     }
     src[j] = row + 8 * c;
   }
-  const int nst = a.d / kStage;
+  // This block's stages: s0 .. s0 + nst - 1 of the a.d / kStage in the row.
+  const int s0 = split * a.split_stages;
+  const int nst = min(a.d / kStage - s0, a.split_stages);
   auto issue = [&](int s) {
     uint8_t* dst = &sh[s % NBUF][0];
 #pragma unroll
     for (int j = 0; j < kIW; ++j)
-      dma16(src[j] + s * kStage, dst + 1024 * (j * NW + wave));
+      dma16(src[j] + (s0 + s) * kStage, dst + 1024 * (j * NW + wave));
   };
 
   f32x4 acc[TM][TN];
@@ -488,18 +499,74 @@ __global__ void __launch_bounds__(kWave * WM * WN * WK) head_static_dma_kernel(S
   __syncthreads();  // all fragment reads done before LDS is reused
   float* stage = reinterpret_cast<float*>(&sh[0][0]);
   if (WK > 1) add_split_k<WM * WN, WK, TM, TN>(acc, stage, wk, wmn, lane);
-  store_block_tile<kMt, kNt, TM, TN>(a, acc, stage, m0, n0, wk == 0, wm * 16 * TM, wn * 16 * TN, lane);
+  if (a.ksplit == 1)
+    store_block_tile<kMt, kNt, TM, TN>(a, acc, stage, m0, n0, wk == 0, wm * 16 * TM, wn * 16 * TN, lane, a.out,
+                                       a.out_bf16 != 0);
+  else
+    store_block_tile<kMt, kNt, TM, TN>(a, acc, stage, m0, n0, wk == 0, wm * 16 * TM, wn * 16 * TN, lane,
+                                       a.partial + (size_t)split * a.M * a.N, false);
 }
 
+// out[m, n] = sum over slices s = 0 .. ksplit - 1 of partial[s][m][n], added
+// in that order (deterministic), then stored as fp32 or bf16.  Four
+// consecutive outputs per thread; 16-byte partial loads when N % 4 == 0.
+__global__ void __launch_bounds__(kBlock) head_static_reduce_kernel(StaticArgs a) {
+  const size_t MN = (size_t)a.M * a.N;
+  const size_t q = ((size_t)blockIdx.x * kBlock + threadIdx.x) * 4;
+  if (q >= MN) return;
+  const bool vec_in = a.N % 4 == 0;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.ksplit; ++s) {
+    const float* p = a.partial + (size_t)s * MN + q;
+    if (vec_in) {
+      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += __uint_as_float(x[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (q + e < MN) v[e] += p[e];
+    }
+  }
+  const bool vec_out = vec_in && (uintptr_t)a.out % (a.out_bf16 ? 8 : 16) == 0;
+  if (vec_out) {
+    if (a.out_bf16) {
+      const uint32_t lo = (uint32_t)to_bf16_rne(v[0]) | ((uint32_t)to_bf16_rne(v[1]) << 16);
+      const uint32_t hi = (uint32_t)to_bf16_rne(v[2]) | ((uint32_t)to_bf16_rne(v[3]) << 16);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + q) = uint2{lo, hi};
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + q) = float4{v[0], v[1], v[2], v[3]};
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (q + e >= MN) break;
+      if (a.out_bf16) static_cast<uint16_t*>(a.out)[q + e] = to_bf16_rne(v[e]);
+      else static_cast<float*>(a.out)[q + e] = v[e];
+    }
+  }
+}
+
+// ksplit > 1 needs a.partial with room for ksplit * M * N floats.
 template <int WM, int WN, int WK, int TM, int TN, int NBUF>
-hipError_t launch_dma(StaticArgs a, hipStream_t st) {
+hipError_t launch_dma(StaticArgs a, int ksplit, hipStream_t st) {
   constexpr int kMt = 16 * WM * TM, kNt = 16 * WN * TN;
   a.m_tiles = (a.M + kMt - 1) / kMt;
-  const long long total = (long long)((a.N + kNt - 1) / kNt) * a.m_tiles;
+  const long long tiles = (long long)((a.N + kNt - 1) / kNt) * a.m_tiles;
+  const int nst = a.d / 64;
+  if (ksplit < 1 || ksplit > nst || (ksplit > 1 && !a.partial)) return hipErrorInvalidValue;
+  a.split_stages = (nst + ksplit - 1) / ksplit;
+  a.ksplit = (nst + a.split_stages - 1) / a.split_stages;  // no empty slice
+  const long long total = tiles * a.ksplit;
   if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-  a.remap = a.m_tiles > 1 && total % 8 == 0;
+  a.remap = (a.m_tiles > 1 || a.ksplit > 1) && total % 8 == 0;
   hipLaunchKernelGGL((head_static_dma_kernel<WM, WN, WK, TM, TN, NBUF>), dim3((unsigned)total),
                      dim3(kWave * WM * WN * WK), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.ksplit == 1) return e;
+  const size_t quads = ((size_t)a.M * a.N + 3) / 4;
+  hipLaunchKernelGGL(head_static_reduce_kernel, dim3((unsigned)((quads + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
+                     a);
   return hipGetLastError();
 }
 
@@ -519,7 +586,8 @@ hipError_t launch_cfg(StaticArgs a, bool vec, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_head_static(const void* h, const void* W, const int32_t* cluster_ids, int M, int d, int V,
-                              int cluster_size, int n_sel, void* out, int out_dtype, hipStream_t st) {
+                              int cluster_size, int n_sel, void* out, int out_dtype, float* partial,
+                              hipStream_t st) {
   StaticArgs a{};
   a.h = static_cast<const uint16_t*>(h);
   a.W = static_cast<const uint16_t*>(W);
@@ -534,14 +602,25 @@ hipError_t launch_head_static(const void* h, const void* W, const int32_t* clust
   a.pair16 = a.out_bf16 && a.N % 2 == 0 && (uintptr_t)out % 4 == 0;
   const bool vec = (d % 8 == 0) && ((uintptr_t)h % 16 == 0) && ((uintptr_t)W % 16 == 0);
   // Widest column tile whose grid still gives most CUs a block: 128 x 128
-  // tiles on 8 waves (2 x 4, each 64 x 32) for wide shortlists; otherwise
-  // narrow tiles whose waves split each stage's MFMA k-steps in two.  The
-  // LDS-DMA kernel takes d % 64 == 0 with 16-byte aligned rows (64 x 32
-  // narrow tiles, 4 waves); the register-staged kernel everything else
-  // (128 x 32 narrow tiles, 4 waves; LDS rows of 64 + 16 bf16).
+  // tiles on 8 waves (2 x 4, each 64 x 32) for wide shortlists.  Narrow
+  // shortlists: with a workspace, 128 x 128 tiles with the K stages split
+  // over about one block per CU (head_static_split), the slices' fp32 tiles
+  // added by a second launch (M = 128, N = 8016: 26.9 against 34.9 us with
+  // W_S from HBM); without one, 64 x 32 tiles whose waves split each stage's
+  // MFMA k-steps in two.  The LDS-DMA kernel takes d % 64 == 0 with 16-byte
+  // aligned rows; the register-staged kernel everything else (128 x 32 narrow
+  // tiles, 4 waves; LDS rows of 64 + 16 bf16).
   const long long t128 = (long long)((M + 127) / 128) * ((a.N + 127) / 128);
-  const bool wide = t128 >= 192;
-  if (vec && d % 64 == 0) return wide ? launch_dma<2, 4, 1, 4, 2, 4>(a, st) : launch_dma<1, 2, 2, 4, 1, 6>(a, st);
+  const bool wide = t128 >= kStaticWideTiles;
+  if (vec && d % 64 == 0) {
+    if (wide) return launch_dma<2, 4, 1, 4, 2, 4>(a, 1, st);
+    const int split = head_static_split(M, d, a.N);
+    if (partial && split > 1) {
+      a.partial = partial;
+      return launch_dma<2, 4, 1, 4, 2, 3>(a, split, st);
+    }
+    return launch_dma<1, 2, 2, 4, 1, 6>(a, 1, st);
+  }
   return wide ? launch_cfg<2, 4, 1, 4, 2, 4, 64, 16>(a, vec, st) : launch_cfg<2, 1, 2, 4, 2, 4, 64, 16>(a, vec, st);
 }
 

@@ -210,15 +210,34 @@ static void head_args() {
            SPEC_ERR_INVALID_ARG);
     free(ns);
   }
-  EXPECT(sv::validate_head_static(h, W, c, 128, 4096, 128256, 1, 32768, o, SPEC_F32, &empty) == SPEC_OK);
-  EXPECT(sv::validate_head_static(fake(0x10001), W, c, 128, 4096, 128256, 1, 32768, o, SPEC_F32, &empty) ==
+  EXPECT(sv::validate_head_static(h, W, c, 128, 4096, 128256, 1, 32768, o, SPEC_F32, nullptr, 0, &empty) == SPEC_OK);
+  EXPECT(sv::validate_head_static(fake(0x10001), W, c, 128, 4096, 128256, 1, 32768, o, SPEC_F32, nullptr, 0, &empty) ==
          SPEC_ERR_INVALID_ARG);
-  EXPECT(sv::validate_head_static(h, W, c, 128, 4096, 128256, 1, 32768, fake(0x40002), SPEC_F32, &empty) ==
+  EXPECT(sv::validate_head_static(h, W, c, 128, 4096, 128256, 1, 32768, fake(0x40002), SPEC_F32, nullptr, 0, &empty) ==
          SPEC_ERR_INVALID_ARG);
-  EXPECT(sv::validate_head_static(h, W, c, 128, 4096, 128256, 1, 32768, fake(0x40002), SPEC_BF16, &empty) ==
+  EXPECT(sv::validate_head_static(h, W, c, 128, 4096, 128256, 1, 32768, fake(0x40002), SPEC_BF16, nullptr, 0, &empty) ==
          SPEC_OK);
-  EXPECT(sv::validate_head_static(h, W, c, INT_MAX, INT_MAX, 1 << 30, 1, 1 << 30, o, SPEC_F32, &empty) != SPEC_OK);
-  EXPECT(sv::validate_head_static(h, W, c, 0, 64, 100, 10, 3, o, SPEC_F32, &empty) == SPEC_OK && empty);
+  EXPECT(sv::validate_head_static(h, W, c, INT_MAX, INT_MAX, 1 << 30, 1, 1 << 30, o, SPEC_F32, nullptr, 0, &empty) != SPEC_OK);
+  EXPECT(sv::validate_head_static(h, W, c, 0, 64, 100, 10, 3, o, SPEC_F32, nullptr, 0, &empty) == SPEC_OK && empty);
+  // the K split: 4 slices of 128 x 8016 fp32 at M = 128, N = 8016; wide shortlists do not split
+  EXPECT(sv::head_static_split(128, 4096, 8016) == 4);
+  EXPECT(sv::head_static_split(128, 4096, 32768) == 1);
+  EXPECT(sv::head_static_split(128, 4000, 8016) == 1);
+  EXPECT(sv::head_static_split(1, 256, 64) == 1);
+  const size_t need = sv::head_static_workspace_bytes(128, 4096, 8016);
+  EXPECT(need == (size_t)4 * 128 * 8016 * 4);
+  EXPECT(sv::validate_head_static(h, W, c, 128, 4096, 128256, 501, 16, o, SPEC_F32, fake(0x100000), need, &empty) ==
+         SPEC_OK);
+  EXPECT(sv::validate_head_static(h, W, c, 128, 4096, 128256, 501, 16, o, SPEC_F32, fake(0x100000), need - 1,
+                                  &empty) == SPEC_ERR_WORKSPACE);
+  EXPECT(sv::validate_head_static(h, W, c, 128, 4096, 128256, 501, 16, o, SPEC_F32, fake(0x100080), need, &empty) ==
+         SPEC_ERR_WORKSPACE);
+  for (int M : {1, 7, 128, 1000})
+    for (int N : {1, 64, 8016, 20000, 32768})
+      for (int d : {64, 128, 4096, 4100}) {
+        const int s = sv::head_static_split(M, d, N);
+        EXPECT(s >= 1 && s <= sv::kStaticMaxSplit && (s == 1 || s * 4 <= d / 64));
+      }
 }
 
 static void kv_args() {

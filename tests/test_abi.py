@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.spec_abi_version() == 1
+    assert lib.spec_abi_version() == 2
     for code in range(5):
         s = lib.spec_status_string(code).decode()
         assert s.startswith("SPEC_")
@@ -124,20 +124,32 @@ def test_head_validation(lib):
 def test_static_head_validation(lib):
     fake = ctypes.c_void_p(0x10000)
     f = lib.spec_draft_head_static
-    assert f(fake, fake, fake, 4, 64, 1000, 7, 2, fake, 0, None) == 2      # V % cs
-    assert f(None, fake, fake, 4, 64, 1000, 10, 2, fake, 0, None) == 1     # NULL h
-    assert f(fake, fake, fake, 4, 64, 1000, 10, 2, None, 0, None) == 1     # NULL out
-    assert f(fake, fake, fake, 4, 64, 1000, 10, 101, fake, 0, None) == 1   # n_sel > V / cs
-    assert f(fake, fake, fake, 4, 0, 1000, 10, 2, fake, 0, None) == 1      # d < 1
-    assert f(fake, fake, fake, -1, 64, 1000, 10, 2, fake, 0, None) == 1    # M < 0
-    assert f(fake, fake, fake, 4, 64, 1000, 10, 2, fake, 7, None) == 1     # bad dtype
-    odd = ctypes.c_void_p(0x10001)
-    assert f(odd, fake, fake, 4, 64, 1000, 10, 2, fake, 0, None) == 1      # h not on a bf16 boundary
-    assert f(fake, fake, fake, 4, 64, 1000, 10, 2, ctypes.c_void_p(0x10002), 0, None) == 1  # fp32 out misaligned
-    assert f(None, None, None, 0, 64, 1000, 10, 2, None, 0, None) == 0     # M = 0: nothing to do
-    assert f(None, None, None, 4, 64, 1000, 10, 0, None, 0, None) == 0     # empty shortlist
+
+    def call(h=fake, W=fake, ids=fake, M=4, d=64, V=1000, cs=10, n_sel=2, out=fake, dt=0, ws=None, wsb=0):
+        return f(h, W, ids, M, d, V, cs, n_sel, out, dt, ws, wsb, None)
+
+    assert call(cs=7) == 2                                # V % cs
+    assert call(h=None) == 1                              # NULL h
+    assert call(out=None) == 1                            # NULL out
+    assert call(n_sel=101) == 1                           # n_sel > V / cs
+    assert call(d=0) == 1                                 # d < 1
+    assert call(M=-1) == 1                                # M < 0
+    assert call(dt=7) == 1                                # bad dtype
+    assert call(h=ctypes.c_void_p(0x10001)) == 1          # h not on a bf16 boundary
+    assert call(out=ctypes.c_void_p(0x10002)) == 1        # fp32 out misaligned
+    assert call(None, None, None, M=0, out=None) == 0     # M = 0: nothing to do
+    assert call(None, None, None, n_sel=0, out=None) == 0  # empty shortlist
     # more than 2^31 - 1 output tiles of 128 x 32
-    assert f(fake, fake, fake, 0x7fffffff, 8, 1 << 20, 1, 1 << 20, fake, 0, None) == 2
+    assert call(M=0x7fffffff, d=8, V=1 << 20, cs=1, n_sel=1 << 20) == 2
+    # the K split's workspace: 4 slices of fp32 [128, 8016] at M = 128, d = 4096, 16 clusters of 501
+    need = lib.spec_draft_head_static_workspace_bytes(128, 4096, 128256, 501, 16)
+    assert need == 4 * 128 * 8016 * 4
+    assert lib.spec_draft_head_static_workspace_bytes(128, 4096, 128256, 1, 32768) == 0   # wide: no split
+    assert lib.spec_draft_head_static_workspace_bytes(128, 4000, 128256, 501, 16) == 0    # d % 64 != 0
+    assert lib.spec_draft_head_static_workspace_bytes(128, 4096, 128257, 501, 16) == 0    # V % cs
+    big = dict(M=128, d=4096, V=128256, cs=501, n_sel=16)
+    assert call(ws=ctypes.c_void_p(0x100000), wsb=need - 1, **big) == 3     # too small
+    assert call(ws=ctypes.c_void_p(0x100080), wsb=need, **big) == 3         # not 256-byte aligned
 
 
 def test_kv_commit_validation(lib):

@@ -137,3 +137,36 @@ def test_static_head_empty():
     out = sv.spec_draft_head_static(torch.zeros((3, 64), dtype=torch.bfloat16, device=DEV), W,
                                     torch.zeros((0,), dtype=torch.int32, device=DEV), 10)
     assert out.shape == (3, 0)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_static_head_k_split_against_oracle_and_single_launch(dtype):
+    """Narrow shortlists with d % 64 == 0 split d over blocks (fp32 partial tiles
+    added in a fixed order by a second launch): M = 130 (two row tiles, the
+    second of 2 rows), d = 1024 (four slices of 4 stages), N = 1000 in clusters
+    of 8; against the oracle and against the unsplit kernel."""
+    import speculative_sampling_verification_vocab_amd as sv
+    hc = head_case(13, 10, 1024, 8000, 1000, 1, trial=11)
+    ids = _static_ids(8000, 8, 125, seed=13)
+    assert sv._native.load().spec_draft_head_static_workspace_bytes(130, 1024, 8000, 8, 125) == 4 * 130 * 1000 * 4
+    got, ref = _check(hc.h, hc.W, ids, 8, dtype)
+    one = sv.spec_draft_head_static(hc.h.to(DEV), hc.W.to(DEV), ids.to(DEV), 8, dtype=dtype, split=False)
+    torch.cuda.synchronize()
+    tol = 2 * HEAD_TOL * ref["absdot"] + 1e-30
+    if dtype == torch.bfloat16:
+        tol = tol + np.abs(ref["compact"]) * 2.0 ** -7
+    assert np.all(np.abs(one.float().cpu().numpy() - got) <= tol)
+    # repeated calls (the workspace is reused) give identical results
+    again = _gpu(hc.h, hc.W, ids, 8, dtype)
+    np.testing.assert_array_equal(again, got)
+
+
+def test_static_head_k_split_out_of_range_ids_read_zero():
+    hc = head_case(2, 3, 512, 1000, 10, 1, trial=12)
+    ids = torch.tensor([1, 10, -1, 4], dtype=torch.int32)
+    got = _gpu(hc.h, hc.W, ids, 100)
+    assert np.all(got[..., 100:300] == 0.0)
+    ref = _oracle(hc.h, hc.W, torch.tensor([1, 4], dtype=torch.int32), 100)
+    tol = HEAD_TOL * ref["absdot"] + 1e-30
+    assert np.all(np.abs(got[..., :100] - ref["compact"][..., :100]) <= tol[..., :100])
+    assert np.all(np.abs(got[..., 300:] - ref["compact"][..., 100:]) <= tol[..., 100:])

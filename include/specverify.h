@@ -139,9 +139,12 @@ spec_status_t spec_verify(const void* target_logits, const void* draft_logits,
 /*
  * Number of kernel launches spec_verify makes for this shape (0 for an empty
  * or invalid shape).  SAMPLE mode: 4 for large batches (row statistics;
- * accept decisions; the sampled rows' tile sums; token pick), 3 for small ones
- * (the accept decisions run in the prologue of the tile-sum launch: B=256,
- * K=7, V=262144 takes 4, B=8, K=5, V=128256 takes 3).  SAMPLE_EARLY_EXIT: K + 2 (row
+ * accept decisions; the sampled rows' tile sums; token pick), 3 for middle
+ * ones (the accept decisions run in the prologue of the tile-sum launch), 2
+ * for small ones (whose tile-sum launch also picks the token in its last
+ * block per sequence): B=256, K=7, V=262144 takes 4, B=64, K=4, V=151936
+ * takes 3, B=8, K=5, V=128256 takes 2; with K = 0, the tile sums and the
+ * pick.  SAMPLE_EARLY_EXIT: K + 2 (row
  * statistics of position i for i = 0..K-1, each launch also deciding
  * position i - 1; then the decision of position K - 1 with the sampled rows'
  * tile sums, and the token pick).  GREEDY mode: 2 (per-tile argmax,

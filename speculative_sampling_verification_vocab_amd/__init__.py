@@ -18,7 +18,7 @@ import torch
 from . import _native
 from ._native import SpecVerifyError  # noqa: F401
 
-__all__ = ["spec_verify", "spec_verify_noalloc", "spec_verify_workspace_bytes", "spec_verify_launch_count", "spec_draft_head_shortlist",
+__all__ = ["spec_verify", "VerifyPlan", "spec_verify_noalloc", "spec_verify_workspace_bytes", "spec_verify_launch_count", "spec_draft_head_shortlist",
            "spec_kv_commit", "spec_verify_sparse_draft", "position_budget", "spec_draft_head_positions",
            "spec_draft_head_static",
            "Workspace", "SpecVerifyError", "abi_version"]
@@ -138,6 +138,74 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_token
     if return_probs:
         return acc, out, pt, pd
     return acc, out
+
+
+class VerifyPlan:
+    """spec_verify prepared once for a fixed shape, for serving loops.
+
+    The output tensors and the workspace are allocated when the plan is made
+    and reused by every call, which is then only argument packing and one C
+    call (no allocation).  Each call returns the same output tensors,
+    overwritten in place: copy them before the next call if they must be kept.
+    Inputs must have the shapes and dtype the plan was made for (checked) and
+    be contiguous GPU tensors."""
+
+    def __init__(self, B: int, K: int, V: int, dtype: torch.dtype = torch.bfloat16, mode: str = "sample", *,
+                 device="cuda", stream=None, return_probs: bool = False):
+        if mode not in _MODES:
+            raise ValueError(f"mode must be one of {list(_MODES)}")
+        if dtype not in _DTYPES:
+            raise ValueError("logits must be bfloat16 or float32")
+        dev = torch.device(device)
+        if dev.index is None:
+            dev = torch.device(dev.type, torch.cuda.current_device())
+        self.B, self.K, self.V, self.dtype, self.mode = int(B), int(K), int(V), dtype, mode
+        self._sampling = mode in _SAMPLING
+        lib = _native.load()
+        self._lib = lib
+        self._dt, self._m = _DTYPES[dtype], _MODES[mode]
+        self.accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
+        self.out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        self.p_target = torch.empty((B, K), dtype=torch.float32, device=dev) if return_probs else None
+        self.p_draft = torch.empty((B, K), dtype=torch.float32, device=dev) if return_probs else None
+        s = _stream_of(dev, stream)
+        need = lib.spec_verify_workspace_bytes(B, K, V, self._dt, self._m)
+        with torch.cuda.stream(s):
+            self._ws = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
+        self._stream = s.cuda_stream
+        self._tail = [self.accepted_len.data_ptr(), self.out_tokens.data_ptr(),
+                      self.p_target.data_ptr() if return_probs else None,
+                      self.p_draft.data_ptr() if return_probs else None,
+                      self._ws.data_ptr(), self._ws.numel(), self._stream]
+        self._shapes = ((B, K + 1, V), (B, K, V), (B, K), (B, K + 1, 2))
+        self._out = (self.accepted_len, self.out_tokens) + ((self.p_target, self.p_draft) if return_probs else ())
+
+    def _arg(self, t, shape, dtype, name):
+        if t.shape != shape or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor {dtype} {list(shape)}")
+        return t.data_ptr()
+
+    def __call__(self, target, draft, draft_tokens, uniforms, temperature: float = 1.0, events=None):
+        sh = self._shapes
+        tp = self._arg(target, sh[0], self.dtype, "target")
+        dp = up = kp = None
+        if self.K > 0:
+            kp = self._arg(draft_tokens, sh[2], torch.int32, "draft_tokens")
+        if self._sampling:
+            if self.K > 0:
+                dp = self._arg(draft, sh[1], self.dtype, "draft")
+            up = self._arg(uniforms, sh[3], torch.float32, "uniforms")
+        args = [tp, dp, kp, up, self.B, self.K, self.V, self._dt,
+                ctypes.c_float(temperature if self._sampling else 0.0), self._m, *self._tail]
+        if events is None:
+            st = self._lib.spec_verify(*args)
+        else:
+            evs = list(events)
+            arr = (ctypes.c_void_p * max(1, len(evs)))(*[e.cuda_event if e is not None else None for e in evs])
+            st = self._lib.spec_verify_timed(*args, arr, len(evs))
+        if st:
+            _native.check(st, "spec_verify")
+        return self._out
 
 
 def _check_verify_inputs(target, draft, draft_tokens, uniforms, mode):

@@ -32,6 +32,7 @@ constexpr int sample_tile_elems(int elem_bytes) { return kWave * vec_elems(elem_
 constexpr int kMaxTilesPerWaveS = 8;
 constexpr int kSampleBlocksWanted = 1024;  // 4 per CU
 constexpr int kEEBlocksForTwo = 4096;      // early-exit phase blocks at one tile per wave from which waves take two
+constexpr long long kFusedPickMaxBlocks = 512;  // sampling grids up to this size pick in their last block
 constexpr int kHeadMaxCtx = 1024;          // contexts the shortlist head lists per cluster
 constexpr size_t kMaxGrid = 0x7fffffffu;
 
@@ -76,6 +77,7 @@ struct VerifyShape {
   int TPW_s;     // sampling-pass tiles per wave
   int TPW_e;     // early-exit phases: statistics tiles per wave
   bool decide;   // SAMPLE: a separate decision launch before the sampling pass
+  bool fused_pick;  // SAMPLE: the last sampling block of each sequence picks its token (K > 0)
 };
 
 struct VerifyWorkspace {
@@ -85,6 +87,7 @@ struct VerifyWorkspace {
   ArgTile* part_g;      // [B][K+1][NT]
   float* gx;            // [B][2K] logits at the draft tokens: target rows 0..K-1, then draft rows
   int32_t* cont;        // [K][B] early exit: 1 if the sequence accepted positions 0..j and goes on
+  uint32_t* arrive;     // [B] SAMPLE: sampling blocks of the sequence that have finished (zeroed by the statistics pass)
 };
 
 struct VerifyIO {
@@ -130,6 +133,13 @@ inline VerifyShape make_shape(int B, int K, int V, int dtype, bool aligned) {
   // A separate decision launch pays off once blocks cover several sampling
   // tiles (B=256, K=7, V=262144: 353 -> 348 us; B=8: 21.8 -> 24.5 us with it).
   s.decide = s.TPW_s > 1;
+  // Small sampling grids pick the token in their last block per sequence
+  // instead of a launch of their own (B=1, K=4, V=32000: 20 -> 14 us; B=8,
+  // K=5, V=128256: 19.5 -> 18 us).  A statistics launch precedes them to
+  // clear the arrival counters.  Large grids keep the separate pick: there the
+  // arrival round trip and the pick's registers in every sampling block cost
+  // more than the launch (B=256, K=7, V=262144: 66 -> 71 us).
+  s.fused_pick = K > 0 && !s.decide && (long long)B * s.NG_s <= kFusedPickMaxBlocks;
   return s;
 }
 
@@ -146,7 +156,7 @@ inline size_t verify_workspace_layout(const VerifyShape& s, int mode, void* base
     off = align256(off + bytes);
     return at;
   };
-  size_t o_pa = 0, o_rows = 0, o_pb = 0, o_pg = 0, o_gx = 0, o_cont = 0;
+  size_t o_pa = 0, o_rows = 0, o_pb = 0, o_pg = 0, o_gx = 0, o_cont = 0, o_arr = 0;
   if (greedy) {
     o_pg = take(B * (K + 1) * (size_t)s.NT * sizeof(ArgTile));
   } else {
@@ -155,6 +165,7 @@ inline size_t verify_workspace_layout(const VerifyShape& s, int mode, void* base
     o_pb = take(B * (size_t)s.NT_s * sizeof(SampleTile));
     o_gx = take(B * 2 * (K > 0 ? K : 1) * sizeof(float));
     if (early) o_cont = take(B * (K > 0 ? K : 1) * sizeof(int32_t));
+    else o_arr = take(B * sizeof(uint32_t));
   }
   if (out && base) {
     VerifyWorkspace w{};
@@ -167,13 +178,18 @@ inline size_t verify_workspace_layout(const VerifyShape& s, int mode, void* base
       w.part_b = reinterpret_cast<SampleTile*>(p + o_pb);
       w.gx = reinterpret_cast<float*>(p + o_gx);
       if (early) w.cont = reinterpret_cast<int32_t*>(p + o_cont);
+      else w.arrive = reinterpret_cast<uint32_t*>(p + o_arr);
     }
     *out = w;
   }
   return off;
 }
 
-inline int sample_launches(const VerifyShape& s) { return s.B == 0 ? 0 : (s.decide ? 4 : 3); }
+// statistics (K > 0), decisions (large batches), sampling, and the pick when
+// it is not fused into the sampling launch
+inline int sample_launches(const VerifyShape& s) {
+  return s.B == 0 ? 0 : (s.K > 0 ? 1 : 0) + (s.decide ? 1 : 0) + 1 + (s.fused_pick ? 0 : 1);
+}
 inline int early_exit_launches(const VerifyShape& s) { return s.B == 0 ? 0 : s.K + 2; }
 
 // ---- argument checks ------------------------------------------------------------

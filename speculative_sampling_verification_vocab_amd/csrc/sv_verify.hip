@@ -68,6 +68,8 @@ struct VerifyArgs {
   SampleTile* part_b;    // [B][NTs]
   float* gx;             // [B][2K] logits at the draft tokens (written by the statistics pass)
   int32_t* cont;         // [K][B] early exit only
+  uint32_t* arrive;      // [B] finished sampling blocks per sequence (fused pick)
+  int fused_pick;        // SAMPLE: the last sampling block of a sequence picks its token
   // Sparse draft rows (null cids: dense [B][K][V] draft rows).  Position i's
   // draft logits exist on the union of its nsel[i] clusters of cs ids and are
   // stored compactly, [B][K][L], in ascending token id.
@@ -80,6 +82,17 @@ struct VerifyArgs {
   float* p_t_out;
   float* p_d_out;
 };
+
+// accepted_len and out_tokens.  kCoherent (the fused pick): stored
+// write-through at agent scope, because the first sampling block of a
+// sequence writes them and its last block (possibly on another XCD, whose L2
+// would otherwise write its own dirty copy back later) overwrites position n
+// with the picked token.  Elsewhere one launch writes each entry once.
+template <bool kCoherent = false>
+__device__ __forceinline__ void put_out(int32_t* p, int32_t v) {
+  if constexpr (kCoherent) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
 
 template <typename T>
 __device__ __forceinline__ const T* row_ptr(const void* base, size_t rows_before, int V) {
@@ -401,9 +414,9 @@ __device__ __forceinline__ SampleRowInfo ee_decide(const VerifyArgs& a, int b, i
         }
       }
       for (int q = lane; q <= K; q += kWave)
-        a.out_tokens[(size_t)b * (K + 1) + q] = (n >= 0 && q < n) ? tok[q] : -1;
+        put_out(&a.out_tokens[(size_t)b * (K + 1) + q], (n >= 0 && q < n) ? tok[q] : -1);
       if (lane == 0) {
-        a.accepted_len[b] = n;
+        put_out(&a.accepted_len[b], n);
         a.rows[b] = sr;
       }
     }
@@ -413,6 +426,7 @@ __device__ __forceinline__ SampleRowInfo ee_decide(const VerifyArgs& a, int b, i
 
 // Returns the record for the sampling pass (n = -1 for a faulty sequence; by
 // value and inlined, so it stays in registers).
+template <bool kCoherent = false>
 __device__ __forceinline__ SampleRowInfo accept_sequence(const VerifyArgs& a, int b, bool write) {
   __shared__ float sh_m[2 * kMaxK];
   __shared__ double sh_z[2 * kMaxK];
@@ -505,9 +519,9 @@ __device__ __forceinline__ SampleRowInfo accept_sequence(const VerifyArgs& a, in
     }
     // Thread i holds draft token i; position n and the padding get -1 here,
     // pick_kernel overwrites position n with the sampled token.
-    if (i <= K) a.out_tokens[(size_t)b * (K + 1) + i] = (n >= 0 && i < n) ? d : -1;
+    if (i <= K) put_out<kCoherent>(&a.out_tokens[(size_t)b * (K + 1) + i], (n >= 0 && i < n) ? d : -1);
     if (i == 0) {
-      a.accepted_len[b] = n;
+      put_out<kCoherent>(&a.accepted_len[b], n);
       a.rows[b] = info;
     }
   }
@@ -556,11 +570,43 @@ __device__ __forceinline__ float lane_value(float v, int l) {
 template <typename T>
 constexpr int kSubTiles = kTile<T> / kTileS<T>;  // sampling tiles per statistics tile
 
+// With the fused pick, sampling-pass tile records are written and read with
+// agent-scope atomic accesses: write-through stores and loads that are
+// coherent across the XCDs' separate L2 caches, so the last block of a
+// sequence sees every other block's records once it has seen their arrivals.
+// (A separate pick launch reads them after a kernel boundary.)
+template <bool kCoherent>
+__device__ __forceinline__ void put_sample_tile(SampleTile* p, const SampleTile& v) {
+  if constexpr (!kCoherent) {
+    *p = v;
+  } else {
+    const double w[6] = {v.mt, v.md, v.zt, v.zd, v.g, v.h};
+    uint64_t* q = reinterpret_cast<uint64_t*>(p);
+#pragma unroll
+    for (int i = 0; i < 6; ++i)
+      __hip_atomic_store(q + i, __builtin_bit_cast(uint64_t, w[i]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <bool kCoherent>
+__device__ __forceinline__ SampleTile get_sample_tile(const SampleTile* p) {
+  if constexpr (!kCoherent) {
+    return *p;
+  } else {
+    const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+    double w[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i)
+      w[i] = __builtin_bit_cast(double, __hip_atomic_load(q + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    return SampleTile{w[0], w[1], w[2], w[3], w[4], w[5]};
+  }
+}
+
 // Residual tile sums of tile t from packed slices cx (target) and cy (draft)
 // with references (mt, md) and positive-set ratio rho.
 // ht and hd are exp_ref_hi of the references mt and md; the sums are in units
 // of 2^(x * s - h), which pick_block rescales by 2^-lo.
-template <typename T, int NL>
+template <typename T, int NL, bool kCoherent>
 __device__ __forceinline__ void residual_tile(const VerifyArgs& a, int b, int t, float mt, float md, float ht,
                                               float hd, float rho, const u32x4 (&cx)[NL], const u32x4 (&cy)[NL]) {
   constexpr int P = NL * Elem<T>::kVec;
@@ -581,11 +627,12 @@ __device__ __forceinline__ void residual_tile(const VerifyArgs& a, int b, int t,
   zd = wave_sum(zd);
   gs = wave_sum(gs);
   hs = wave_sum(hs);
-  if (lane == 0) a.part_b[(size_t)b * a.NTs + t] = SampleTile{(double)mt, (double)md, zt, zd, gs, hs};
+  if (lane == 0)
+    put_sample_tile<kCoherent>(a.part_b + (size_t)b * a.NTs + t, SampleTile{(double)mt, (double)md, zt, zd, gs, hs});
 }
 
 // Bonus-row tile sums of tile t (target row K), referenced to the tile's own maximum.
-template <typename T, int NL>
+template <typename T, int NL, bool kCoherent>
 __device__ __forceinline__ void bonus_tile(const VerifyArgs& a, int b, int t, const u32x4 (&cx)[NL]) {
   constexpr int P = NL * Elem<T>::kVec;
   const int lane = threadIdx.x & (kWave - 1);
@@ -597,15 +644,27 @@ __device__ __forceinline__ void bonus_tile(const VerifyArgs& a, int b, int t, co
     for (int i = 0; i < P; ++i) zt += (double)exp2_ref(raw_elem<T>(cx, i), a.s_hi, ht);
   }
   zt = wave_sum(zt);
-  if (lane == 0) a.part_b[(size_t)b * a.NTs + t] = SampleTile{(double)mt, (double)kNegInf, zt, 0.0, 0.0, 0.0};
+  if (lane == 0)
+    put_sample_tile<kCoherent>(a.part_b + (size_t)b * a.NTs + t,
+                               SampleTile{(double)mt, (double)kNegInf, zt, 0.0, 0.0, 0.0});
 }
+
+// The token pick of sequence b (defined below): kFused when it runs in the
+// sampling launch's last block of the sequence, which passes its own copy of
+// the row record and reads the tile records with coherent loads.
+template <typename T, bool kAligned, bool kSparse = false, bool kFused = false>
+__device__ __forceinline__ void pick_block(const VerifyArgs& a, int b, const SampleRowInfo& sr_local);
 
 // Block `blk` of the sampling pass.
 // kFromRows: n and the row record come from the early-exit decisions
 // (a.rows) instead of this block's own accept prologue.
 // kDecided: decide_kernel has taken every accept decision and left the
 // record in rows[b].
-template <typename T, bool kAligned, bool kFromRows = false, bool kSparse = false, bool kDecided = false>
+// kFused (small grids of the SAMPLE schedule, a.fused_pick): each block
+// counts itself in arrive[b] once its tile records are written, and the last
+// of the sequence's blocks picks the token.
+template <typename T, bool kAligned, bool kFromRows = false, bool kSparse = false, bool kDecided = false,
+          bool kFused = false>
 __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int K = a.K;
@@ -637,7 +696,7 @@ __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
       n = sr.n;
     }
   } else {
-    sr = accept_sequence(a, b, g == 0);
+    sr = accept_sequence<kFused>(a, b, g == 0);
     n = sr.n;
   }
   if (n < 0) return;  // faulty sequence: outputs already written
@@ -657,31 +716,47 @@ __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
     __shared__ int16_t sh_tab[kRankTab];
     if (resid) tab = build_rank_tab(a, b, n, sh_tab);  // resid is uniform over the block
   }
-  if (tile_of(0) >= a.NTs) return;
-  // Residual: lane l holds the references and the ratio of statistics tile T0 + l.
-  const int T0 = g * a.TPWs * kWavesPerBlock / kSubTiles<T>;
-  float ref_t = kNegInf, ref_d = kNegInf, rho_l = 0.0f;
-  if (resid && lane < a.TPWs * kWavesPerBlock / kSubTiles<T> && T0 + lane < a.NT) {
-    const size_t R = 2 * (size_t)K;
-    ref_t = a.part_a[((size_t)b * R + n) * a.NT + T0 + lane].m;
-    // a sparse draft row has no dense tiles: its row maximum is the reference
-    ref_d = kSparse ? sr.m_d : a.part_a[((size_t)b * R + K + n) * a.NT + T0 + lane].m;
-    rho_l = tile_rho(ref_t, ref_d, sr, a.s64, a.s_hi);
+  if (tile_of(0) < a.NTs) {
+    // Residual: lane l holds the references and the ratio of statistics tile T0 + l.
+    const int T0 = g * a.TPWs * kWavesPerBlock / kSubTiles<T>;
+    float ref_t = kNegInf, ref_d = kNegInf, rho_l = 0.0f;
+    if (resid && lane < a.TPWs * kWavesPerBlock / kSubTiles<T> && T0 + lane < a.NT) {
+      const size_t R = 2 * (size_t)K;
+      ref_t = a.part_a[((size_t)b * R + n) * a.NT + T0 + lane].m;
+      // a sparse draft row has no dense tiles: its row maximum is the reference
+      ref_d = kSparse ? sr.m_d : a.part_a[((size_t)b * R + K + n) * a.NT + T0 + lane].m;
+      rho_l = tile_rho(ref_t, ref_d, sr, a.s64, a.s_hi);
+    }
+    const float hi_t = exp_ref_hi(ref_t, a.s_hi), hi_d = exp_ref_hi(ref_d, a.s_hi);
+    for (int j = 0; j < a.TPWs; ++j) {
+      const int t = tile_of(j);
+      if (t >= a.NTs) break;
+      u32x4 cx[NL], cy[NL];
+      load_raw<T, kAligned, kLoadsS>(trow, a.V, t, lane, cx);
+      if (resid) {
+        if constexpr (kSparse) sparse_tile_raw<T>(a, b, n, t, lane, cy, tab);
+        else load_raw<T, kAligned, kLoadsS>(drow, a.V, t, lane, cy);
+        const int lt = t / kSubTiles<T> - T0;
+        residual_tile<T, NL, kFused>(a, b, t, lane_value(ref_t, lt), lane_value(ref_d, lt), lane_value(hi_t, lt),
+                                     lane_value(hi_d, lt), lane_value(rho_l, lt), cx, cy);
+      } else {
+        bonus_tile<T, NL, kFused>(a, b, t, cx);
+      }
+    }
   }
-  const float hi_t = exp_ref_hi(ref_t, a.s_hi), hi_d = exp_ref_hi(ref_d, a.s_hi);
-  for (int j = 0; j < a.TPWs; ++j) {
-    const int t = tile_of(j);
-    if (t >= a.NTs) break;
-    u32x4 cx[NL], cy[NL];
-    load_raw<T, kAligned, kLoadsS>(trow, a.V, t, lane, cx);
-    if (resid) {
-      if constexpr (kSparse) sparse_tile_raw<T>(a, b, n, t, lane, cy, tab);
-      else load_raw<T, kAligned, kLoadsS>(drow, a.V, t, lane, cy);
-      const int lt = t / kSubTiles<T> - T0;
-      residual_tile<T>(a, b, t, lane_value(ref_t, lt), lane_value(ref_d, lt), lane_value(hi_t, lt),
-                       lane_value(hi_d, lt), lane_value(rho_l, lt), cx, cy);
-    } else {
-      bonus_tile<T>(a, b, t, cx);
+  if constexpr (kFused) {
+    {
+      // This block's tile records have completed (write-through); then it
+      // counts itself.  Every block of the sequence reaches this point (n is
+      // the same in each), so the last arrival sees all the records.
+      __shared__ int sh_last;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0)
+        sh_last = __hip_atomic_fetch_add(a.arrive + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  (unsigned)(a.NGs - 1);
+      __syncthreads();
+      if (sh_last) pick_block<T, kAligned, kSparse, true>(a, b, sr);
     }
   }
 }
@@ -750,8 +825,8 @@ __device__ __forceinline__ void block_min2(int& x, int& y, int* sh) {
 // The tile sums of the sequence (one per thread for up to 256 tiles) and the
 // sample uniforms are loaded together with the row record, so the block waits
 // for one memory round trip before the tile choice and one for the tile.
-template <typename T, bool kAligned, bool kSparse = false>
-__device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
+template <typename T, bool kAligned, bool kSparse, bool kFused>
+__device__ __forceinline__ void pick_block(const VerifyArgs& a, int b, const SampleRowInfo& sr_local) {
   __shared__ double sh_d[4 * kWavesPerBlock];
   __shared__ float sh_f[2 * kWavesPerBlock];
   __shared__ int sh_i[2 * kWavesPerBlock];
@@ -764,13 +839,13 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
   const SampleTile* P = a.part_b + (size_t)b * NT;
   const bool cached = NT <= kBlock;
   SampleTile q0{kNegInfD, kNegInfD, 0.0, 0.0, 0.0, 0.0};
-  if (cached && (int)threadIdx.x < NT) q0 = P[threadIdx.x];
+  if (cached && (int)threadIdx.x < NT) q0 = get_sample_tile<kFused>(P + threadIdx.x);
   if ((int)threadIdx.x <= K) sh_u[threadIdx.x] = a.uniforms[((size_t)b * (K + 1) + threadIdx.x) * 2 + 1];
-  const SampleRowInfo sr = a.rows[b];
+  const SampleRowInfo sr = kFused ? sr_local : a.rows[b];
   const int n = K == 0 ? 0 : sr.n;
   if (n < 0) return;  // uniform over the block: every thread read the same record
   const bool resid = n < K;
-  auto tile_at = [&](int tt) -> SampleTile { return cached ? q0 : P[tt]; };
+  auto tile_at = [&](int tt) -> SampleTile { return cached ? q0 : get_sample_tile<kFused>(P + tt); };
 
   // Reference maxima: statistics-pass maxima for a residual pair, the maximum
   // over tiles for the bonus row (the statistics pass does not read row K).
@@ -808,8 +883,8 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
   block_sum4(zbt, zbd, G, H, sh_d);
   if (!isfinite(mref_t) || !(zbt > 0.0) || !isfinite(zbt) || (resid && (!(zbd > 0.0) || !isfinite(zbd)))) {
     // A sampled row without a finite maximum: the sequence is faulty.
-    for (int i = threadIdx.x; i <= K; i += kBlock) a.out_tokens[(size_t)b * (K + 1) + i] = -1;
-    if (threadIdx.x == 0) a.accepted_len[b] = -1;
+    for (int i = threadIdx.x; i <= K; i += kBlock) put_out<kFused>(&a.out_tokens[(size_t)b * (K + 1) + i], -1);
+    if (threadIdx.x == 0) put_out<kFused>(&a.accepted_len[b], -1);
     return;
   }
 
@@ -867,8 +942,8 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
   const bool no_cross = jstar < 0;
   if (no_cross) jstar = last_mass;
   if (jstar < 0) {
-    for (int i = threadIdx.x; i <= K; i += kBlock) a.out_tokens[(size_t)b * (K + 1) + i] = -1;
-    if (threadIdx.x == 0) a.accepted_len[b] = -1;
+    for (int i = threadIdx.x; i <= K; i += kBlock) put_out<kFused>(&a.out_tokens[(size_t)b * (K + 1) + i], -1);
+    if (threadIdx.x == 0) put_out<kFused>(&a.accepted_len[b], -1);
     return;
   }
 
@@ -946,10 +1021,10 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
   block_min2(mine, neg_last_pos, sh_i);
   const int token = mine != 0x7fffffff ? mine : -neg_last_pos;
   if (threadIdx.x == 0) {
-    a.out_tokens[(size_t)b * (K + 1) + n] = token;
-    a.accepted_len[b] = token >= 0 ? n : -1;
+    put_out<kFused>(&a.out_tokens[(size_t)b * (K + 1) + n], token);
+    put_out<kFused>(&a.accepted_len[b], token >= 0 ? n : -1);
     if (token < 0)
-      for (int i = 0; i <= K; ++i) a.out_tokens[(size_t)b * (K + 1) + i] = -1;
+      for (int i = 0; i <= K; ++i) put_out<kFused>(&a.out_tokens[(size_t)b * (K + 1) + i], -1);
   }
 }
 
@@ -957,6 +1032,11 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b) {
 // scratch and measured 16 % slower than the compiler's five.)
 template <typename T, bool kAligned, bool kSparse = false>
 __global__ void __launch_bounds__(kBlock) stats_kernel(VerifyArgs a) {
+  // The sampling launch that follows counts its finished blocks per sequence
+  // from zero (the workspace holds the previous call's counts).
+  if (a.fused_pick)
+    for (int i = blockIdx.x * kBlock + threadIdx.x; i < a.B; i += gridDim.x * kBlock)
+      __hip_atomic_store(a.arrive + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   stats_block<T, kAligned, kSparse>(a, blockIdx.x);
 }
 
@@ -970,14 +1050,14 @@ __global__ void __launch_bounds__(kBlock) decide_kernel(VerifyArgs a) {
   (void)accept_sequence(a, blockIdx.x, true);
 }
 
-template <typename T, bool kAligned, bool kSparse = false, bool kDecided = false>
+template <typename T, bool kAligned, bool kSparse = false, bool kDecided = false, bool kFused = false>
 __global__ void __launch_bounds__(kBlock) sample_kernel(VerifyArgs a) {
-  sample_block<T, kAligned, false, kSparse, kDecided>(a, blockIdx.x);
+  sample_block<T, kAligned, false, kSparse, kDecided, kFused>(a, blockIdx.x);
 }
 
 template <typename T, bool kAligned, bool kSparse = false>
 __global__ void __launch_bounds__(kBlock) pick_kernel(VerifyArgs a) {
-  pick_block<T, kAligned, kSparse>(a, blockIdx.x);
+  pick_block<T, kAligned, kSparse, false>(a, blockIdx.x, SampleRowInfo{});
 }
 
 // ---------------------------------------------------------------------------
@@ -1184,6 +1264,8 @@ static VerifyArgs verify_args(const VerifyShape& s, const VerifyIO& io, const Ve
   a.part_b = ws.part_b;
   a.gx = ws.gx;
   a.cont = ws.cont;
+  a.arrive = ws.arrive;
+  a.fused_pick = 0;
   a.cids = io.cids;
   if (io.cids) {
     a.L = io.L;
@@ -1208,11 +1290,12 @@ static hipError_t sample_pipeline(const VerifyShape& s, const VerifyArgs& a, hip
     ++k;
   };
   hipError_t e = hipSuccess;
-  record();
-  if (s.K > 0)
+  if (s.K > 0) {
+    record();
     e = dispatch4(s.dtype, s.aligned, dim3((unsigned)((size_t)s.B * 2 * s.K * s.NG)), st,
                   stats_kernel<uint16_t, true, kSparse>, stats_kernel<uint16_t, false, kSparse>,
                   stats_kernel<float, true, kSparse>, stats_kernel<float, false, kSparse>, a);
+  }
   record();
   const dim3 sgrid((unsigned)((size_t)s.B * s.NG_s));
   if (s.decide) {
@@ -1225,16 +1308,22 @@ static hipError_t sample_pipeline(const VerifyShape& s, const VerifyArgs& a, hip
       e = dispatch4(s.dtype, s.aligned, sgrid, st, sample_kernel<uint16_t, true, kSparse, true>,
                     sample_kernel<uint16_t, false, kSparse, true>, sample_kernel<float, true, kSparse, true>,
                     sample_kernel<float, false, kSparse, true>, a);
+  } else if (e == hipSuccess && s.fused_pick) {
+    e = dispatch4(s.dtype, s.aligned, sgrid, st, sample_kernel<uint16_t, true, kSparse, false, true>,
+                  sample_kernel<uint16_t, false, kSparse, false, true>, sample_kernel<float, true, kSparse, false, true>,
+                  sample_kernel<float, false, kSparse, false, true>, a);
   } else if (e == hipSuccess) {
     e = dispatch4(s.dtype, s.aligned, sgrid, st, sample_kernel<uint16_t, true, kSparse>,
                   sample_kernel<uint16_t, false, kSparse>, sample_kernel<float, true, kSparse>,
                   sample_kernel<float, false, kSparse>, a);
   }
-  record();
-  if (e == hipSuccess)
-    e = dispatch4(s.dtype, s.aligned, dim3((unsigned)s.B), st, pick_kernel<uint16_t, true, kSparse>,
-                  pick_kernel<uint16_t, false, kSparse>, pick_kernel<float, true, kSparse>,
-                  pick_kernel<float, false, kSparse>, a);
+  if (!s.fused_pick) {
+    record();
+    if (e == hipSuccess)
+      e = dispatch4(s.dtype, s.aligned, dim3((unsigned)s.B), st, pick_kernel<uint16_t, true, kSparse>,
+                    pick_kernel<uint16_t, false, kSparse>, pick_kernel<float, true, kSparse>,
+                    pick_kernel<float, false, kSparse>, a);
+  }
   record();
   return e;
 }
@@ -1248,7 +1337,8 @@ static hipError_t sample_pipeline(const VerifyShape& s, const VerifyArgs& a, hip
 hipError_t launch_sample_pipeline(const VerifyShape& s, const VerifyIO& io, const VerifyWorkspace& ws,
                                   hipStream_t st, void* const* events, int n_events) {
   if (s.B == 0) return hipSuccess;
-  const VerifyArgs a = verify_args(s, io, ws);
+  VerifyArgs a = verify_args(s, io, ws);
+  a.fused_pick = s.fused_pick ? 1 : 0;
   return io.cids ? sample_pipeline<true>(s, a, st, events, n_events)
                  : sample_pipeline<false>(s, a, st, events, n_events);
 }

@@ -60,7 +60,9 @@ def test_workspace_sizes(lib):
 def test_launch_counts(lib):
     f = lib.spec_verify_launch_count
     assert f(256, 7, 262144, 1, 0) == 4            # statistics, decisions, sampling, pick
-    assert f(8, 5, 128256, 1, 0) == 3              # small batch: decisions in the sampling prologue
+    assert f(64, 4, 151936, 1, 0) == 3             # decisions in the sampling prologue
+    assert f(8, 5, 128256, 1, 0) == 2              # small grid: the sampling launch also picks
+    assert f(8, 0, 128256, 1, 0) == 2              # K = 0: sampling, then a separate pick
     assert f(256, 7, 262144, 1, 1) == 2            # greedy argmax, finalize
     assert f(256, 7, 262144, 1, 2) == 7 + 2        # one launch per position; sampling; pick
     assert f(4, 0, 1000, 0, 2) == 2

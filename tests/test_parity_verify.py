@@ -113,7 +113,7 @@ def test_sample_decision_launch_and_prologue_agree():
     from speculative_sampling_verification_vocab_amd import _native
     lib = _native.load()
     assert lib.spec_verify_launch_count(1024, 2, 16384, 1, 0) == 4
-    assert lib.spec_verify_launch_count(64, 2, 16384, 1, 0) == 3
+    assert lib.spec_verify_launch_count(64, 2, 16384, 1, 0) == 2    # small grid: fused pick
     c = _case(1024, 2, 16384, "bf16", key=(25,))
     rep, out, orc = check_case(c)
     for s0 in range(0, 1024, 64):
@@ -299,3 +299,24 @@ def test_concurrent_streams_use_separate_default_workspaces():
         hc = VerifyCase(c.target.cpu(), c.draft.cpu(), c.draft_tokens.cpu(), c.uniforms.cpu(), c.temperature, c.dtype)
         rep = compare(r[0], r[1], run_oracle(hc, gpu=r), c.K)
         assert not rep.failures, rep.failures[:3]
+
+
+@pytest.mark.parametrize("mode", ["sample", "greedy", "sample_early_exit"])
+def test_verify_plan_matches_spec_verify(mode):
+    """VerifyPlan (outputs and workspace allocated once, one C call per step)
+    gives spec_verify's outputs on consecutive calls with different inputs."""
+    import speculative_sampling_verification_vocab_amd as sv
+    print(f"case verify plan {mode}: B=8 K=5 V=30000 bf16", flush=True)
+    dev = torch.device("cuda", 0)
+    plan = sv.VerifyPlan(8, 5, 30000, torch.bfloat16, mode, device=dev, return_probs=True)
+    for j in range(3):
+        c = verify_case(8, 5, 30000, "bf16", target_std=3.0, zipf_s=1.1, sigma=0.5, temperature=0.8,
+                        key=(33, j), device=dev)
+        greedy = mode == "greedy"
+        got = [t.cpu().numpy() for t in plan(c.target, c.draft, c.draft_tokens, c.uniforms, c.temperature)]
+        ref = sv.spec_verify(c.target, None if greedy else c.draft, c.draft_tokens, None if greedy else c.uniforms,
+                             0.0 if greedy else c.temperature, mode, return_probs=True)
+        for g, r in zip(got, ref):
+            np.testing.assert_array_equal(g, r.cpu().numpy())
+    with pytest.raises(ValueError):
+        plan(c.target[:4], c.draft, c.draft_tokens, c.uniforms, c.temperature)

@@ -365,6 +365,16 @@ spec_status_t spec_kv_commit(void* cache, const void* staging, const int32_t* ac
                              int32_t* cache_len, int32_t* status, int32_t P, int32_t B, int32_t K,
                              int32_t L_max, int32_t E, spec_dtype_t dtype, void* stream);
 
+/*
+ * Measurement aid, not part of the method: reads `bytes` (a multiple of
+ * 32 KiB) of device memory at `src` (16-byte aligned) with the statistics
+ * pass's access pattern (each wave 8 KiB contiguous in 16-byte nontemporal
+ * loads) and no arithmetic, so its rate is the read-only streaming ceiling
+ * the streaming passes compare with.  `sink` is a device int32 that is
+ * written only if the data's XOR equals a fixed constant.  One launch.
+ */
+spec_status_t spec_read_stream_probe(const void* src, size_t bytes, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

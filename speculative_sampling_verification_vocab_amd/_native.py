@@ -69,6 +69,8 @@ def load() -> ctypes.CDLL:
         lib.spec_draft_head_static_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         lib.spec_draft_head_static_workspace_bytes.restype = sz
         lib.spec_draft_head_static.restype = ctypes.c_int
+        lib.spec_read_stream_probe.argtypes = [P, sz, P, P]
+        lib.spec_read_stream_probe.restype = ctypes.c_int
         lib.spec_position_budget.argtypes = [i32, i32]
         lib.spec_position_budget.restype = i32
         lib.spec_kv_commit.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_int, P]

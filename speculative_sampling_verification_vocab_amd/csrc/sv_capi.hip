@@ -277,4 +277,13 @@ spec_status_t spec_kv_commit(void* cache, const void* staging, const int32_t* ac
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
+spec_status_t spec_read_stream_probe(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink || bytes == 0 || bytes % 32768 != 0 || (uintptr_t)src % 16 != 0 || (uintptr_t)sink % 4 != 0)
+    return SPEC_ERR_INVALID_ARG;
+  if (bytes / 32768 > 0x7fffffffu) return SPEC_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  const hipError_t e = sv::launch_read_stream(src, bytes, sink, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
 }  // extern "C"

@@ -39,6 +39,9 @@ hipError_t launch_head_static(const void* h, const void* W, const int32_t* clust
                               int cluster_size, int n_sel, void* out, int out_dtype, float* partial,
                               hipStream_t st);
 
+// Read-only stream of bytes (a multiple of 32 KiB) for the roofline reference.
+hipError_t launch_read_stream(const void* src, size_t bytes, void* sink, hipStream_t st);
+
 // KV-cache commit: copy, then lengths and status (two launches).
 hipError_t launch_kv_commit(void* cache, const void* staging, const int32_t* accepted_len, int32_t* cache_len,
                             int32_t* status, int P, int B, int K, int Lmax, int64_t row_bytes, int elem_bytes,

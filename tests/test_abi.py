@@ -228,3 +228,13 @@ def test_position_budget_matches_the_printed_formula(lib):
     assert [position_budget(t, 16) for t in range(5)] == [16, 16, 2, 2, 1]
     with pytest.raises(ValueError):
         position_budget(-1, 16)
+
+
+def test_read_stream_probe_validation(lib):
+    fake = ctypes.c_void_p(0x10000)
+    f = lib.spec_read_stream_probe
+    assert f(None, 32768, fake, None) == 1
+    assert f(fake, 0, fake, None) == 1
+    assert f(fake, 32768 + 16, fake, None) == 1          # not a multiple of 32 KiB
+    assert f(ctypes.c_void_p(0x10008), 32768, fake, None) == 1   # not 16-byte aligned
+    assert f(fake, 32768, None, None) == 1

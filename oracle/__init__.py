@@ -50,6 +50,8 @@ def _load():
             lib.oracle_verify.restype = ctypes.c_int
             lib.oracle_row_stats.argtypes = [P, ctypes.c_int, i32, i32, ctypes.c_float, P, P]
             lib.oracle_row_stats.restype = ctypes.c_int
+            lib.oracle_overlap.argtypes = [P, P, ctypes.c_int, i32, i32, ctypes.c_float, P]
+            lib.oracle_overlap.restype = ctypes.c_int
             lib.oracle_head.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, P, P, P]
             lib.oracle_head.restype = ctypes.c_int
             lib.oracle_kv_commit.argtypes = [P, P, P, P, P, i32, i32, i32, i32, ctypes.c_int64]
@@ -155,6 +157,33 @@ def row_stats(x, temperature):
     Z = np.empty(R, np.float64)
     lib.oracle_row_stats(_ptr(arr), dt, R, V, float(np.float32(temperature)), _ptr(m), _ptr(Z))
     return m.reshape(arr.shape[:-1]), Z.reshape(arr.shape[:-1])
+
+
+def overlap(target, draft, temperature, threads=1):
+    """beta = sum_v min(P_t(v), P_d(v)) in fp64 per pair of rows: target and
+    draft of the same shape [..., V] (for verify inputs pass target[:, :K])."""
+    lib = _load()
+    ta, dt1 = _as_logits(target)
+    da, dt2 = _as_logits(draft)
+    assert dt1 == dt2 and ta.shape == da.shape
+    V = ta.shape[-1]
+    R = int(np.prod(ta.shape[:-1]))
+    ta = ta.reshape(R, V)
+    da = da.reshape(R, V)
+    beta = np.empty(R, np.float64)
+    T = float(np.float32(temperature))
+
+    def run(r0, r1):
+        if r1 > r0:
+            lib.oracle_overlap(_ptr(ta[r0:r1]), _ptr(da[r0:r1]), dt1, r1 - r0, V, T, _ptr(beta[r0:r1]))
+
+    if threads <= 1 or R <= 1:
+        run(0, R)
+    else:
+        step = (R + threads - 1) // threads
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda r0: run(r0, min(R, r0 + step)), range(0, R, step)))
+    return beta.reshape(target.shape[:-1])
 
 
 def head(h, W, cluster_ids, cluster_size, dense=False, threads=1):

@@ -271,6 +271,35 @@ int oracle_row_stats(const void* x, int dtype, int32_t R, int32_t V, float tempe
 }
 
 /*
+ * Acceptance probability of one position: beta = sum_v min(P_t(v), P_d(v)),
+ * the chance that the draft token drawn from P_d survives the accept test
+ * (RuneLab explainer, the single-position figure: 42/26/16/10/6 against
+ * 20/45/10/5/20 is accepted 67 % of the time; the pages print the value, and
+ * the sum of the overlap is what produces it).  target and draft hold R rows
+ * of V each, paired row by row; beta[r] is NaN for a row without a finite
+ * maximum.
+ */
+int oracle_overlap(const void* target, const void* draft, int dtype, int32_t R, int32_t V, float temperature,
+                   double* beta) {
+  const double T = (double)temperature;
+  for (int32_t r = 0; r < R; ++r) {
+    const size_t row0 = (size_t)r * V;
+    double mt, Zt, md, Zd;
+    row_stats(target, dtype, row0, V, T, &mt, &Zt);
+    row_stats(draft, dtype, row0, V, T, &md, &Zd);
+    if (!row_ok(mt, Zt) || !row_ok(md, Zd)) { beta[r] = NAN; continue; }
+    double s = 0.0;
+    for (int32_t v = 0; v < V; ++v) {
+      const double pt = prob_at(target, dtype, row0, v, mt, Zt, T);
+      const double pd = prob_at(draft, dtype, row0, v, md, Zd, T);
+      s += pt < pd ? pt : pd;
+    }
+    beta[r] = s;
+  }
+  return 0;
+}
+
+/*
  * Shortlisted drafter head (DynaSpec summary, lowest.today: "Model architecture",
  * items 1, 3 and 4): each context b picks n_sel clusters; its shortlist is the
  * union of those clusters, cluster c being the contiguous ids

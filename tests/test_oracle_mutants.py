@@ -50,6 +50,10 @@ MUTANTS = {
     "zero_residual_fallback_uncounted": ("if (fallbacks) fallbacks[b] = 1;", "(void)0;"),
     "probe_interval_without_own_weight": ("const double Cg1 = Cg0 + w[g];", "const double Cg1 = Cg0;"),
     "probe_gap_not_divided_by_mass": ("probe_gap[b] = gap / S;", "probe_gap[b] = gap;"),
+    # acceptance probability of one position
+    "overlap_takes_max": ("s += pt < pd ? pt : pd;", "s += pt > pd ? pt : pd;"),
+    "overlap_draft_normalised_by_target": ("const double pd = prob_at(draft, dtype, row0, v, md, Zd, T);",
+                                           "const double pd = prob_at(draft, dtype, row0, v, md, Zt, T);"),
     "kv_commit_off_by_one": ("(size_t)Lmax + (size_t)(len + j)) * (size_t)row_bytes;",
                              "(size_t)Lmax + (size_t)(len + j + 1)) * (size_t)row_bytes;"),
     "kv_commit_includes_rejected": ("for (int32_t j = 0; j < n; ++j) {", "for (int32_t j = 0; j <= n && j < K; ++j) {"),
@@ -84,6 +88,9 @@ PINS = [
     margin_pins.test_probe_gap_undefined_cases,
     margin_pins.test_zero_residual_falls_back_to_the_target_row,
     margin_pins.test_no_crossing_takes_the_largest_id_of_positive_weight,
+    pins.test_overlap_worked_example_is_the_printed_acceptance,
+    pins.test_overlap_is_one_minus_total_variation,
+    pins.test_overlap_limits,
     kv_pins.test_exercise_prefix_plus_accepted_drafts,
     kv_pins.test_multi_step_cache_holds_the_committed_stream,
     kv_pins.test_status_cases_commit_nothing,
@@ -109,7 +116,7 @@ def test_mutant_is_caught(name, monkeypatch):
     with tempfile.TemporaryDirectory() as tmp:
         so = _build_mutant(name, old, new, tmp)
         lib = ctypes.CDLL(so)
-        for fn in ("oracle_verify", "oracle_row_stats", "oracle_head", "oracle_kv_commit"):
+        for fn in ("oracle_verify", "oracle_row_stats", "oracle_overlap", "oracle_head", "oracle_kv_commit"):
             getattr(lib, fn).argtypes = getattr(real, fn).argtypes
             getattr(lib, fn).restype = getattr(real, fn).restype
         monkeypatch.setattr(oracle, "_lib", lib)

@@ -409,3 +409,44 @@ def test_inverse_cdf_skips_zero_weight_tokens():
     r = oracle.verify(x, y, np.array([[4]], np.int32), uni, 1.0)
     assert r["accepted_len"][0] == 0
     assert r["out_tokens"][0, 0] == 3
+
+
+# --------------------------------------------------------------------------------------
+# Acceptance probability beta = sum_v min(P_t, P_d) of one position.
+# --------------------------------------------------------------------------------------
+
+def test_overlap_worked_example_is_the_printed_acceptance():
+    """RuneLab explainer, single-position figure: the two rows are accepted
+    67 % of the time."""
+    g, pt, pd = _worked()
+    beta = oracle.overlap(_logits_from_probs(pt)[None], _logits_from_probs(pd)[None], 1.0)
+    assert abs(float(beta[0]) - g["printed"]["accept_percent"] / 100) < 1e-6
+
+
+def test_overlap_is_one_minus_total_variation():
+    """sum_v min(p, q) = 1 - (1/2) sum_v |p - q| for two distributions; both
+    sides of the identity from an fp64 softmax of the same float32 logits
+    (scipy), at two temperatures and with a -inf entry in the draft."""
+    rng = np.random.default_rng(7)
+    V = 97
+    t = rng.normal(0.0, 2.0, (6, V)).astype(np.float32)
+    d = (t + rng.normal(0.0, 0.8, (6, V))).astype(np.float32)
+    d[2, 5] = -np.inf
+    for T in (1.0, 0.6):
+        beta = oracle.overlap(t, d, T)
+        p = scipy.special.softmax(t.astype(np.float64) / np.float64(np.float32(T)), axis=-1)
+        q = scipy.special.softmax(d.astype(np.float64) / np.float64(np.float32(T)), axis=-1)
+        want = 1.0 - 0.5 * np.abs(p - q).sum(-1)
+        np.testing.assert_allclose(beta, want, rtol=0, atol=1e-12)
+        assert np.all((beta > 0) & (beta < 1))
+
+
+def test_overlap_limits():
+    """Identical rows overlap fully; rows with disjoint supports not at all;
+    a row with no finite logit has no beta."""
+    x = np.array([[0.3, -1.0, 2.0, -np.inf]], np.float32)
+    assert abs(float(oracle.overlap(x, x, 1.3)[0]) - 1.0) < 1e-12
+    a = np.array([[0.0, 1.0, -np.inf, -np.inf]], np.float32)
+    b = np.array([[-np.inf, -np.inf, 0.5, 2.0]], np.float32)
+    assert float(oracle.overlap(a, b, 1.0)[0]) == 0.0
+    assert np.isnan(oracle.overlap(np.full((1, 4), -np.inf, np.float32), a, 1.0)[0])

@@ -108,6 +108,31 @@ def cpu_baseline(case, res, args, K):
         wall += time.perf_counter() - t1
         reps += 1
     agree = int(np.sum(orc["accepted_len"] == res[0][sl].cpu().numpy()))
+    # The same sample, untimed: decision-level agreement with the GPU outputs
+    # (the tie accounting of the parity tests) and, in sample mode, the
+    # per-position acceptance probabilities beta = sum_v min(P_t, P_d).
+    from tests.parity_util import compare, probe_tokens
+    g_len, g_out = res[0][sl].cpu().numpy(), res[1][sl].cpu().numpy()
+    orc_p = oracle.verify(tgt_h, dr_h, tok_h, uni_h, case.temperature, mode=mode, threads=threads,
+                          probe_token=None if greedy else probe_tokens(g_len, g_out))
+    rep = compare(g_len, g_out, orc_p, K, greedy=greedy)
+    parity = {"sequences": nb, "decisions": rep.decisions, "disagreements": rep.excused + len(rep.failures),
+              "excused_ties": rep.excused, "failures": len(rep.failures),
+              "rule": "a disagreement is excused only within 1e-6 of the oracle's decision boundary"}
+    beta = None
+    if not greedy and K > 0:
+        b = oracle.overlap(tgt_h[:, :K].contiguous(), dr_h, case.temperature, threads=threads)
+        prod = np.ones(nb)
+        expect = np.zeros(nb)
+        for i in range(K + 1):
+            expect += prod
+            if i < K:
+                prod = prod * b[:, i]
+        a = float(np.mean(b))
+        beta = {"alpha_mean_beta": a, "expected_tokens_per_verify_exact": float(np.mean(expect)),
+                "closed_form_tokens_at_mean_beta": (1 - a ** (K + 1)) / (1 - a) if a < 1 else float(K + 1),
+                "observed_mean_tokens_per_verify": float(np.mean(g_len[g_len >= 0] + 1)),
+                "sample": f"first {nb} sequences, fp64 oracle"}
     # one thread on a smaller slice of the same sample, for the per-core rate
     n1 = max(1, min(nb, 16))
     t1 = time.perf_counter()
@@ -118,7 +143,26 @@ def cpu_baseline(case, res, args, K):
             "single_thread_value": n1 * (K + 1) / w1,
             "sample": f"first {nb} of {B} sequences of the same batch x {reps} repetitions, fp64 C oracle, "
                       f"{threads} threads, {wall:.2f} s wall; accepted_len agrees on {agree}/{nb}; "
-                      f"single thread: first {n1} sequences once, {w1:.2f} s"}
+                      f"single thread: first {n1} sequences once, {w1:.2f} s",
+            "parity_sample": parity, "acceptance_sample": beta}
+
+
+def acceptance_report(n, K):
+    """Acceptance from the GPU outputs of one step: alpha = accepted drafts /
+    accept tests taken (a sequence that accepted n drafts took min(n + 1, K)
+    tests), the mean tokens emitted per verify, and the closed form
+    (1 - alpha^(K+1)) / (1 - alpha) for i.i.d. acceptance at that alpha."""
+    import numpy as np
+    n = np.asarray(n)
+    n = n[n >= 0].astype(np.int64)
+    tests = int(np.minimum(n + 1, K).sum()) if K > 0 else 0
+    alpha = float(n.sum()) / tests if tests else float("nan")
+    closed = None
+    if tests:
+        closed = (1 - alpha ** (K + 1)) / (1 - alpha) if alpha < 1 else float(K + 1)
+    return {"alpha_observed": alpha, "accept_tests": tests, "accepted_drafts": int(n.sum()),
+            "mean_tokens_per_verify": float(np.mean(n + 1)) if n.size else float("nan"),
+            "closed_form_tokens_at_alpha_observed": closed}
 
 
 def copy_reference(dev, gib=1.0, reps=5):
@@ -454,6 +498,7 @@ def main():
         "hbm_frac_step": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernels_ms": k_ms,
         "mean_tokens_per_verify": mean_tokens,
+        "acceptance": acceptance_report(res[0].cpu().numpy(), K),
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": dom_bytes,
@@ -548,6 +593,7 @@ def bench_shortlist(args, dev):
                    "cluster_size": cs, "n_sel": n_sel, "selected_clusters_union": sel, "temperature": 1.0},
         "kernels_ms": k_ms,
         "mean_tokens_per_verify": float((acc[acc >= 0] + 1).mean()),
+        "acceptance": acceptance_report(res[0].cpu().numpy(), K),
         "roofline": {"bound": "hbm", "kernel": "head_mfma_kernel (shortlist gather-GEMM)", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic_from_profile(HEAD_PROFILE_PMC, HEAD_SOURCES),

@@ -103,3 +103,16 @@ def test_profile_figures_are_used_only_for_the_source_they_were_taken_on(tmp_pat
     assert bench.profile_value(str(tmp_path / "absent.md"), "hbm_bytes_per_launch", [str(src)]) is None
     src.write_text("__global__ void k() { /* changed */ }\n")
     assert bench.profile_value(str(summary), "hbm_bytes_per_launch", [str(src)]) is None
+
+
+def test_acceptance_report_counts_the_tests_taken():
+    """alpha = accepted drafts / accept tests taken: a sequence that accepted n
+    of K drafts took min(n + 1, K) tests; faulty sequences (-1) are left out."""
+    import bench
+    r = bench.acceptance_report(np.array([0, 4, 2, -1]), 4)
+    assert r["accepted_drafts"] == 6 and r["accept_tests"] == 1 + 4 + 3
+    assert r["alpha_observed"] == 6 / 8
+    assert r["mean_tokens_per_verify"] == (1 + 5 + 3) / 3
+    a = 0.75
+    assert abs(r["closed_form_tokens_at_alpha_observed"] - (1 - a ** 5) / (1 - a)) < 1e-12
+    assert bench.acceptance_report(np.array([3, 3]), 3)["closed_form_tokens_at_alpha_observed"] == 4.0

@@ -17,8 +17,15 @@ Prints ONE JSON line on stdout:
              steps, against MI355X's 8 TB/s HBM peak; `traffic` is HBM bytes
              per launch from the rocprofv3 PMC summary in profiles/ when that
              summary matches the current kernel source, else null.
+             Beside the peak: the measured rate of a read-only stream of the
+             same loads (spec_read_stream_probe) and of a device copy.
+  acceptance alpha observed (accepted drafts / accept tests taken), mean
+             tokens per verify and the closed form at that alpha.
   cpu_baseline  the fp64 oracle timed on this host's cores on a sample of the
-             same batch (it is a baseline, not a target).
+             same batch (it is a baseline, not a target); untimed on the same
+             sample: mean beta = sum_v min(P_t, P_d) with the exact expected
+             tokens per verify, and a decision-level comparison of the GPU
+             outputs with the oracle (disagreements, excused ties, failures).
   early_exit the position-by-position schedule on the same batch (identical
              outputs; rows after each sequence's first rejection not read).
   kv_commit  the KV-cache commit of that batch's accepted drafts on a

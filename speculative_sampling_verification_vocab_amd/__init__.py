@@ -37,9 +37,11 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _need_gpu(t: torch.Tensor, name: str):
+def _need_gpu(t: torch.Tensor, name: str, device: Optional[torch.device] = None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, the device of the call's first tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
@@ -75,7 +77,9 @@ class Workspace:
         self.buf = torch.empty(0, dtype=torch.uint8, device=self.device)
         self._stream = None
 
-    def get(self, nbytes: int, stream=None) -> torch.Tensor:
+    def get(self, nbytes: int, stream=None, device=None) -> torch.Tensor:
+        if device is not None and torch.device(device) != self.device:
+            raise ValueError(f"this workspace is on {self.device}, the call on {device}")
         s = _stream_of(self.device, stream)
         if self.buf.numel() < nbytes:
             with torch.cuda.stream(s):
@@ -123,7 +127,7 @@ def spec_verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_token
     pt = torch.empty((B, K), dtype=torch.float32, device=dev) if return_probs else None
     pd = torch.empty((B, K), dtype=torch.float32, device=dev) if return_probs else None
     need = lib.spec_verify_workspace_bytes(B, K, V, dt, _MODES[mode])
-    ws = (workspace or _workspace_for(dev, stream)).get(need, stream)
+    ws = (workspace or _workspace_for(dev, stream)).get(need, stream, dev)
     args = [_ptr(target), _ptr(draft) if sampling else None,
             _ptr(draft_tokens) if K > 0 else None, _ptr(uniforms) if sampling else None,
             B, K, V, dt, ctypes.c_float(temperature if sampling else 0.0), _MODES[mode],
@@ -148,7 +152,9 @@ class VerifyPlan:
     call (no allocation).  Each call returns the same output tensors,
     overwritten in place: copy them before the next call if they must be kept.
     Inputs must have the shapes and dtype the plan was made for (checked) and
-    be contiguous GPU tensors."""
+    be contiguous tensors on the plan's device.  Calls run on the stream the
+    plan was made for (`stream`, else the current stream at that time), and
+    calls that overlap in time on one plan race on its workspace and outputs."""
 
     def __init__(self, B: int, K: int, V: int, dtype: torch.dtype = torch.bfloat16, mode: str = "sample", *,
                  device="cuda", stream=None, return_probs: bool = False):
@@ -160,6 +166,7 @@ class VerifyPlan:
         if dev.index is None:
             dev = torch.device(dev.type, torch.cuda.current_device())
         self.B, self.K, self.V, self.dtype, self.mode = int(B), int(K), int(V), dtype, mode
+        self.device = dev
         self._sampling = mode in _SAMPLING
         lib = _native.load()
         self._lib = lib
@@ -181,8 +188,8 @@ class VerifyPlan:
         self._out = (self.accepted_len, self.out_tokens) + ((self.p_target, self.p_draft) if return_probs else ())
 
     def _arg(self, t, shape, dtype, name):
-        if t.shape != shape or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous GPU tensor {dtype} {list(shape)}")
+        if t.shape != shape or t.dtype != dtype or t.device != self.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dtype} {list(shape)} tensor on {self.device}")
         return t.data_ptr()
 
     def __call__(self, target, draft, draft_tokens, uniforms, temperature: float = 1.0, events=None):
@@ -224,19 +231,19 @@ def _check_verify_inputs(target, draft, draft_tokens, uniforms, mode):
     if sampling and K > 0:
         if draft is None:
             raise ValueError("draft logits are required in sample mode")
-        _need_gpu(draft, "draft")
+        _need_gpu(draft, "draft", target.device)
         if draft.dtype != target.dtype or tuple(draft.shape) != (B, K, V):
             raise ValueError("draft must match target dtype and be [B, K, V]")
     if K > 0:
         if draft_tokens is None:
             raise ValueError("draft_tokens are required when K > 0")
-        _need_gpu(draft_tokens, "draft_tokens")
+        _need_gpu(draft_tokens, "draft_tokens", target.device)
         if draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != (B, K):
             raise ValueError("draft_tokens must be int32 [B, K]")
     if sampling:
         if uniforms is None:
             raise ValueError("uniforms are required in sample mode")
-        _need_gpu(uniforms, "uniforms")
+        _need_gpu(uniforms, "uniforms", target.device)
         if uniforms.dtype != torch.float32 or tuple(uniforms.shape) != (B, K + 1, 2):
             raise ValueError("uniforms must be float32 [B, K+1, 2]")
     return B, K, V, dt, sampling
@@ -255,7 +262,7 @@ def spec_verify_noalloc(target: torch.Tensor, draft: Optional[torch.Tensor], dra
         raise ValueError("out must hold 2 or 4 tensors")
     want = [((B,), torch.int32), ((B, K + 1), torch.int32), ((B, K), torch.float32), ((B, K), torch.float32)]
     for t, (shape, dtype) in zip(out, want):
-        _need_gpu(t, "out")
+        _need_gpu(t, "out", target.device)
         if tuple(t.shape) != shape or t.dtype != dtype:
             raise ValueError(f"out tensor must be {dtype} {list(shape)}")
     pt, pd = (out[2], out[3]) if len(out) == 4 else (None, None)
@@ -274,7 +281,7 @@ def spec_draft_head_shortlist(h: torch.Tensor, W: torch.Tensor, cluster_ids: tor
     (ascending).  Returns (compact float32 [B, K, n_sel*cluster_size] or None,
     dense [B, K, V] of dense_dtype with -inf off the shortlist, or None)."""
     for t, name in ((h, "h"), (W, "W"), (cluster_ids, "cluster_ids")):
-        _need_gpu(t, name)
+        _need_gpu(t, name, h.device)
     if h.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
         raise ValueError("h and W must be bfloat16")
     if cluster_ids.dtype != torch.int32:
@@ -304,7 +311,7 @@ def spec_kv_commit(cache: torch.Tensor, staging: torch.Tensor, accepted_len: tor
     spec_verify; cache_len int32 [B], advanced in place.  Returns the status
     tensor (int32 [B]: 0 committed, 1 no room, 2 accepted_len outside [0, K])."""
     for t, name in ((cache, "cache"), (staging, "staging"), (accepted_len, "accepted_len"), (cache_len, "cache_len")):
-        _need_gpu(t, name)
+        _need_gpu(t, name, cache.device)
     dt = _DTYPES.get(cache.dtype)
     if dt is None or staging.dtype != cache.dtype:
         raise ValueError("cache and staging must both be bfloat16 or both float32")
@@ -323,6 +330,10 @@ def spec_kv_commit(cache: torch.Tensor, staging: torch.Tensor, accepted_len: tor
             raise ValueError(f"{name} must be contiguous int32 [B]")
     if status is None:
         status = torch.empty(B, dtype=torch.int32, device=cache.device)
+    else:
+        _need_gpu(status, "status", cache.device)
+        if status.dtype != torch.int32 or tuple(status.shape) != (B,):
+            raise ValueError("status must be contiguous int32 [B]")
     st = _native.load().spec_kv_commit(_ptr(cache), _ptr(staging), _ptr(accepted_len), _ptr(cache_len),
                                        _ptr(status), P, B, K, Lmax, E, dt, _stream_handle(cache.device, stream))
     _native.check(st, "spec_kv_commit")
@@ -362,7 +373,7 @@ def spec_verify_sparse_draft(target: torch.Tensor, draft_compact: torch.Tensor, 
     if K > 0:
         for t, name in ((draft_compact, "draft_compact"), (cluster_ids, "cluster_ids"),
                         (draft_tokens, "draft_tokens")):
-            _need_gpu(t, name)
+            _need_gpu(t, name, target.device)
         if draft_compact.dtype != target.dtype or draft_compact.dim() != 3 or draft_compact.shape[:2] != (B, K):
             raise ValueError("draft_compact must be [B, K, L] with the target's dtype")
         if cluster_ids.dtype != torch.int32 or cluster_ids.dim() != 3 or cluster_ids.shape[:2] != (B, K):
@@ -371,7 +382,7 @@ def spec_verify_sparse_draft(target: torch.Tensor, draft_compact: torch.Tensor, 
             raise ValueError("draft_tokens must be int32 [B, K]")
         L, S = draft_compact.shape[2], cluster_ids.shape[2]
         draft_compact, cluster_ids = draft_compact.contiguous(), cluster_ids.contiguous()
-    _need_gpu(uniforms, "uniforms")
+    _need_gpu(uniforms, "uniforms", target.device)
     if uniforms.dtype != torch.float32 or tuple(uniforms.shape) != (B, K + 1, 2):
         raise ValueError("uniforms must be float32 [B, K+1, 2]")
     lib = _native.load()
@@ -381,7 +392,7 @@ def spec_verify_sparse_draft(target: torch.Tensor, draft_compact: torch.Tensor, 
     pt = torch.empty((B, K), dtype=torch.float32, device=dev) if return_probs else None
     pd = torch.empty((B, K), dtype=torch.float32, device=dev) if return_probs else None
     need = lib.spec_verify_workspace_bytes(B, K, V, dt, _MODES["sample"])
-    ws = (workspace or _workspace_for(dev, stream)).get(need, stream)
+    ws = (workspace or _workspace_for(dev, stream)).get(need, stream, dev)
     st = lib.spec_verify_sparse_draft(_ptr(target), _ptr(draft_compact) if K > 0 else None,
                                       _ptr(cluster_ids) if K > 0 else None, ns, L, S, int(cluster_size),
                                       _ptr(draft_tokens) if K > 0 else None, _ptr(uniforms), B, K, V, dt,
@@ -401,7 +412,7 @@ def spec_draft_head_positions(h: torch.Tensor, W: torch.Tensor, cluster_ids: tor
     [B, K, L] of `dtype` (L defaults to S * cluster_size), the input that
     spec_verify_sparse_draft takes."""
     for t, name in ((h, "h"), (W, "W"), (cluster_ids, "cluster_ids")):
-        _need_gpu(t, name)
+        _need_gpu(t, name, h.device)
     if h.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
         raise ValueError("h and W must be bfloat16")
     B, K, d = h.shape
@@ -417,8 +428,9 @@ def spec_draft_head_positions(h: torch.Tensor, W: torch.Tensor, cluster_ids: tor
         raise ValueError("dtype must be bfloat16 or float32")
     if out is None:
         out = torch.empty((B, K, L), dtype=dtype, device=h.device)
-    elif out.dtype != dtype or tuple(out.shape) != (B, K, L) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B, K, L] tensor of dtype")
+    elif out.dtype != dtype or tuple(out.shape) != (B, K, L) or not out.is_contiguous() \
+            or out.device != h.device:
+        raise ValueError("out must be on h's device, a contiguous [B, K, L] tensor of dtype")
     ns = (ctypes.c_int32 * max(1, K))(*[int(x) for x in n_sel])
     st = _native.load().spec_draft_head_positions(_ptr(h.contiguous()), _ptr(W.contiguous()),
                                                   _ptr(cluster_ids.contiguous()), ns, B, K, d, V,
@@ -438,7 +450,7 @@ def spec_draft_head_static(h: torch.Tensor, W: torch.Tensor, cluster_ids: torch.
     shortlists split d over blocks through a workspace (the stream's default
     one unless given); split=False runs the single-launch kernel."""
     for t, name in ((h, "h"), (W, "W"), (cluster_ids, "cluster_ids")):
-        _need_gpu(t, name)
+        _need_gpu(t, name, h.device)
     if h.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
         raise ValueError("h and W must be bfloat16")
     if cluster_ids.dtype != torch.int32 or cluster_ids.dim() != 1:
@@ -453,14 +465,15 @@ def spec_draft_head_static(h: torch.Tensor, W: torch.Tensor, cluster_ids: torch.
     shape = tuple(h.shape[:-1]) + (N,)
     if out is None:
         out = torch.empty(shape, dtype=dtype, device=h.device)
-    elif out.dtype != dtype or tuple(out.shape) != shape or not out.is_contiguous():
-        raise ValueError("out must be contiguous with shape h.shape[:-1] + (N,) and dtype")
+    elif out.dtype != dtype or tuple(out.shape) != shape or not out.is_contiguous() \
+            or out.device != h.device:
+        raise ValueError("out must be on h's device, contiguous with shape h.shape[:-1] + (N,) and dtype")
     lib = _native.load()
     ws, wsb = None, 0
     need = lib.spec_draft_head_static_workspace_bytes(M, d, V, int(cluster_size), cluster_ids.numel()) \
         if split and M > 0 and cluster_ids.numel() > 0 else 0
     if need:
-        buf = (workspace or _workspace_for(h.device, stream)).get(need, stream)
+        buf = (workspace or _workspace_for(h.device, stream)).get(need, stream, h.device)
         ws, wsb = _ptr(buf), buf.numel()
     st = lib.spec_draft_head_static(_ptr(h.contiguous()), _ptr(W.contiguous()),
                                     _ptr(cluster_ids.contiguous()), M, d, V, int(cluster_size),

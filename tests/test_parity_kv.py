@@ -103,3 +103,21 @@ def test_verify_then_commit():
     np.testing.assert_array_equal(ln.cpu().numpy(), exp[1])
     np.testing.assert_array_equal(st.cpu().numpy(), exp[2])
     assert np.all(exp[2] == 0)
+
+
+def test_caller_status_tensor_is_checked():
+    """A caller-supplied status tensor must be int32 [B] on the cache's device
+    (the kernel writes B entries into it)."""
+    import speculative_sampling_verification_vocab_amd as sv
+    dev = torch.device("cuda", 0)
+    cache = torch.zeros(2, 3, 10, 8, dtype=torch.bfloat16, device=dev)
+    staging = torch.zeros(2, 3, 2, 8, dtype=torch.bfloat16, device=dev)
+    n = torch.tensor([0, 1, 2], dtype=torch.int32, device=dev)
+    ln = torch.tensor([1, 2, 3], dtype=torch.int32, device=dev)
+    for bad in (torch.zeros(2, dtype=torch.int32, device=dev), torch.zeros(3, dtype=torch.int64, device=dev),
+                torch.zeros(3, dtype=torch.int32)):
+        with pytest.raises(ValueError):
+            sv.spec_kv_commit(cache, staging, n, ln, bad)
+    good = torch.full((3,), 7, dtype=torch.int32, device=dev)
+    assert sv.spec_kv_commit(cache, staging, n, ln, good) is good
+    assert good.tolist() == [0, 0, 0] and ln.tolist() == [1, 3, 5]

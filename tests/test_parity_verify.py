@@ -320,3 +320,5 @@ def test_verify_plan_matches_spec_verify(mode):
             np.testing.assert_array_equal(g, r.cpu().numpy())
     with pytest.raises(ValueError):
         plan(c.target[:4], c.draft, c.draft_tokens, c.uniforms, c.temperature)
+    with pytest.raises(ValueError):  # not on the plan's device
+        plan(c.target.cpu(), c.draft, c.draft_tokens, c.uniforms, c.temperature)

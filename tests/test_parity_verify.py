@@ -269,6 +269,69 @@ def test_offsets_past_4_gib():
         assert rep.prob_max_rel < 1e-5
 
 
+def test_largest_vocabulary():
+    """V = 2^30, the largest vocabulary the library takes (B=1, K=2, bf16: 10
+    GiB of logits).  Every logit is -inf except at a few ids spread over the
+    row, including the last ones, so the rule's outcome depends only on those
+    ids: the oracle runs on the rows compressed to them (same order, so the
+    inverse CDF over token ids is the same) and its ids are mapped back.  The
+    GPU reads the full rows in SAMPLE, SAMPLE_EARLY_EXIT and GREEDY."""
+    import speculative_sampling_verification_vocab_amd as sv
+    print("case largest vocabulary: B=1 K=2 V=2^30 bf16", flush=True)
+    dev = torch.device("cuda", 0)
+    B, K, V = 1, 2, 1 << 30
+    ids = np.array([0, 5, 4095, 4096, (1 << 29) + 7, V - 4097, V - 9, V - 2, V - 1], np.int64)
+    rng = np.random.default_rng(30)
+    lt = rng.normal(0.0, 1.5, (K + 1, ids.size)).astype(np.float32)
+    ld = (lt[:K] + rng.normal(0.0, 1.0, (K, ids.size))).astype(np.float32)
+    ld[0, 1] = -np.inf   # a target token the draft never proposes
+    lt[1, 6] = -np.inf   # a draft token the target rules out
+    ld[0, 7] = lt[0, 7] + 3.0  # the draft overweights its first token
+    lt_b = torch.from_numpy(lt).to(torch.bfloat16)
+    ld_b = torch.from_numpy(ld).to(torch.bfloat16)
+    tok_i = np.array([[7, 6]], np.int32)            # indices into ids: V - 2, then V - 9
+
+    def prob(row, i):
+        x = row.float().numpy().astype(np.float64)
+        return float(np.exp(x[i] - x.max()) / np.exp(x - x.max()).sum())
+
+    ratio = prob(lt_b[0], 7) / prob(ld_b[0], 7)
+    assert ratio < 0.9
+    for u_acc in (0.5 * ratio, 0.5 * (1.0 + ratio)):  # accept position 0, then reject it
+        uni = np.full((B, K + 1, 2), 0.5, np.float32)
+        uni[0, 0, 0] = u_acc
+        uni[0, :, 1] = [0.61, 0.37, 0.83]
+        target = torch.full((B, K + 1, V), float("-inf"), dtype=torch.bfloat16, device=dev)
+        draft = torch.full((B, K, V), float("-inf"), dtype=torch.bfloat16, device=dev)
+        idx = torch.from_numpy(ids).to(dev)
+        target[0][:, idx] = lt_b.to(dev)
+        draft[0][:, idx] = ld_b.to(dev)
+        tok = torch.from_numpy(ids[tok_i].astype(np.int32)).to(dev)
+        uni_d = torch.from_numpy(uni).to(dev)
+        outs = {}
+        for m in ("sample", "sample_early_exit", "greedy"):
+            res = sv.spec_verify(target, draft, tok, uni_d, 1.0 if m != "greedy" else 0.0, m, return_probs=True)
+            torch.cuda.synchronize()
+            outs[m] = [r.cpu().numpy() for r in res]
+        del target, draft
+        torch.cuda.empty_cache()
+        np.testing.assert_array_equal(outs["sample_early_exit"][0], outs["sample"][0])
+        np.testing.assert_array_equal(outs["sample_early_exit"][1], outs["sample"][1])
+        small = VerifyCase(lt_b[None], ld_b[None], torch.from_numpy(tok_i), torch.from_numpy(uni), 1.0, "bf16")
+        for m in ("sample", "greedy"):
+            o = outs[m]
+            # GPU ids back to indices into `ids` (-1 stays -1)
+            pos = {int(v): i for i, v in enumerate(ids)}
+            o_idx = np.vectorize(lambda v: pos.get(int(v), -2) if v >= 0 else -1)(o[1]).astype(np.int32)
+            assert np.all(o_idx >= -1), o[1]
+            greedy = m == "greedy"
+            rep = compare(o[0], o_idx, run_oracle(small, m, gpu=(o[0], o_idx)), K, greedy=greedy,
+                          gpu_pt=None if greedy else o[2], gpu_pd=None if greedy else o[3])
+            assert not rep.failures, (u_acc, m, rep.failures)
+            assert rep.prob_max_rel < 1e-5
+        assert (outs["sample"][0][0] == 0) == (u_acc > ratio)
+
+
 def test_concurrent_streams_use_separate_default_workspaces():
     """Two calls on two streams at once, without explicit workspaces: each
     stream gets its own default scratch, so both match their single-stream

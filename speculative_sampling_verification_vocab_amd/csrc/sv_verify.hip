@@ -205,9 +205,10 @@ __device__ __forceinline__ void sparse_tile_load(const VerifyArgs& a, int b, int
 
 // (tile max, tile sum) of one statistics tile.  Each exponent is one FMA,
 // x*s - c with c = RN(ml*s): exact before its single rounding, like
-// RN((x - ml)*s).  The constant offset delta = ml*s - c (exact by FMA) is
-// put back once per lane, in the factor that scales the lane sum to the tile
-// maximum.
+// RN((x - ml)*s), but offset by delta = ml*s - c (exact by FMA), since
+// x*s - c = (x - ml)*s + delta.  The offset is taken out once per lane, in
+// the factor 2^((ml - M)*s - delta) that scales the lane sum to the tile
+// maximum M.
 template <typename T>
 __device__ __forceinline__ void stats_tile(const VerifyArgs& a, const float (&x)[kPerLane<T>], TileStat* out) {
 #pragma clang fp contract(off)
@@ -221,7 +222,7 @@ __device__ __forceinline__ void stats_tile(const VerifyArgs& a, const float (&x)
     for (int e = 0; e < kPerLane<T>; ++e) sl += exp2_fast(__builtin_fmaf(x[e], a.s_hi, -c));
   }
   const float M = wave_max(ml);
-  const float scaled = ml == kNegInf ? 0.0f : sl * exp2_fast((ml - M) * a.s_hi + delta);
+  const float scaled = ml == kNegInf ? 0.0f : sl * exp2_fast((ml - M) * a.s_hi - delta);
   const float S = wave_sum(scaled);
   if (lane == 0) *out = TileStat{M, S};
 }

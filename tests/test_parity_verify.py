@@ -29,11 +29,22 @@ def test_sample_shapes(dtype, V):
     assert rep.excused <= 1
 
 
-@pytest.mark.parametrize("T", [0.37, 0.8, 2.5])
+@pytest.mark.parametrize("T", [0.02, 0.37, 0.8, 2.5, 50.0])
 def test_sample_temperatures(T):
     print(f"case T={T}", flush=True)
     c = _case(8, 4, 12345 * 8, "bf16", T=T, key=(12, int(T * 100)))
     check_case(c)
+
+
+def test_sample_large_logit_magnitudes():
+    """Logits shifted by +3000 and -3000 (fp32): the softmax does not change,
+    but x*s is large, so the exponents' reference offsets (RN(m*s) and its
+    exact remainder) are large and must be taken out exactly."""
+    for shift in (3000.0, -3000.0):
+        print(f"case logits shifted by {shift}", flush=True)
+        c = _case(8, 4, 20000, "f32", key=(18, 0 if shift > 0 else 1))
+        c = VerifyCase(c.target + shift, c.draft + shift, c.draft_tokens, c.uniforms, c.temperature, c.dtype)
+        check_case(c)
 
 
 def test_sample_k0_only_bonus():

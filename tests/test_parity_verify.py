@@ -78,6 +78,47 @@ def test_faulty_sequences():
     assert out[0][0] >= 0 and out[0][5] >= 0
 
 
+def test_nan_logits_mark_the_sequence_faulty():
+    """A NaN in a row the rule reads leaves that row without a finite
+    normaliser: the sequence is faulty on both sides, as for a row without a
+    finite maximum.  bf16 and fp32; a NaN in target and in draft rows, and a
+    NaN in the bonus row (read only when every draft is accepted)."""
+    for dtype in ("bf16", "f32"):
+        print(f"case NaN logits {dtype}", flush=True)
+        c = _case(6, 3, 8192, dtype, sigma=0.05, key=(19,))
+        c.target[1, 0, 17] = float("nan")
+        c.draft[2, 2, 8000] = float("nan")
+        c.target[3, 3, 5] = float("nan")     # bonus row
+        rep, out, orc = check_case(c)
+        for b in (1, 2):
+            assert out[0][b] == -1 and np.all(out[1][b] == -1)
+        # greedy ignores a single NaN (it is never the maximum) on both sides
+        g = VerifyCase(c.target, None, c.draft_tokens, c.uniforms, 0.0, c.dtype)
+        check_case(g, mode="greedy")
+
+
+def test_constant_rows():
+    """Every logit of every row equal: P_t = P_d = 1/V, every draft accepted
+    (ratio exactly 1), and the bonus token is the inverse CDF of a uniform
+    distribution, a boundary case for every u on the 1/V grid."""
+    for dtype, V in (("bf16", 1000), ("f32", 12288)):
+        print(f"case constant rows {dtype} V={V}", flush=True)
+        c = _case(8, 3, V, dtype, key=(20,))
+        c = VerifyCase(torch.full_like(c.target, 0.75), torch.full_like(c.draft, 0.75), c.draft_tokens,
+                       c.uniforms, c.temperature, c.dtype)
+        rep, out, orc = check_case(c)
+        assert np.all(out[0] == 3)
+
+
+def test_near_one_hot_rows():
+    """fp32 logits scaled by 1e4: every row is one-hot to within fp64, so
+    almost every probability underflows to exactly zero on both sides."""
+    print("case near one-hot rows", flush=True)
+    c = _case(8, 4, 9000, "f32", key=(21,))
+    c = VerifyCase(c.target * 1e4, c.draft * 1e4, c.draft_tokens, c.uniforms, c.temperature, c.dtype)
+    check_case(c)
+
+
 def test_faulty_bonus_row_only_matters_when_sampled():
     c = _case(4, 2, 4096, "bf16", sigma=0.0, key=(17,))
     c.target[0, 2, :] = float("-inf")    # bonus row of sequence 0; all drafts accepted

@@ -56,6 +56,25 @@ class Report:
 # every sampling comparison of the session adds to this
 SESSION = Report()
 
+# The probabilities are fp32 outputs: below the smallest normal fp32 (2^-126)
+# they cannot carry PROB_RTOL relative precision (subnormals hold fewer bits,
+# and values under 2^-149 are zero).  There both sides must be below 2^-126;
+# above it the error is relative.
+FLT_MIN = 2.0 ** -126
+
+
+def prob_rel_error(gpu, orc) -> float:
+    """Largest relative error of GPU probabilities against the oracle's, with
+    values where both sides lie below FLT_MIN counted as equal (and a GPU
+    value at or above FLT_MIN where the oracle's is below counted as 1)."""
+    g = np.asarray(gpu, np.float64)
+    o = np.asarray(orc, np.float64)
+    tiny_o = np.abs(o) < FLT_MIN
+    bad_tiny = tiny_o & (np.abs(g) >= FLT_MIN)
+    rel = np.abs(g[~tiny_o] - o[~tiny_o]) / np.abs(o[~tiny_o])
+    worst = float(np.max(rel)) if rel.size else 0.0
+    return max(worst, 1.0 if bad_tiny.any() else 0.0)
+
 
 def decisions_taken(orc_len, K):
     """Accept decisions up to and including the first rejection, plus the sample."""
@@ -120,9 +139,7 @@ def compare(gpu_len, gpu_out, orc, K, greedy=False, gpu_pt=None, gpu_pd=None, se
                 rep.failures.append(("probability NaN pattern differs", key))
                 continue
             if ok.any():
-                denom = np.maximum(np.abs(o[ok]), 1e-300)
-                rel = float(np.max(np.abs(g[ok] - o[ok]) / denom))
-                rep.prob_max_rel = max(rep.prob_max_rel, rel)
+                rep.prob_max_rel = max(rep.prob_max_rel, prob_rel_error(g[ok], o[ok]))
     return rep
 
 

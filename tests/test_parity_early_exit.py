@@ -72,7 +72,7 @@ def test_early_exit_shapes(B, K, V, dtype):
     check_early_exit(_case(B, K, V, dtype, key=(31, V, K)))
 
 
-@pytest.mark.parametrize("sigma,T", [(0.0, 1.0), (4.0, 1.0), (0.7, 0.37), (0.7, 2.5)])
+@pytest.mark.parametrize("sigma,T", [(0.0, 1.0), (4.0, 1.0), (0.7, 0.37), (0.7, 2.5), (0.7, 0.02), (0.7, 50.0)])
 def test_early_exit_acceptance_regimes(sigma, T):
     """Identical draft (all accepted), low acceptance, and two temperatures."""
     print(f"case sigma={sigma} T={T}", flush=True)
@@ -80,6 +80,16 @@ def test_early_exit_acceptance_regimes(sigma, T):
     out = check_early_exit(c)
     if sigma == 0.0:
         assert np.all(out[0] == 6)
+
+
+def test_early_exit_large_logit_magnitudes():
+    """fp32 logits shifted by +3000: large exponent reference offsets in the
+    per-position statistics and decisions."""
+    from workloads import VerifyCase
+    print("case early exit, logits shifted by 3000", flush=True)
+    c = _case(8, 4, 20000, "f32", key=(37,))
+    check_early_exit(VerifyCase(c.target + 3000.0, c.draft + 3000.0, c.draft_tokens, c.uniforms, c.temperature,
+                                c.dtype))
 
 
 def test_early_exit_shortlist_rows_and_boundary_uniforms():

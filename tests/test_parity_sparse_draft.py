@@ -62,6 +62,14 @@ def test_sparse_position_budget(sigma):
     check_sparse(c)
 
 
+@pytest.mark.parametrize("T", [0.02, 50.0])
+def test_sparse_extreme_temperatures(T):
+    """Near-greedy and near-uniform temperatures on compact draft rows, whose
+    exponent reference is the draft row maximum."""
+    print(f"case sparse T={T}", flush=True)
+    check_sparse(sparse_draft_case(6, 3, 8192, 64, [8, 4, 2], "bf16", temperature=T, key=(53, int(T * 100))))
+
+
 def test_draft_token_off_the_shortlist_is_accepted():
     c = sparse_draft_case(4, 3, 8192, 64, [4, 4, 4], "bf16", key=(53,))
     # token 0 of sequence 0 moved off position 0's shortlist: P_d = 0 there

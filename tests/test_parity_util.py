@@ -98,3 +98,15 @@ def test_decisions_taken():
 def test_probe_tokens():
     pt = probe_tokens(np.array([0, 2, -1]), np.array([[5, -1, -1], [1, 2, 9], [-1, -1, -1]]))
     assert pt.tolist() == [5, 9, -1]
+
+
+def test_probability_error_is_relative_above_the_fp32_normal_range():
+    from tests.parity_util import FLT_MIN, prob_rel_error
+    assert prob_rel_error([1.0000358], [1.0]) > 3e-5
+    assert prob_rel_error([0.5, 1e-20 * (1 + 2e-6)], [0.5, 1e-20]) < 3e-6
+    # both below 2^-126 (a subnormal or zero on the fp32 side): equal
+    assert prob_rel_error([0.0, 1e-40], [3e-42, 1e-41]) == 0.0
+    # the oracle below 2^-126 but the GPU not: counted as a full error
+    assert prob_rel_error([2 * FLT_MIN], [1e-41]) == 1.0
+    # the oracle above 2^-126 and the GPU flushed to zero: a full relative error
+    assert prob_rel_error([0.0], [1e-30]) == 1.0

@@ -97,6 +97,19 @@ def test_nan_logits_mark_the_sequence_faulty():
         check_case(g, mode="greedy")
 
 
+def test_small_residual_mass_bf16():
+    """A draft within a few bf16 ulps of the target (sigma 0.02 and 0.005)
+    and accept uniforms of 1 - 2^-24, so nearly every position with a ratio
+    below 1 is rejected and sampled from a residual of small mass."""
+    for sigma in (0.02, 0.005):
+        print(f"case small residual mass sigma={sigma}", flush=True)
+        for seed in range(3):
+            c = _case(64, 4, 32000, "bf16", sigma=sigma, key=(22, seed, int(sigma * 1000)))
+            c.uniforms[:, :, 0] = 1.0 - 2.0 ** -24
+            rep, out, orc = check_case(c)
+            assert np.sum(orc["accepted_len"] < c.K) > 40   # the residual path is exercised
+
+
 def test_constant_rows():
     """Every logit of every row equal: P_t = P_d = 1/V, every draft accepted
     (ratio exactly 1), and the bonus token is the inverse CDF of a uniform

@@ -179,16 +179,14 @@ __global__ void __launch_bounds__(kBlock) dense_fill_kernel(void* dense, size_t 
   }
 }
 
-// SLAB tokens per block (SLAB / 16 waves of 16 MFMA columns); DEPTH stages
-// of loads in flight in registers.  kFull: d % kStageK == 0 and 16-byte
-// aligned rows, so every load is a whole 16-byte piece inside its row; the
-// loads are then issued unconditionally (W rows past the slab re-read its
-// last row, A rows past the pass read h's first row, stages past the end
-// re-read the last one; none of it reaches an output), which keeps the
-// compiler's wait counts partial.  Otherwise loads are guarded per lane and
-// zero-filled past d.
-template <int SLAB, int DEPTH, bool kFull>
-__global__ void __launch_bounds__(SLAB / 16 * kWave) head_mfma_kernel(HeadArgs a) {
+// SLAB tokens per block (SLAB / 16 waves of 16 MFMA columns); one stage of
+// loads in flight in registers.  kFull: d % kStageK == 0 and 16-byte aligned
+// rows, so every load is a whole 16-byte piece inside its row; the loads are
+// then issued without per-lane guards (W rows past the slab re-read its last
+// row, A rows past the pass read h's first row; none of it reaches an
+// output).  Otherwise loads are guarded per lane and zero-filled past d.
+template <int SLAB, bool kFull>
+__global__ void __launch_bounds__(SLAB / 16 * kWave, 3) head_mfma_kernel(HeadArgs a) {
   constexpr int NTH = SLAB / 16 * kWave;
   constexpr int kCols = kStageK / 8, kRowsPerLoad = NTH / kCols;
   constexpr int kWL = SLAB / kRowsPerLoad;        // 16-byte W loads per thread per stage
@@ -253,75 +251,68 @@ __global__ void __launch_bounds__(SLAB / 16 * kWave) head_mfma_kernel(HeadArgs a
           arow[i] = a.h + ((size_t)(ctx >> 16) * K + rr % K) * a.d;
         }
       }
-      u32x4 wreg[DEPTH][kWL], areg[DEPTH][kAL];
-      auto load_stage = [&](int st, u32x4 (&wr)[kWL], u32x4 (&ar)[kAL]) {
+      u32x4 wreg[kWL], areg[kAL];
+      auto load_stage = [&](int st) {
+        const int k = st * kStageK + c8;
         if (kFull) {
-          const int k = min(st, nstage - 1) * kStageK + c8;
 #pragma unroll
           for (int i = 0; i < kWL; ++i)  // W streams once per pass: nontemporal
-            wr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[i] + k));
+            wreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[i] + k));
 #pragma unroll
-          for (int i = 0; i < kAL; ++i) ar[i] = *reinterpret_cast<const u32x4*>(arow[i] + k);
+          for (int i = 0; i < kAL; ++i) areg[i] = *reinterpret_cast<const u32x4*>(arow[i] + k);
         } else {
-          const int k = st * kStageK + c8;
-          const bool live = st < nstage;
 #pragma unroll
-          for (int i = 0; i < kWL; ++i)
-            wr[i] = (live && wrow[i]) ? load8(wrow[i], k, a.d, a.vec_ok) : u32x4{0u, 0u, 0u, 0u};
+          for (int i = 0; i < kWL; ++i) wreg[i] = wrow[i] ? load8(wrow[i], k, a.d, a.vec_ok) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-          for (int i = 0; i < kAL; ++i)
-            ar[i] = (live && arow[i]) ? load8(arow[i], k, a.d, a.vec_ok) : u32x4{0u, 0u, 0u, 0u};
+          for (int i = 0; i < kAL; ++i) areg[i] = arow[i] ? load8(arow[i], k, a.d, a.vec_ok) : u32x4{0u, 0u, 0u, 0u};
         }
+      };
+      auto stage_to_lds = [&]() {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kWL; ++i) *reinterpret_cast<u32x4*>(&sh_w[lds_at(kRowsPerLoad * i + lrow, c8)]) = wreg[i];
+#pragma unroll
+        for (int i = 0; i < kAL; ++i) *reinterpret_cast<u32x4*>(&sh_a[lds_at(kRowsPerLoad * i + lrow, c8)]) = areg[i];
+        __syncthreads();
       };
       f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
       const bool two = nr > 16;
+      auto mfma_stage = [&]() {
 #pragma unroll
-      for (int j = 0; j < DEPTH; ++j) {
-        load_stage(j, wreg[j], areg[j]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      for (int st0 = 0; st0 < nstage; st0 += DEPTH) {
-#pragma unroll
-        for (int j = 0; j < DEPTH; ++j) {
-          const int st = st0 + j;
-          __syncthreads();
-#pragma unroll
-          for (int i = 0; i < kWL; ++i)
-            *reinterpret_cast<u32x4*>(&sh_w[lds_at(kRowsPerLoad * i + lrow, c8)]) = wreg[j][i];
-#pragma unroll
-          for (int i = 0; i < kAL; ++i)
-            *reinterpret_cast<u32x4*>(&sh_a[lds_at(kRowsPerLoad * i + lrow, c8)]) = areg[j][i];
-          __syncthreads();
-          load_stage(st + DEPTH, wreg[j], areg[j]);
-          if (st < nstage) {  // uniform; the loads above stay outside it
-#pragma unroll
-            for (int q = 0; q < kStageK / 32; ++q) {
-              const int kofs = q * 32 + kgrp * 8;
-              const u32x4 bv = *reinterpret_cast<const u32x4*>(&sh_w[lds_at(my_tok, kofs)]);
-              const bf16x8 bfrag = __builtin_bit_cast(bf16x8, bv);
-              const u32x4 a0 = *reinterpret_cast<const u32x4*>(&sh_a[lds_at(lane & 15, kofs)]);
-              acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), bfrag, acc[0], 0, 0, 0);
-              if (two) {
-                const u32x4 a1 = *reinterpret_cast<const u32x4*>(&sh_a[lds_at(16 + (lane & 15), kofs)]);
-                acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), bfrag, acc[1], 0, 0,
-                                                                 0);
-              }
-            }
+        for (int q = 0; q < kStageK / 32; ++q) {
+          const int kofs = q * 32 + kgrp * 8;
+          const u32x4 bv = *reinterpret_cast<const u32x4*>(&sh_w[lds_at(my_tok, kofs)]);
+          const bf16x8 bfrag = __builtin_bit_cast(bf16x8, bv);
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(&sh_a[lds_at(lane & 15, kofs)]);
+          acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), bfrag, acc[0], 0, 0, 0);
+          if (two) {
+            const u32x4 a1 = *reinterpret_cast<const u32x4*>(&sh_a[lds_at(16 + (lane & 15), kofs)]);
+            acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), bfrag, acc[1], 0, 0, 0);
           }
         }
+      };
+      // One stage in flight: the next stage's loads are issued before the
+      // MFMA work on the current one; the last stage issues none.
+      load_stage(0);
+      for (int st = 0; st + 1 < nstage; ++st) {
+        stage_to_lds();
+        load_stage(st + 1);
+        mfma_stage();
       }
+      stage_to_lds();
+      mfma_stage();
       store_pass(a, acc, sh_ctx, p0, r0, nr, tok0, tok_in0, my_tok, ntok, kgrp);
     }
   }
 }
 
-template <int SLAB, int DEPTH>
+template <int SLAB>
 void launch_head_cfg(const HeadArgs& a, int n_clusters, bool full, hipStream_t st) {
   // a multiple of 8 clusters (the excess exits at once), times the slabs of each
   const size_t nslab = (size_t)(a.cs + SLAB - 1) / SLAB;
   const dim3 grid((unsigned)(((size_t)n_clusters + 7) / 8 * 8 * nslab)), block(SLAB / 16 * kWave);
-  if (full) hipLaunchKernelGGL((head_mfma_kernel<SLAB, DEPTH, true>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((head_mfma_kernel<SLAB, DEPTH, false>), grid, block, 0, st, a);
+  if (full) hipLaunchKernelGGL((head_mfma_kernel<SLAB, true>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((head_mfma_kernel<SLAB, false>), grid, block, 0, st, a);
 }
 
 }  // namespace
@@ -359,7 +350,7 @@ hipError_t launch_head(const void* h, const void* W, const int32_t* cluster_ids,
   const bool full = a.vec_ok && d % kStageK == 0;
   // 64-token slabs with one stage in flight: 32-token slabs (more, smaller
   // blocks) and two stages in flight both measured slower.
-  launch_head_cfg<64, 1>(a, n_clusters, full, st);
+  launch_head_cfg<64>(a, n_clusters, full, st);
   return hipGetLastError();
 }
 

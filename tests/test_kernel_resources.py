@@ -44,3 +44,14 @@ def test_every_kernel_has_no_private_segment(device_asm):
 def test_no_packed_fp32_valu(device_asm):
     for name, asm in device_asm.items():
         assert not re.search(r"\bv_pk_(fma|mul|add)_f32\b", asm), name
+
+
+def test_shortlist_head_fits_three_blocks_per_cu(device_asm):
+    # Three 4-wave blocks per CU: LDS (53.4 KB each) allows three, and the
+    # register file must too (512 per SIMD lane / 3 waves, in units of 8).
+    asm = device_asm["sv_head.hip"]
+    found = 0
+    for m in re.finditer(r"\.name:\s+(_ZN\S*head_mfma_kernel\S*)\s*\n(?:.*\n)*?\s+\.vgpr_count:\s+(\d+)", asm):
+        found += 1
+        assert int(m.group(2)) <= 168, (m.group(1), m.group(2))
+    assert found == 2

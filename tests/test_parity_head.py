@@ -74,6 +74,8 @@ def _small(B, K, d, n_clusters, cs, n_sel, seed):
     (2, 3, 100, 8, 16, 8),        # d % 8 != 0: element loads; every cluster selected
     (4, 40, 64, 6, 64, 2),        # K > 32: several row passes per context
     (40, 1, 128, 4, 32, 3),       # many contexts share a cluster
+    (3, 2, 256, 10, 70, 3),       # whole-stage rows, one stage: no loads inside the stage loop
+    (4, 4, 512, 12, 64, 4),       # whole-stage rows, two stages
 ])
 def test_head_small(B, K, d, nc, cs, n_sel):
     print(f"head B={B} K={K} d={d} clusters={nc}x{cs} n_sel={n_sel}", flush=True)

@@ -58,3 +58,24 @@ def test_random_case(i):
     go = run_oracle(c, "greedy")
     grep_ = compare(g[0], g[1], go, K, greedy=True)
     assert not grep_.failures, grep_.failures[:3]
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_sparse_draft_case(i):
+    """The sparse-draft form (compact draft rows over per-position cluster
+    shortlists) on seeded random shapes, against the oracle on the dense form."""
+    from tests.test_parity_sparse_draft import check_sparse
+    from workloads import sparse_draft_case
+    r = np.random.default_rng([75, i])
+    B = int(r.integers(100, 301)) if i % 4 == 3 else int(r.integers(1, 41))
+    K = int(r.choice([0, 1, 2, 3, 4, 7]))
+    cs = int(r.choice([1, 7, 50, 64, 501]))
+    nc = int(r.integers(1, 80)) if cs > 1 else int(r.integers(64, 40000))
+    V = nc * cs
+    n_sel = [int(r.integers(1, nc + 1)) for _ in range(K)]
+    dtype = "bf16" if r.random() < 0.6 else "f32"
+    T = float(np.exp(r.uniform(np.log(0.1), np.log(10.0))))
+    sigma = float(r.choice([0.05, 0.3, 0.7, 1.5]))
+    print(f"random sparse case {i}: B={B} K={K} V={V} clusters={nc}x{cs} n_sel={n_sel} {dtype} T={T:.4g} "
+          f"sigma={sigma}", flush=True)
+    check_sparse(sparse_draft_case(B, K, V, cs, n_sel, dtype, temperature=T, sigma=sigma, key=(76, i)))

@@ -57,6 +57,15 @@ MUTANTS = {
     "kv_commit_off_by_one": ("(size_t)Lmax + (size_t)(len + j)) * (size_t)row_bytes;",
                              "(size_t)Lmax + (size_t)(len + j + 1)) * (size_t)row_bytes;"),
     "kv_commit_includes_rejected": ("for (int32_t j = 0; j < n; ++j) {", "for (int32_t j = 0; j <= n && j < K; ++j) {"),
+    "head_w_transposed": ("double wv = logit_at(W, OR_BF16, (size_t)tok * d + (size_t)j);",
+                          "double wv = logit_at(W, OR_BF16, (size_t)j * V + (size_t)tok);"),
+    "head_tokens_reversed_in_cluster": ("int32_t tok = c * cluster_size + t;",
+                                        "int32_t tok = c * cluster_size + (cluster_size - 1 - t);"),
+    "head_compact_in_reverse_selection_order": (
+        "size_t o = ((size_t)b * K + k) * (size_t)L + (size_t)s * cluster_size + (size_t)t;",
+        "size_t o = ((size_t)b * K + k) * (size_t)L + (size_t)(n_sel - 1 - s) * cluster_size + (size_t)t;"),
+    "head_absdot_signed": ("aacc += fabs(hv * wv);", "aacc += hv * wv;"),
+    "head_dense_zero_fill": ("dense[i] = -INFINITY;", "dense[i] = 0.0;"),
     "kv_commit_no_room_check": ("if (len < 0 || len > Lmax - n) { status[b] = 1; continue; }",
                                 "if (len < 0) { status[b] = 1; continue; }"),
 }
@@ -91,6 +100,9 @@ PINS = [
     pins.test_overlap_worked_example_is_the_printed_acceptance,
     pins.test_overlap_is_one_minus_total_variation,
     pins.test_overlap_limits,
+    pins.test_head_all_clusters_is_dense_matmul_and_permutation_free,
+    pins.test_head_one_hot_rows_pick_columns_of_W,
+    pins.test_head_absdot_is_the_sum_of_absolute_products,
     kv_pins.test_exercise_prefix_plus_accepted_drafts,
     kv_pins.test_multi_step_cache_holds_the_committed_stream,
     kv_pins.test_status_cases_commit_nothing,

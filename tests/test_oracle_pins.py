@@ -380,6 +380,59 @@ def test_head_all_clusters_is_dense_matmul_and_permutation_free():
         oracle.head(h, W, np.array([[4, 1, 7], [0, 4, 11]], np.int32), cs)
 
 
+def test_head_one_hot_rows_pick_columns_of_W():
+    """With h[b, k] the unit vector e_j, the logit of token v is W[v, j]
+    exactly (DynaSpec summary, "Model architecture" item 4: logits over the
+    selected clusters only).  W holds small integers that encode (v, j), so
+    the shortlist layout (entry s, offset t -> token c_s * cs + t), the column
+    read, the magnitude sum and the dense scatter are all read off exactly."""
+    import torch
+    B, K, d, V, cs = 2, 3, 16, 40, 5
+    j_of = np.array([[0, 7, 15], [3, 3, 9]])
+    h = torch.zeros(B, K, d)
+    for b in range(B):
+        for k in range(K):
+            h[b, k, j_of[b, k]] = 1.0
+    Wf = (np.arange(V)[:, None] + 1) + 64.0 * (np.arange(d)[None, :] % 3)   # integers up to 168
+    W = torch.from_numpy(Wf).to(torch.bfloat16)
+    assert np.array_equal(W.double().numpy(), Wf)                           # exact in bf16
+    sel = np.array([[1, 4, 6], [0, 2, 7]], np.int32)
+    r = oracle.head(h.to(torch.bfloat16), W, sel, cs, dense=True)
+    for b in range(B):
+        for k in range(K):
+            off = np.ones(V, bool)
+            for s, c in enumerate(sel[b]):
+                for t in range(cs):
+                    tok = c * cs + t
+                    want = Wf[tok, j_of[b, k]]
+                    assert r["compact"][b, k, s * cs + t] == want
+                    assert r["absdot"][b, k, s * cs + t] == abs(want)
+                    assert r["dense"][b, k, tok] == want
+                    off[tok] = False
+            assert np.all(np.isneginf(r["dense"][b, k, off]))
+
+
+def test_head_absdot_is_the_sum_of_absolute_products():
+    """absdot, the magnitude the head's tolerance is relative to, is
+    sum_j |h_j W_vj|.  With h = +-1 and W rows (v + 1) * a_j * (-1)^j,
+    a_j = 2^j, the logit cancels to -85 (v + 1) times h's sign while absdot
+    is 255 (v + 1)."""
+    import torch
+    B, K, d, V, cs = 1, 2, 8, 6, 3
+    h = torch.ones(B, K, d)
+    h[0, 1] = -1.0
+    a = 2.0 ** np.arange(d)
+    Wf = np.stack([(v + 1) * a * (-1.0) ** np.arange(d) for v in range(V)])
+    W = torch.from_numpy(Wf).to(torch.bfloat16)
+    assert np.array_equal(W.double().numpy(), Wf)
+    r = oracle.head(h.to(torch.bfloat16), W, np.array([[0, 1]], np.int32), cs)
+    v = np.arange(V)
+    np.testing.assert_array_equal(r["compact"][0, 0], -85.0 * (v + 1))
+    np.testing.assert_array_equal(r["compact"][0, 1], 85.0 * (v + 1))
+    np.testing.assert_array_equal(r["absdot"][0, 0], 255.0 * (v + 1))
+    np.testing.assert_array_equal(r["absdot"][0, 1], 255.0 * (v + 1))
+
+
 # --------------------------------------------------------------------------------------
 # Boundary conventions: strict accept comparison and the inverse-CDF boundary.
 # --------------------------------------------------------------------------------------

@@ -3,7 +3,8 @@
 Shapes are drawn from a fixed seed: the number of contexts, positions and
 hidden dims (multiples of 256, of 64, of 8 and none of these, so every load
 path of both kernels is taken), the number and size of clusters and how many
-each context keeps, and the output dtypes.  Tolerances are those of the
+each context keeps, and the output dtypes (the static head both with d split over blocks and
+in one launch).  Tolerances are those of the
 hand-picked head tests: 1e-5 of sum_j |h_j W_tj| per logit, plus the bf16
 unit roundoff for bf16 outputs, and the dense output's -inf pattern exact.
 """
@@ -12,7 +13,7 @@ import pytest
 import torch
 
 from tests.test_parity_head import _check as check_shortlist, _small
-from tests.test_parity_static_head import _check as check_static, _static_ids
+from tests.test_parity_static_head import DEV, HEAD_TOL, _check as check_static, _static_ids
 from workloads import head_case
 
 pytestmark = pytest.mark.gpu
@@ -64,4 +65,14 @@ def test_random_static_head(i):
     print(f"static head case {i}: B={B} K={K} d={d} V={V} clusters={nc}x{cs} n_sel={n_sel} out={dtype}",
           flush=True)
     hc = head_case(B, K, d, V, nc, 1, trial=7400 + i)
-    check_static(hc.h, hc.W, _static_ids(V, cs, n_sel, seed=7400 + i), cs, dtype)
+    ids = _static_ids(V, cs, n_sel, seed=7400 + i)
+    got, ref = check_static(hc.h, hc.W, ids, cs, dtype)
+    # the single-launch form (no split of d over blocks) against the same oracle values
+    import speculative_sampling_verification_vocab_amd as sv
+    one = sv.spec_draft_head_static(hc.h.to(DEV), hc.W.to(DEV), ids.to(DEV), cs, dtype=dtype, split=False)
+    torch.cuda.synchronize()
+    one = one.float().cpu().numpy()
+    tol = HEAD_TOL * ref["absdot"] + 1e-30
+    if dtype == torch.bfloat16:
+        tol = tol + np.abs(ref["compact"]) * 2.0 ** -8
+    assert np.all(np.abs(one - ref["compact"]) <= tol)

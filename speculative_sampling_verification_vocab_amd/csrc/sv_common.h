@@ -304,10 +304,33 @@ __device__ __forceinline__ float exp_ref_hi(float m, float s) {
   return m == -__builtin_inff() ? __builtin_inff() : m * s;
 }
 
-// lo = m * s - RN(m * s), exact; |lo| <= 2^-25 |m * s|; 0 when m is -inf.
+// Wide references: |m * s| at or above 2^26.  The remainder lo of RN(m * s)
+// is half an ulp of m * s at most, so it grows with |m * s| (up to 2 at 2^26,
+// hundreds past 2^32), and once it nears 128 the one-FMA element value
+// 2^((x - m) * s + lo) leaves the fp32 range: every element of a row
+// overflows or underflows.  Elements of a tile with a wide reference take
+// RN((x - m) * s) instead (x - m is exact for every x near enough to m to
+// carry weight, since |m| is then far above the distance), and such a
+// reference has no remainder to take out (exp_ref_lo returns 0).  This is
+// the case only when the logits' magnitude over T exceeds about 2^25.5
+// (logits near 10 at T below about 2e-7).  -inf references are never wide.
+constexpr float kExpRefWide = 67108864.0f;  // 2^26
+__device__ __forceinline__ bool exp_ref_wide(float m, float s) {
+#pragma clang fp contract(off)
+  return m != -__builtin_inff() && !(__builtin_fabsf(m * s) < kExpRefWide);
+}
+
+// 2^RN((x - m) * s), the element value under a wide reference.
+__device__ __forceinline__ float exp2_wide(float x, float m, float s) {
+#pragma clang fp contract(off)
+  return __builtin_amdgcn_exp2f((x - m) * s);
+}
+
+// lo = m * s - RN(m * s), exact; |lo| <= 2^-25 |m * s|; 0 when m is -inf or
+// wide.
 __device__ __forceinline__ float exp_ref_lo(float m, float s) {
 #pragma clang fp contract(off)
-  if (m == -__builtin_inff()) return 0.0f;
+  if (m == -__builtin_inff() || exp_ref_wide(m, s)) return 0.0f;
   const float hi = m * s;
   return __builtin_fmaf(m, s, -hi);
 }

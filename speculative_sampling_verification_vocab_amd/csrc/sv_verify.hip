@@ -208,18 +208,26 @@ __device__ __forceinline__ void sparse_tile_load(const VerifyArgs& a, int b, int
 // RN((x - ml)*s), but offset by delta = ml*s - c (exact by FMA), since
 // x*s - c = (x - ml)*s + delta.  The offset is taken out once per lane, in
 // the factor 2^((ml - M)*s - delta) that scales the lane sum to the tile
-// maximum M.
+// maximum M.  When a lane's maximum is a wide reference (|ml*s| >= 2^26,
+// where 2^delta can leave the fp32 range), every lane of the wave takes
+// RN((x - ml)*s) instead, with no offset.
 template <typename T>
 __device__ __forceinline__ void stats_tile(const VerifyArgs& a, const float (&x)[kPerLane<T>], TileStat* out) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & (kWave - 1);
   const float ml = lane_max(x);
   const float c = ml * a.s_hi;
-  const float delta = __builtin_fmaf(ml, a.s_hi, -c);
+  const bool wide = __ballot(exp_ref_wide(ml, a.s_hi)) != 0;  // uniform over the wave
+  const float delta = wide ? 0.0f : __builtin_fmaf(ml, a.s_hi, -c);
   float sl = 0.0f;
   if (ml != kNegInf) {
+    if (!wide) {
 #pragma unroll
-    for (int e = 0; e < kPerLane<T>; ++e) sl += exp2_fast(__builtin_fmaf(x[e], a.s_hi, -c));
+      for (int e = 0; e < kPerLane<T>; ++e) sl += exp2_fast(__builtin_fmaf(x[e], a.s_hi, -c));
+    } else {
+#pragma unroll
+      for (int e = 0; e < kPerLane<T>; ++e) sl += exp2_wide(x[e], ml, a.s_hi);
+    }
   }
   const float M = wave_max(ml);
   const float scaled = ml == kNegInf ? 0.0f : sl * exp2_fast((ml - M) * a.s_hi - delta);
@@ -548,6 +556,11 @@ __device__ __forceinline__ float tile_rho(float mt, float md, const SampleRowInf
 // when m is -inf (the tile is all -inf).
 template <int N>
 __device__ __forceinline__ void tile_exp(const float (&x)[N], float m, const VerifyArgs& a, float (&e)[N]) {
+  if (exp_ref_wide(m, a.s_hi)) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) e[i] = exp2_wide(x[i], m, a.s_hi);
+    return;
+  }
   const float hi = exp_ref_hi(m, a.s_hi);
 #pragma unroll
   for (int i = 0; i < N; ++i) e[i] = exp2_ref(x[i], a.s_hi, hi);
@@ -613,16 +626,27 @@ __device__ __forceinline__ void residual_tile(const VerifyArgs& a, int b, int t,
   constexpr int P = NL * Elem<T>::kVec;
   const int lane = threadIdx.x & (kWave - 1);
   double zt = 0.0, zd = 0.0, gs = 0.0, hs = 0.0;
-#pragma unroll
-  for (int i = 0; i < P; ++i) {
-    const float e = exp2_ref(raw_elem<T>(cx, i), a.s_hi, ht);
-    const float f = exp2_ref(raw_elem<T>(cy, i), a.s_hi, hd);
+  auto add = [&](float e, float f) {
     const double et = (double)e, ed = (double)f;
     const double in = e * rho > f ? 1.0 : 0.0;
     zt += et;
     zd += ed;
     gs = __builtin_fma(et, in, gs);
     hs = __builtin_fma(ed, in, hs);
+  };
+  // The references are uniform over the wave, and so is this branch.
+  const bool wt = exp_ref_wide(mt, a.s_hi), wd = exp_ref_wide(md, a.s_hi);
+  if (!(wt || wd)) {
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+      add(exp2_ref(raw_elem<T>(cx, i), a.s_hi, ht), exp2_ref(raw_elem<T>(cy, i), a.s_hi, hd));
+  } else {
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const float x = raw_elem<T>(cx, i), y = raw_elem<T>(cy, i);
+      add(wt ? exp2_wide(x, mt, a.s_hi) : exp2_ref(x, a.s_hi, ht),
+          wd ? exp2_wide(y, md, a.s_hi) : exp2_ref(y, a.s_hi, hd));
+    }
   }
   zt = wave_sum(zt);
   zd = wave_sum(zd);
@@ -639,7 +663,10 @@ __device__ __forceinline__ void bonus_tile(const VerifyArgs& a, int b, int t, co
   const int lane = threadIdx.x & (kWave - 1);
   const float mt = wave_max(raw_lane_max<T>(cx));
   double zt = 0.0;
-  if (mt != kNegInf) {
+  if (exp_ref_wide(mt, a.s_hi)) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) zt += (double)exp2_wide(raw_elem<T>(cx, i), mt, a.s_hi);
+  } else if (mt != kNegInf) {
     const float ht = exp_ref_hi(mt, a.s_hi);
 #pragma unroll
     for (int i = 0; i < P; ++i) zt += (double)exp2_ref(raw_elem<T>(cx, i), a.s_hi, ht);

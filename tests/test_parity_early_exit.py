@@ -82,6 +82,14 @@ def test_early_exit_acceptance_regimes(sigma, T):
         assert np.all(out[0] == 6)
 
 
+@pytest.mark.parametrize("T", [1e-7, 1e-20])
+def test_early_exit_tiny_temperatures(T):
+    """Wide exponent references (|m * s| >= 2^26) in the phase and sampling kernels."""
+    print(f"case early exit T={T}", flush=True)
+    out = check_early_exit(_case(8, 4, 12345 * 8, "bf16", T=T, key=(39, int(-np.log10(T)))))
+    assert np.all(out[0] >= 0)
+
+
 def test_early_exit_large_logit_magnitudes():
     """fp32 logits shifted by +3000: large exponent reference offsets in the
     per-position statistics and decisions."""

@@ -62,7 +62,7 @@ def test_sparse_position_budget(sigma):
     check_sparse(c)
 
 
-@pytest.mark.parametrize("T", [0.02, 50.0])
+@pytest.mark.parametrize("T", [0.02, 50.0, 1e-7, 1e-20])
 def test_sparse_extreme_temperatures(T):
     """Near-greedy and near-uniform temperatures on compact draft rows, whose
     exponent reference is the draft row maximum."""

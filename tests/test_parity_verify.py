@@ -36,6 +36,29 @@ def test_sample_temperatures(T):
     check_case(c)
 
 
+@pytest.mark.parametrize("T", [1e-7, 1e-20, 1e-30])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sample_tiny_temperatures(T, dtype):
+    """Temperatures at which |max logit| * log2(e) / T reaches 2^26 and far
+    beyond (at 1e-7 only the tiles with the larger maxima do): there the
+    exponent references are wide, and each tile whose reference is wide takes
+    RN((x - m) * s) instead of the one-FMA form, whose remainder 2^lo would
+    leave the fp32 range."""
+    print(f"case T={T} {dtype}", flush=True)
+    c = _case(8, 4, 12345 * 8, dtype, T=T, key=(19, int(-np.log10(T))))
+    rep, out, orc = check_case(c)
+    assert np.all(out[0] >= 0)
+
+
+def test_sample_large_logits_at_small_temperature():
+    """Logits shifted by +3000 at T = 1e-5: |m * s| is about 4.3e8, a wide
+    reference in every tile."""
+    c = _case(8, 4, 20000, "f32", T=1e-5, key=(20,))
+    c = VerifyCase(c.target + 3000.0, c.draft + 3000.0, c.draft_tokens, c.uniforms, c.temperature, c.dtype)
+    rep, out, orc = check_case(c)
+    assert np.all(out[0] >= 0)
+
+
 def test_sample_large_logit_magnitudes():
     """Logits shifted by +3000 and -3000 (fp32): the softmax does not change,
     but x*s is large, so the exponents' reference offsets (RN(m*s) and its

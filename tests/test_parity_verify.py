@@ -59,6 +59,25 @@ def test_sample_large_logits_at_small_temperature():
     assert np.all(out[0] >= 0)
 
 
+@pytest.mark.parametrize("scale", [1e10, 1e37])
+def test_sample_scaled_logits(scale):
+    """fp32 logits scaled by 1e10 and 1e37: at T = 1 every reference is wide
+    (a near-greedy row); at T = scale the softmax is that of the unscaled
+    logits, computed from products near the top of the fp32 range."""
+    c = _case(8, 4, 20000, "f32", key=(21,))
+    for T in (1.0, float(np.float32(scale))):
+        print(f"case logits x {scale}, T={T}", flush=True)
+        check_case(VerifyCase(c.target * scale, c.draft * scale, c.draft_tokens, c.uniforms, T, c.dtype))
+
+
+def test_sample_huge_temperature():
+    """T = 1e38: s = log2(e)/T is 1.4e-38, next to the smallest normal fp32;
+    every exponent's argument is within rounding of 0, and both distributions
+    are uniform."""
+    rep, out, orc = check_case(_case(8, 4, 20000, "bf16", T=1e38, key=(22,)))
+    assert np.all(out[0] == 4)
+
+
 def test_sample_large_logit_magnitudes():
     """Logits shifted by +3000 and -3000 (fp32): the softmax does not change,
     but x*s is large, so the exponents' reference offsets (RN(m*s) and its

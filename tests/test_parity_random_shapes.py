@@ -2,10 +2,11 @@
 
 The other parity tests pick their shapes by hand (tile edges, ragged rows,
 the benchmarked workloads).  This sweep draws B, K, V, the logit dtype, the
-temperature, the target's spread and prior and the draft's distance from the
-target at random (a fixed seed, so every run checks the same cases), and
-runs each case through SAMPLE (against the oracle, decision by decision),
-the early-exit schedule (bit-identical to SAMPLE) and GREEDY (against the
+temperature (a third of the cases anywhere from 1e-25 to 1e25), the
+target's spread and prior and the draft's distance from the target at
+random (a fixed seed, so every run checks the same cases), and runs each
+case through SAMPLE (against the oracle, decision by decision), the
+early-exit schedule (bit-identical to SAMPLE) and GREEDY (against the
 oracle's argmax rule).  The case's parameters are printed before its GPU
 calls.
 """
@@ -34,6 +35,8 @@ def _draw(i):
         V = int(r.integers(20000, 40001))
     dtype = "bf16" if r.random() < 0.6 else "f32"
     T = float(np.exp(r.uniform(np.log(0.05), np.log(20.0))))
+    if i % 3 == 2:  # a third of the cases anywhere from 1e-25 to 1e25
+        T = float(np.float32(np.exp(r.uniform(np.log(1e-25), np.log(1e25)))))
     std = float(r.uniform(0.5, 5.0))
     zipf = float(r.choice([0.0, 1.1]))
     sigma = float(r.choice([0.0, 0.05, 0.3, 0.7, 1.5, 3.0]))

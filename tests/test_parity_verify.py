@@ -78,6 +78,14 @@ def test_sample_huge_temperature():
     assert np.all(out[0] == 4)
 
 
+@pytest.mark.parametrize("mode", ["sample", "greedy"])
+def test_very_large_batch_small_vocabulary(mode):
+    """B = 100,000 sequences of 33-token rows: grids of hundreds of thousands
+    of blocks and one decision block per sequence."""
+    c = _case(100000, 4, 33, "bf16", std=2.0, zipf=0.0, key=(23,))
+    check_case(c, mode)
+
+
 def test_sample_large_logit_magnitudes():
     """Logits shifted by +3000 and -3000 (fp32): the softmax does not change,
     but x*s is large, so the exponents' reference offsets (RN(m*s) and its

@@ -121,6 +121,8 @@ def test_head_validation(lib):
     assert f(fake, fake, fake, 2, 4, 64, 1000, 10, 2, None, None, 0, None, 0, None) == 1
     assert f(fake, fake, fake, 2, 4, 64, 1000, 10, 101, fake, None, 0, None, 0, None) == 1
     assert f(fake, fake, fake, 0, 4, 64, 1000, 10, 2, fake, None, 0, None, 0, None) == 0
+    # more contexts than a cluster's context list holds (1024)
+    assert f(fake, fake, fake, 1025, 4, 64, 1000, 10, 2, fake, None, 0, None, 0, None) == 2
 
 
 def test_static_head_validation(lib):

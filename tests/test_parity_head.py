@@ -82,6 +82,13 @@ def test_head_small(B, K, d, nc, cs, n_sel):
     _check(_small(B, K, d, nc, cs, n_sel, seed=B * 1000 + K))
 
 
+def test_head_max_contexts():
+    """1024 contexts (the most one cluster's context list holds), each keeping
+    every cluster: every block lists all 1024 and makes 128 passes of 32
+    (context, position) rows over its slab."""
+    _check(_small(1024, 4, 64, 4, 32, 4, seed=13), dense_dtype=torch.bfloat16)
+
+
 def test_head_all_clusters_is_dense_gemm():
     hc = _small(3, 4, 256, 10, 24, 10, seed=5)
     comp, dense, ref = _check(hc)

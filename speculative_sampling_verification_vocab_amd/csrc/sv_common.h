@@ -181,6 +181,10 @@ constexpr int kHalfMirror = 0x141;
 constexpr int kMirror = 0x140;
 constexpr int kBcast15 = 0x142;
 constexpr int kBcast31 = 0x143;
+constexpr int kShr1 = 0x111;  // row_shr:1 (within rows of 16 lanes)
+constexpr int kShr2 = 0x112;
+constexpr int kShr4 = 0x114;
+constexpr int kShr8 = 0x118;
 
 template <int kCtrl, int kRowMask>
 __device__ __forceinline__ int mov(int old, int v) {
@@ -235,13 +239,17 @@ __device__ __forceinline__ int wave_max(int v) {
   return dpp::reduce(v, (int)0x80000000, [](int x, int y) { return max(x, y); });
 }
 
-// Inclusive prefix sum over the 64 lanes in lane order.
-__device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    double u = __shfl_up(v, o);
-    if (lane >= o) v += u;
-  }
+// Inclusive prefix sum over the 64 lanes in lane order, with DPP lane moves:
+// row shifts by 1, 2, 4 and 8 scan each row of 16 lanes (a lane shifted in
+// from outside its row adds 0), then row_bcast15 adds row 0's total to row 1
+// and row 2's to row 3, and row_bcast31 the total of rows 0-1 to rows 2-3.
+__device__ __forceinline__ double wave_inclusive_scan(double v) {
+  v += dpp::mov<dpp::kShr1, 0xf>(0.0, v);
+  v += dpp::mov<dpp::kShr2, 0xf>(0.0, v);
+  v += dpp::mov<dpp::kShr4, 0xf>(0.0, v);
+  v += dpp::mov<dpp::kShr8, 0xf>(0.0, v);
+  v += dpp::mov<dpp::kBcast15, 0xa>(0.0, v);
+  v += dpp::mov<dpp::kBcast31, 0xc>(0.0, v);
   return v;
 }
 

@@ -130,9 +130,13 @@ inline VerifyShape make_shape(int B, int K, int V, int dtype, bool aligned) {
   }
   s.NG_s = (s.NT_s + s.TPW_s * kWavesPerBlock - 1) / (s.TPW_s * kWavesPerBlock);
   s.TPW_e = (long long)B * 2 * s.NG >= kEEBlocksForTwo ? 2 : 1;
-  // A separate decision launch pays off once blocks cover several sampling
-  // tiles (B=256, K=7, V=262144: 353 -> 348 us; B=8: 21.8 -> 24.5 us with it).
-  s.decide = s.TPW_s > 1;
+  // Every sampling block takes its sequence's accept decisions in its
+  // prologue, unless that prologue is heavy (more than 16 rows, four per
+  // wave, or more than 64 partials per row) in a grid of blocks that cover
+  // several sampling tiles: then a separate launch takes them once per
+  // sequence.  (B=256, K=7, V=262144: 346.6 -> 345.5 us without that launch;
+  // B=8, K=5, V=128256: 21.8 -> 24.5 us with it.)
+  s.decide = s.TPW_s > 1 && (2 * K > 4 * kWavesPerBlock || s.NT > kWave);
   // Small sampling grids pick the token in their last block per sequence
   // instead of a launch of their own (B=1, K=4, V=32000: 20 -> 14 us; B=8,
   // K=5, V=128256: 19.5 -> 18 us).  A statistics launch precedes them to

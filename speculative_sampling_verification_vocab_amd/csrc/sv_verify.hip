@@ -9,10 +9,11 @@
 //  2. The accept decisions: combine the sequence's partials into (max, Z) per
 //     row, evaluate P_t,i(d_i) and P_d,i(d_i) in double, take every decision
 //     u < min(1, P_t/P_d) and find the first rejection n (Speculative Decoding
-//     lesson, nextadmin.net, "Core algorithm" steps 4-5, "Step 1").  Large
-//     batches run them in decide_kernel, one block per sequence; small ones in
-//     the prologue of every sampling block (the sequence's first block writes
-//     the outputs), which saves a launch.
+//     lesson, nextadmin.net, "Core algorithm" steps 4-5, "Step 1").  They run
+//     in the prologue of every sampling block (the sequence's first block
+//     writes the outputs), which saves a launch; only when that prologue is
+//     heavy (many rows or many partials per row) and large grids would repeat
+//     it in many blocks does decide_kernel take them once per sequence.
 //  3. sample_kernel re-reads only what the output token at n needs: its tiles
 //     of target and draft row n at a rejection (residual (P_t - P_d)_+,
 //     "Step 2"), or of target row K when every draft was accepted (bonus
@@ -439,13 +440,10 @@ template <bool kCoherent = false>
 __device__ __forceinline__ SampleRowInfo accept_sequence(const VerifyArgs& a, int b, bool write) {
   __shared__ float sh_m[2 * kMaxK];
   __shared__ double sh_z[2 * kMaxK];
-  __shared__ int sh_acc[kMaxK];
-  __shared__ int sh_bad;
   __shared__ int sh_n;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int K = a.K, R = 2 * K;
   if (K == 0) return SampleRowInfo{0.0f, 0.0f, 1.0, 1.0, 0};
-  if (threadIdx.x == 0) sh_bad = 0;
   // Loads that do not depend on each other go first: the drafted tokens,
   // their logits (recorded by the statistics pass) and the accept uniforms.
   double xt = 0.0, xd = 0.0;
@@ -455,10 +453,11 @@ __device__ __forceinline__ SampleRowInfo accept_sequence(const VerifyArgs& a, in
     const int i = threadIdx.x;
     d = a.tokens[(size_t)b * K + i];
     u = a.uniforms[((size_t)b * (K + 1) + i) * 2];
-    if (d >= 0 && d < a.V) {
-      xt = (double)a.gx[(size_t)b * R + i];
-      xd = (double)a.gx[(size_t)b * R + K + i];
-    }
+    // Loaded whatever the token is, so these loads do not wait for it: the
+    // slot of a token outside [0, V) was not written, and the test marks such
+    // a position faulty without reading it.
+    xt = (double)a.gx[(size_t)b * R + i];
+    xd = (double)a.gx[(size_t)b * R + K + i];
   }
   // Row (max, Z).  Wave w owns rows w, w+4, ...  When each row has at most 64
   // tiles and a wave at most kRowsPerWave rows, every partial is loaded
@@ -499,22 +498,17 @@ __device__ __forceinline__ SampleRowInfo accept_sequence(const VerifyArgs& a, in
   __syncthreads();
 
   double pt = __builtin_nan(""), pd = __builtin_nan("");
+  bool acc = true, bad = false;
   if ((int)threadIdx.x < K) {
     const int i = threadIdx.x;
-    bool bad;
-    const bool acc = accept_test(a, d, xt, xd, sh_m[i], sh_m[K + i], sh_z[i], sh_z[K + i], u, pt, pd, bad);
-    if (bad) atomicOr(&sh_bad, 1);
-    sh_acc[i] = acc;
+    acc = accept_test(a, d, xt, xd, sh_m[i], sh_m[K + i], sh_z[i], sh_z[K + i], u, pt, pd, bad);
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int n = K;
-    for (int i = 0; i < K; ++i)
-      if (!sh_acc[i]) {
-        n = i;
-        break;
-      }
-    sh_n = sh_bad ? -1 : n;
+  // Positions 0..K-1 (K <= 64) are the lanes of wave 0: the first rejection
+  // is the lowest lane of its ballot.
+  if (wave == 0) {
+    const uint64_t rej = __ballot(!acc);
+    const bool any_bad = __ballot(bad) != 0;
+    if (lane == 0) sh_n = any_bad ? -1 : (rej ? (int)__builtin_ctzll(rej) : K);
   }
   __syncthreads();
   const int n = sh_n;
@@ -569,6 +563,11 @@ __device__ __forceinline__ void tile_exp(const float (&x)[N], float m, const Ver
 // Value of v in lane l (l the same in every lane of the wave).
 __device__ __forceinline__ float lane_value(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), __builtin_amdgcn_readfirstlane(l)));
+}
+__device__ __forceinline__ double lane_value(double v, int l) {
+  const int i = __builtin_amdgcn_readfirstlane(l);
+  return __hiloint2double(__builtin_amdgcn_readlane((int)__double2hiint(v), i),
+                          __builtin_amdgcn_readlane((int)__double2loint(v), i));
 }
 
 // ---------------------------------------------------------------------------
@@ -698,6 +697,18 @@ __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
   const int K = a.K;
   const int g = blk % a.NGs;
   const int b = blk / a.NGs;
+  // The exponent references of the block's statistics tiles in every row
+  // that can be sampled (target rows 0..K-1, then, for dense drafts, draft
+  // rows 0..K-1), loaded together with the sequence's record or decision
+  // inputs, so that they cost no round trip of their own once n is known.
+  // Thread j holds row j / nst, statistics tile T0 + j % nst.
+  const int nst = a.TPWs * kWavesPerBlock / kSubTiles<T>;  // statistics tiles the block covers
+  const int T0 = g * nst;
+  const int nref = (kSparse ? 1 : 2) * K * nst;
+  const bool pre = nref <= kBlock;
+  float pref = kNegInf;
+  if (pre && (int)threadIdx.x < nref && T0 + (int)threadIdx.x % nst < a.NT)
+    pref = a.part_a[((size_t)b * 2 * K + threadIdx.x / nst) * a.NT + T0 + threadIdx.x % nst].m;
   SampleRowInfo sr;
   int n;
   if constexpr (kDecided) {
@@ -729,6 +740,11 @@ __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
   }
   if (n < 0) return;  // faulty sequence: outputs already written
   const bool resid = n < K;
+  __shared__ float sh_ref[kBlock];
+  if (pre) {
+    sh_ref[threadIdx.x] = pref;
+    __syncthreads();
+  }
   const T* trow = row_ptr<T>(a.target, (size_t)b * (K + 1) + n, a.V);
   const T* drow = resid && !kSparse ? row_ptr<T>(a.draft, (size_t)b * K + n, a.V) : trow;
   constexpr int NL = kLoadsS;
@@ -746,13 +762,13 @@ __device__ __forceinline__ void sample_block(const VerifyArgs& a, int blk) {
   }
   if (tile_of(0) < a.NTs) {
     // Residual: lane l holds the references and the ratio of statistics tile T0 + l.
-    const int T0 = g * a.TPWs * kWavesPerBlock / kSubTiles<T>;
     float ref_t = kNegInf, ref_d = kNegInf, rho_l = 0.0f;
-    if (resid && lane < a.TPWs * kWavesPerBlock / kSubTiles<T> && T0 + lane < a.NT) {
+    if (resid && lane < nst && T0 + lane < a.NT) {
       const size_t R = 2 * (size_t)K;
-      ref_t = a.part_a[((size_t)b * R + n) * a.NT + T0 + lane].m;
+      ref_t = pre ? sh_ref[n * nst + lane] : a.part_a[((size_t)b * R + n) * a.NT + T0 + lane].m;
       // a sparse draft row has no dense tiles: its row maximum is the reference
-      ref_d = kSparse ? sr.m_d : a.part_a[((size_t)b * R + K + n) * a.NT + T0 + lane].m;
+      if constexpr (kSparse) ref_d = sr.m_d;
+      else ref_d = pre ? sh_ref[(K + n) * nst + lane] : a.part_a[((size_t)b * R + K + n) * a.NT + T0 + lane].m;
       rho_l = tile_rho(ref_t, ref_d, sr, a.s64, a.s_hi);
     }
     const float hi_t = exp_ref_hi(ref_t, a.s_hi), hi_d = exp_ref_hi(ref_d, a.s_hi);
@@ -860,7 +876,6 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b, const Sam
   __shared__ int sh_i[2 * kWavesPerBlock];
   __shared__ double sh_scan[kWavesPerBlock];
   __shared__ double sh_cbefore;
-  __shared__ float sh_u[kMaxK + 1];
   constexpr double kNegInfD = -__builtin_inf();
   const int K = a.K, NT = a.NTs;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -868,7 +883,10 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b, const Sam
   const bool cached = NT <= kBlock;
   SampleTile q0{kNegInfD, kNegInfD, 0.0, 0.0, 0.0, 0.0};
   if (cached && (int)threadIdx.x < NT) q0 = get_sample_tile<kFused>(P + threadIdx.x);
-  if ((int)threadIdx.x <= K) sh_u[threadIdx.x] = a.uniforms[((size_t)b * (K + 1) + threadIdx.x) * 2 + 1];
+  // The sample uniforms of every position, loaded before n is known (thread i
+  // holds position i's).
+  float ui = 0.0f;
+  if ((int)threadIdx.x <= K) ui = a.uniforms[((size_t)b * (K + 1) + threadIdx.x) * 2 + 1];
   const SampleRowInfo sr = kFused ? sr_local : a.rows[b];
   const int n = K == 0 ? 0 : sr.n;
   if (n < 0) return;  // uniform over the block: every thread read the same record
@@ -878,12 +896,6 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b, const Sam
   // Reference maxima: statistics-pass maxima for a residual pair, the maximum
   // over tiles for the bonus row (the statistics pass does not read row K).
   float mref_t = sr.m_t;
-  if (!resid) {
-    float mm = kNegInf, unused = kNegInf;
-    for (int tt = threadIdx.x; tt < NT; tt += kBlock) mm = fmaxf(mm, (float)tile_at(tt).mt);
-    block_max2(mm, unused, sh_f);
-    mref_t = mm;
-  }
   // Tile weights 2^((tile reference - row reference) * s) of the target and
   // draft rows, times 2^-lo of the tile reference (the sampling pass's sums
   // are relative to RN(reference * s)).  One pass gives the rows' normalisers
@@ -895,81 +907,161 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b, const Sam
   auto w_d = [&](double md) {
     return md == kNegInfD ? 0.0 : exp2((md - (double)sr.m_d) * a.s64) * exp_ref_scale((float)md, a.s_hi);
   };
-  double zbt = 0.0, zbd = 0.0, G = 0.0, H = 0.0, wt0 = 0.0, wd0 = 0.0;
-  if (isfinite(mref_t)) {
-    for (int tt = threadIdx.x; tt < NT; tt += kBlock) {
-      const SampleTile q = tile_at(tt);
-      const double wt = w_t(q.mt), wd = resid ? w_d(q.md) : 0.0;
-      wt0 = wt;
-      wd0 = wd;
-      zbt += q.zt * wt;
-      zbd += q.zd * wd;
-      G += q.g * wt;
-      H += q.h * wd;
-    }
-  }
-  block_sum4(zbt, zbd, G, H, sh_d);
-  if (!isfinite(mref_t) || !(zbt > 0.0) || !isfinite(zbt) || (resid && (!(zbd > 0.0) || !isfinite(zbd)))) {
-    // A sampled row without a finite maximum: the sequence is faulty.
-    for (int i = threadIdx.x; i <= K; i += kBlock) put_out<kFused>(&a.out_tokens[(size_t)b * (K + 1) + i], -1);
-    if (threadIdx.x == 0) put_out<kFused>(&a.accepted_len[b], -1);
-    return;
-  }
-
-  // P_t(v) = e_t(v) * w_t / Z_t and P_d(v) = e_d(v) * w_d / Z_d within a tile.
-  const double izt = 1.0 / zbt, izd = resid ? 1.0 / zbd : 0.0;
-  // Residual mass S = sum (P_t - P_d) over the positive set; a rejection whose
-  // residual rounding left no mass samples P_t instead (total mass 1).
-  double S = resid ? G * izt - H * izd : 1.0;
-  const bool fallback = resid && !(S > 0.0);
-  if (fallback) S = 1.0;
-  auto tile_mass = [&](const SampleTile& q, double wt, double wd) -> double {
-    if (!resid || fallback) return q.zt * wt * izt;
-    return q.g * wt * izt - q.h * wd * izd;
+  // The choice: P_t(v) = e_t(v) * w_t * izt and P_d(v) = e_d(v) * w_d * izd
+  // within a tile (izt, izd the reciprocal row normalisers); the residual mass
+  // S = sum (P_t - P_d) over the positive set, where a rejection whose
+  // residual rounding left no mass samples P_t instead (fallback, total mass
+  // 1); the inverse-CDF point u * S; the tile jstar holding it and the mass
+  // before that tile, or, when rounding leaves the point beyond every
+  // boundary (no_cross), the last tile with mass.
+  double izt = 0.0, izd = 0.0, target = 0.0, cbefore = 0.0;
+  int jstar = -1;
+  bool fallback = false, no_cross = false, faulty = false;
+  auto row_faulty = [&](double zt, double zd) {
+    // a sampled row without a finite maximum and normaliser
+    return !isfinite(mref_t) || !(zt > 0.0) || !isfinite(zt) || (resid && (!(zd > 0.0) || !isfinite(zd)));
   };
-  const double target = (double)sh_u[n] * S;
-
-  // Tile holding the inverse-CDF point: block scan over tiles in id order.
-  int jstar = -1, last_mass = -1;
-  double cbefore = 0.0, offset = 0.0;
-  for (int c0 = 0; c0 < NT; c0 += kBlock) {
-    const int tt = c0 + threadIdx.x;
-    double ms = 0.0;
-    if (tt < NT) {
-      const SampleTile q = tile_at(tt);
-      ms = cached ? tile_mass(q, wt0, wd0) : tile_mass(q, w_t(q.mt), resid ? w_d(q.md) : 0.0);
+  if (NT <= kWave) {
+    // Every tile record is in one lane of wave 0, which takes the choice with
+    // wave-wide reductions and passes it on through LDS: one barrier where
+    // the block-wide path below takes six.  For NT <= 64 the block-wide path
+    // adds the same values in the same order (waves 1-3 only add zeros), so
+    // both make the same choice.
+    struct Choice {
+      double izt, izd, target, cbefore;
+      float mref_t;
+      int jstar, flags;
+    };
+    __shared__ Choice sh_c;
+    if (wave == 0) {
+      const float u_n = n < kWave ? lane_value(ui, n) : a.uniforms[((size_t)b * (K + 1) + n) * 2 + 1];
+      const bool has = lane < NT;
+      if (!resid) mref_t = wave_max((float)q0.mt);  // q0.mt is -inf past NT
+      double zbt = 0.0, zbd = 0.0, G = 0.0, H = 0.0, wt = 0.0, wd = 0.0;
+      if (isfinite(mref_t) && has) {
+        wt = w_t(q0.mt);
+        wd = resid ? w_d(q0.md) : 0.0;
+        zbt += q0.zt * wt;
+        zbd += q0.zd * wd;
+        G += q0.g * wt;
+        H += q0.h * wd;
+      }
+      zbt = wave_sum(zbt);
+      zbd = wave_sum(zbd);
+      G = wave_sum(G);
+      H = wave_sum(H);
+      Choice c{0.0, 0.0, 0.0, 0.0, mref_t, -1, 0};
+      if (row_faulty(zbt, zbd)) {
+        c.flags = 1;
+      } else {
+        c.izt = 1.0 / zbt;
+        c.izd = resid ? 1.0 / zbd : 0.0;
+        double S = resid ? G * c.izt - H * c.izd : 1.0;
+        const bool fb = resid && !(S > 0.0);
+        if (fb) S = 1.0;
+        c.target = (double)u_n * S;
+        const double ms = !has ? 0.0 : (!resid || fb) ? q0.zt * wt * c.izt : q0.g * wt * c.izt - q0.h * wd * c.izd;
+        const double incl = wave_inclusive_scan(ms);
+        const uint64_t cross = __ballot(has && incl > c.target);
+        const uint64_t mass = __ballot(has && ms > 0.0);
+        if (cross) {
+          c.jstar = (int)__builtin_ctzll(cross);
+          c.cbefore = lane_value(incl - ms, c.jstar);
+        } else {
+          c.jstar = mass ? 63 - (int)__builtin_clzll(mass) : -1;
+          c.flags |= 2;
+        }
+        if (fb) c.flags |= 4;
+      }
+      if (lane == 0) sh_c = c;
     }
-    double incl = wave_inclusive_scan(ms, lane);
-    if (lane == kWave - 1) sh_scan[wave] = incl;
     __syncthreads();
-    double before_wave = 0.0, total = 0.0;
+    const Choice c = sh_c;
+    izt = c.izt;
+    izd = c.izd;
+    target = c.target;
+    cbefore = c.cbefore;
+    mref_t = c.mref_t;
+    jstar = c.jstar;
+    faulty = c.flags & 1;
+    no_cross = c.flags & 2;
+    fallback = c.flags & 4;
+  } else {
+    __shared__ float sh_u[kMaxK + 1];
+    if ((int)threadIdx.x <= K) sh_u[threadIdx.x] = ui;  // read after the barriers below
+    if (!resid) {
+      float mm = kNegInf, unused = kNegInf;
+      for (int tt = threadIdx.x; tt < NT; tt += kBlock) mm = fmaxf(mm, (float)tile_at(tt).mt);
+      block_max2(mm, unused, sh_f);
+      mref_t = mm;
+    }
+    double zbt = 0.0, zbd = 0.0, G = 0.0, H = 0.0, wt0 = 0.0, wd0 = 0.0;
+    if (isfinite(mref_t)) {
+      for (int tt = threadIdx.x; tt < NT; tt += kBlock) {
+        const SampleTile q = tile_at(tt);
+        const double wt = w_t(q.mt), wd = resid ? w_d(q.md) : 0.0;
+        wt0 = wt;
+        wd0 = wd;
+        zbt += q.zt * wt;
+        zbd += q.zd * wd;
+        G += q.g * wt;
+        H += q.h * wd;
+      }
+    }
+    block_sum4(zbt, zbd, G, H, sh_d);
+    faulty = row_faulty(zbt, zbd);
+    if (!faulty) {
+      izt = 1.0 / zbt;
+      izd = resid ? 1.0 / zbd : 0.0;
+      double S = resid ? G * izt - H * izd : 1.0;
+      fallback = resid && !(S > 0.0);
+      if (fallback) S = 1.0;
+      auto tile_mass = [&](const SampleTile& q, double wt, double wd) -> double {
+        if (!resid || fallback) return q.zt * wt * izt;
+        return q.g * wt * izt - q.h * wd * izd;
+      };
+      target = (double)sh_u[n] * S;
+      // Block scan over tiles in id order, 256 tiles per round.
+      int last_mass = -1;
+      double offset = 0.0;
+      for (int c0 = 0; c0 < NT; c0 += kBlock) {
+        const int tt = c0 + threadIdx.x;
+        double ms = 0.0;
+        if (tt < NT) {
+          const SampleTile q = tile_at(tt);
+          ms = cached ? tile_mass(q, wt0, wd0) : tile_mass(q, w_t(q.mt), resid ? w_d(q.md) : 0.0);
+        }
+        double incl = wave_inclusive_scan(ms);
+        if (lane == kWave - 1) sh_scan[wave] = incl;
+        __syncthreads();
+        double before_wave = 0.0, total = 0.0;
 #pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) {
-      if (w < wave) before_wave += sh_scan[w];
-      total += sh_scan[w];
+        for (int w = 0; w < kWavesPerBlock; ++w) {
+          if (w < wave) before_wave += sh_scan[w];
+          total += sh_scan[w];
+        }
+        incl += before_wave;
+        const bool cross = tt < NT && offset + incl > target;
+        // First crossing tile of this round, and its last tile with mass.
+        int first = cross ? tt : 0x7fffffff;
+        int neg_last = (tt < NT && ms > 0.0) ? -tt : 1;
+        block_min2(first, neg_last, sh_i);  // its barriers also retire sh_scan
+        if (neg_last <= 0) last_mass = -neg_last;
+        if (first != 0x7fffffff) {
+          if (tt == first) sh_cbefore = offset + incl - ms;
+          __syncthreads();
+          cbefore = sh_cbefore;
+          jstar = first;
+          break;
+        }
+        offset += total;
+      }
+      no_cross = jstar < 0;
+      if (no_cross) jstar = last_mass;
     }
-    incl += before_wave;
-    const bool cross = tt < NT && offset + incl > target;
-    // First crossing tile of this chunk, and its last tile with mass (for
-    // the case that rounding leaves the point beyond every boundary).
-    int first = cross ? tt : 0x7fffffff;
-    int neg_last = (tt < NT && ms > 0.0) ? -tt : 1;
-    block_min2(first, neg_last, sh_i);  // its barriers also retire sh_scan
-    if (neg_last <= 0) last_mass = -neg_last;
-    if (first != 0x7fffffff) {
-      if (tt == first) sh_cbefore = offset + incl - ms;
-      __syncthreads();
-      cbefore = sh_cbefore;
-      jstar = first;
-      break;
-    }
-    offset += total;
   }
-  // No crossing: take the last tile with mass, and in it the last element
-  // with positive weight.
-  const bool no_cross = jstar < 0;
-  if (no_cross) jstar = last_mass;
-  if (jstar < 0) {
+  if (faulty || jstar < 0) {
+    // faulty row, or a row with no mass at all
     for (int i = threadIdx.x; i <= K; i += kBlock) put_out<kFused>(&a.out_tokens[(size_t)b * (K + 1) + i], -1);
     if (threadIdx.x == 0) put_out<kFused>(&a.accepted_len[b], -1);
     return;
@@ -1031,7 +1123,7 @@ __device__ __forceinline__ void pick_block(const VerifyArgs& a, int b, const Sam
     cum[k] = acc;
     if (w[k] > 0.0) last_pos = id0 + k;
   }
-  const double incl = wave_inclusive_scan(acc, lane);
+  const double incl = wave_inclusive_scan(acc);
   if (lane == kWave - 1) sh_scan[wave] = incl;
   __syncthreads();
   double before = cbefore;
@@ -1071,9 +1163,10 @@ __global__ void __launch_bounds__(kBlock) stats_kernel(VerifyArgs a) {
 // Every accept decision of sequence blockIdx.x and its first rejection
 // (Speculative Decoding lesson, "Core algorithm" steps 4-5, "Step 1"): the
 // outputs up to the first rejection, P(d) at each position, and the record
-// the sampling and pick kernels read.  Large batches take the decisions here
-// once per sequence; small ones in the prologue of every sampling block,
-// which saves this launch.
+// the sampling and pick kernels read.  Used for large grids whose sampling
+// prologue would be heavy (more than 16 rows or 64 partials per row); other
+// shapes take the decisions in the prologue of every sampling block, which
+// saves this launch.
 __global__ void __launch_bounds__(kBlock) decide_kernel(VerifyArgs a) {
   (void)accept_sequence(a, blockIdx.x, true);
 }

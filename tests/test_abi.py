@@ -59,7 +59,9 @@ def test_workspace_sizes(lib):
 
 def test_launch_counts(lib):
     f = lib.spec_verify_launch_count
-    assert f(256, 7, 262144, 1, 0) == 4            # statistics, decisions, sampling, pick
+    assert f(256, 7, 262144, 1, 0) == 3            # statistics, sampling (decisions in its prologue), pick
+    assert f(256, 9, 262144, 1, 0) == 4            # 18 rows: statistics, decisions, sampling, pick
+    assert f(256, 7, 600000, 1, 0) == 4            # 147 partials per row: a decision launch too
     assert f(64, 4, 151936, 1, 0) == 3             # decisions in the sampling prologue
     assert f(8, 5, 128256, 1, 0) == 2              # small grid: the sampling launch also picks
     assert f(8, 0, 128256, 1, 0) == 2              # K = 0: sampling, then a separate pick

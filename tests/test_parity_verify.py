@@ -221,15 +221,16 @@ def test_sample_max_k(sigma):
 
 
 def test_sample_decision_launch_and_prologue_agree():
-    """B=1024, V=16384 takes the separate decision launch (two sampling tiles
-    per wave); the same sequences in batches of 64 take the decisions in the
-    sampling prologue.  Outputs are bit-identical and match the oracle."""
+    """B=1024, K=9, V=16384 takes the separate decision launch (two sampling
+    tiles per wave, 18 rows per sequence); the same sequences in batches of 64
+    take the decisions in the sampling prologue.  Outputs are bit-identical
+    and match the oracle."""
     import speculative_sampling_verification_vocab_amd as sv
     from speculative_sampling_verification_vocab_amd import _native
     lib = _native.load()
-    assert lib.spec_verify_launch_count(1024, 2, 16384, 1, 0) == 4
-    assert lib.spec_verify_launch_count(64, 2, 16384, 1, 0) == 2    # small grid: fused pick
-    c = _case(1024, 2, 16384, "bf16", key=(25,))
+    assert lib.spec_verify_launch_count(1024, 9, 16384, 1, 0) == 4
+    assert lib.spec_verify_launch_count(64, 9, 16384, 1, 0) == 2    # small grid: fused pick
+    c = _case(1024, 9, 16384, "bf16", key=(25,))
     rep, out, orc = check_case(c)
     for s0 in range(0, 1024, 64):
         part = VerifyCase(c.target[s0:s0 + 64], c.draft[s0:s0 + 64], c.draft_tokens[s0:s0 + 64],

@@ -240,6 +240,23 @@ def test_sample_decision_launch_and_prologue_agree():
             np.testing.assert_array_equal(o[k], out[k][s0:s0 + 64])
 
 
+@pytest.mark.parametrize("V,dtype", [(131072, "bf16"), (131073, "bf16"), (65536, "f32"), (65537, "f32")])
+def test_pick_choice_at_64_sampling_tiles(V, dtype):
+    """Rows of exactly 64 sampling tiles (2048 bf16 or 1024 fp32 ids each)
+    take the pick's one-wave tile choice, rows of 65 the block-wide one; both
+    in the sampling launch's last block (B=8) and in the pick launch (B=96),
+    against the oracle, with rejections and bonus tokens in the mix."""
+    import speculative_sampling_verification_vocab_amd as sv
+    for B in (8, 96):
+        fused = sv.spec_verify_launch_count(B, 3, V, torch.bfloat16 if dtype == "bf16" else torch.float32,
+                                            "sample") == 2
+        print(f"case V={V} dtype={dtype} B={B} fused pick={fused}", flush=True)
+        assert fused == (B == 8)
+        c = _case(B, 3, V, dtype, sigma=0.3, key=(26, V, B))
+        rep, out, orc = check_case(c)
+        assert np.any(out[0] == 3) and np.any(out[0] < 3)
+
+
 @pytest.mark.parametrize("V,dtype", [(600000, "bf16"), (300000, "f32")])
 def test_sample_long_rows(V, dtype):
     """147 statistics tiles and 293 sampling tiles per row: the combine over

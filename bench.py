@@ -30,6 +30,11 @@ Prints ONE JSON line on stdout:
              outputs; rows after each sequence's first rejection not read).
   kv_commit  the KV-cache commit of that batch's accepted drafts on a
              Llama-3-8B-like cache layout (bytes moved, HBM rate).
+  greedy, small_batches, shortlist_head
+             (default workload, unless --no-extras) GREEDY mode on the same
+             batch; the smaller batch configurations (B=1, 8, 64), warm and
+             cold; the shortlisted drafter head with full-vocabulary verify,
+             its sparse-draft form and the static shared shortlist head.
 """
 from __future__ import annotations
 
@@ -323,6 +328,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=256, help="sequences timed on the CPU oracle")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="thread-seconds of oracle work to time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the small-batch, greedy and drafter-head measurements of the default run")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run one plain device copy of this many GiB (PMC scaling reference)")
     args = ap.parse_args()
@@ -349,7 +356,8 @@ def main():
         log(f"calibration copy: {n * 4} bytes read, {n * 4} bytes written")
         del a, b
     if args.workload == HEAD_WORKLOAD:
-        return bench_shortlist(args, dev)
+        print(json.dumps(bench_shortlist(args, dev)), flush=True)
+        return
     t0 = time.time()
     case = workload_case(args.workload, device=dev, greedy=args.mode == "greedy")
     torch.cuda.synchronize()
@@ -485,6 +493,19 @@ def main():
     kv = None
     if args.mode == "sample" and not args.no_kv_commit:
         kv = bench_kv_commit(res[0], K, args.steps, dev)
+    extras = {}
+    if args.mode == "sample" and not args.no_extras and args.workload == "b256_k7_v262144_bf16":
+        # the other rows of the path, measured in the same run: GREEDY on this
+        # batch, the smaller batch configurations, and the drafter heads
+        log("greedy on the benchmark batch")
+        extras["greedy"] = bench_greedy(case, sets, args.steps, args.warmup, dev)
+        log("small batch configurations")
+        extras["small_batches"] = bench_small_batches(dev)
+        log("drafter heads (shortlist gather-GEMM + verify, sparse draft, static shortlist)")
+        head = bench_shortlist(args, dev)
+        extras["shortlist_head"] = {k: head[k] for k in ("ms_per_step", "value", "unit", "config", "kernels_ms",
+                                                         "roofline", "mfma", "acceptance", "sparse_draft",
+                                                         "static_head", "cache_residency_verify")}
 
     out = {
         "metric": "verified draft positions/sec (B*(K+1)) and achieved HBM GB/s vs peak",
@@ -522,6 +543,7 @@ def main():
         out["early_exit"] = early
     if kv is not None:
         out["kv_commit"] = kv
+    out.update(extras)
     print(json.dumps(out), flush=True)
 
 
@@ -620,7 +642,91 @@ def bench_shortlist(args, dev):
     out["roofline"]["measured_copy_gbs"] = copy_reference(dev)
     out["sparse_draft"] = bench_sparse_draft(hc, target, uni, args.steps, args.warmup, dev)
     out["static_head"] = bench_static_head(hc, args.steps, args.warmup, dev)
-    print(json.dumps(out), flush=True)
+    return out
+
+
+SMALL_BATCHES = (("b1_k4_v32000_f32", (0.5,)), ("b8_k5_v128256_bf16", (0.2, 1.0)),
+                 ("b64_k4_v151936_bf16", (0.1, 0.5, 1.0, 2.0)))
+
+
+def bench_small_batches(dev):
+    """The smaller verify configurations, one call at a time as a serving loop
+    makes them (VerifyPlan: no allocation per call): B=1, K=4, V=32000 f32;
+    B=8, K=5, V=128256 bf16 at draft noise sigma 0.2 and 1.0 (T=0.8), and its
+    greedy run on argmax drafts; B=64, K=4, V=151936 bf16 at sigma 0.1, 0.5,
+    1.0, 2.0 (T=1).  Median call time with HIP events around the call, with
+    the inputs cache-resident (warm) and after a 512 MiB read (cold), and the
+    acceptance the call produced beside the closed form at that alpha."""
+    import torch
+
+    import speculative_sampling_verification_vocab_amd as sv
+    from workloads import workload_case
+
+    out = []
+    for name, sigmas in SMALL_BATCHES:
+        runs = [(sw, sig, "sample") for sw, sig in enumerate(sigmas)]
+        if name.startswith("b8_"):
+            runs.append((0, sigmas[0], "greedy"))
+        for sw, sig, mode in runs:
+            case = workload_case(name, sweep=sw, device=dev, greedy=mode == "greedy")
+            B, K, V = case.B, case.K, case.V
+            esz = 2 if case.dtype == "bf16" else 4
+            plan = sv.VerifyPlan(B, K, V, case.target.dtype, mode, device=dev)
+            args = (case.target, case.draft, case.draft_tokens, case.uniforms, case.temperature)
+            res = plan(*args)
+            torch.cuda.synchronize()
+            acc = acceptance_report(res[0].cpu().numpy(), K)
+            rows = (K + 1) if mode == "greedy" else (2 * K + 1)
+            t = cold_warm(lambda: plan(*args), B * rows * V * esz, dev)
+            out.append({"workload": name, "mode": mode, "sigma": sig, "temperature": case.temperature,
+                        "launches": sv.spec_verify_launch_count(B, K, V, case.target.dtype, mode),
+                        "warm_us": t["warm_us"], "cold_us": t["cold_us"], "logit_bytes": t["input_bytes"],
+                        "cold_gbs": t["cold_gbs"], "hbm_frac_cold": t["cold_gbs"] / HBM_PEAK_GBS,
+                        "acceptance": acc})
+            del case, plan, res
+    return out
+
+
+def bench_greedy(case, sets, steps, warmup, dev):
+    """GREEDY mode on the benchmark batch: argmax of every target row and the
+    longest matching prefix.  Mean step time (no instrumentation) and the
+    argmax pass's rate on its B*(K+1)*V logits (HIP events on its launch)."""
+    import numpy as np
+    import torch
+
+    import speculative_sampling_verification_vocab_amd as sv
+
+    B, K, V = case.B, case.K, case.V
+    esz = 2 if case.dtype == "bf16" else 4
+    plan = sv.VerifyPlan(B, K, V, case.target.dtype, "greedy", device=dev)
+
+    def step(i, evs=None):
+        c = sets[i % len(sets)]
+        return plan(c.target, None, c.draft_tokens, None, 0.0, events=evs)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e3 in evs:
+        for e in e3:
+            e.record()  # creates the underlying hipEvent the library records into
+    torch.cuda.synchronize()
+    for i, e3 in enumerate(evs):
+        step(i, e3)
+    torch.cuda.synchronize()
+    argmax_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    fin_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    nbytes = B * (K + 1) * V * esz
+    return {"mode": "greedy", "ms_per_step": ms, "value": B * (K + 1) / (ms * 1e-3), "unit": "positions/s",
+            "argmax_kernel_ms": argmax_ms, "finalize_kernel_ms": fin_ms, "logit_bytes": nbytes,
+            "argmax_gbs": nbytes / (argmax_ms * 1e-3) / 1e9,
+            "argmax_hbm_frac": nbytes / (argmax_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def bench_static_head(hc, steps, warmup, dev):
